@@ -1,0 +1,118 @@
+"""CPU oracle of the multi-scale deformable attention core (test infrastructure).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package. The product path never does.
+
+The arithmetic lives in ``msda_oracle.c`` (plain C, double accumulation, single
+thread); this module only marshals numpy arrays into it. See the header of
+``msda_oracle.c`` for what is computed and which passages of the pages each
+step follows.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+
+_i64 = ctypes.c_int64
+_pd = ctypes.POINTER(ctypes.c_double)
+_pf = ctypes.POINTER(ctypes.c_float)
+_pi = ctypes.POINTER(ctypes.c_int64)
+
+
+def library(path=None):
+    """Load (building first if absent) the oracle shared library."""
+    global _LIB
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _LIB is None:
+        if not os.path.exists(_build.LIBRARY):
+            _build.build()
+        _LIB = _bind(ctypes.CDLL(_build.LIBRARY))
+    return _LIB
+
+
+def _bind(lib):
+    lib.msda_oracle_forward.restype = ctypes.c_int
+    lib.msda_oracle_forward.argtypes = [_i64] * 7 + [_pd, _pi, _pi, _pf, _pd, _pd, _pd]
+    lib.msda_oracle_backward.restype = ctypes.c_int
+    lib.msda_oracle_backward.argtypes = [_i64] * 7 + [_pd, _pi, _pi, _pf, _pd, _pd, _pd, _pd,
+                                                      _pd, _pd, _pd, _pd]
+    lib.msda_oracle_version.restype = ctypes.c_int
+    return lib
+
+
+def _ptr(a, ctype):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _prep(value, spatial_shapes, level_start_index, sampling_locations, attention_weights):
+    value = np.ascontiguousarray(value, dtype=np.float64)
+    shapes = np.ascontiguousarray(spatial_shapes, dtype=np.int64).reshape(-1, 2)
+    lsi = np.ascontiguousarray(level_start_index, dtype=np.int64).reshape(-1)
+    loc = np.ascontiguousarray(sampling_locations, dtype=np.float32)
+    attn = np.ascontiguousarray(attention_weights, dtype=np.float64)
+    if value.ndim != 4 or loc.ndim != 6 or attn.ndim != 5:
+        raise ValueError("value must be [B,Nv,M,D], locations [B,Nq,M,L,K,2], "
+                         "weights [B,Nq,M,L,K]")
+    B, Nv, M, D = value.shape
+    Bq, Nq, Mq, L, K, two = loc.shape
+    if (Bq, Mq, two) != (B, M, 2) or attn.shape != (B, Nq, M, L, K):
+        raise ValueError("inconsistent shapes")
+    if shapes.shape[0] != L or lsi.shape[0] != L:
+        raise ValueError("spatial_shapes / level_start_index do not have L rows")
+    dims = (B, Nv, M, D, L, Nq, K)
+    return dims, value, shapes, lsi, loc, attn
+
+
+def forward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
+            with_abs=False, lib=None):
+    """Core forward in double. Returns out [B,Nq,M,D] (and the per-element
+    absolute term sums when ``with_abs``). ``lib`` selects another build of
+    the oracle (the default is the in-tree one)."""
+    dims, value, shapes, lsi, loc, attn = _prep(value, spatial_shapes, level_start_index,
+                                                sampling_locations, attention_weights)
+    B, Nv, M, D, L, Nq, K = dims
+    out = np.empty((B, Nq, M, D), np.float64)
+    out_abs = np.empty_like(out) if with_abs else None
+    rc = (lib or library()).msda_oracle_forward(*dims, _ptr(value, ctypes.c_double),
+                                       _ptr(shapes, ctypes.c_int64), _ptr(lsi, ctypes.c_int64),
+                                       _ptr(loc, ctypes.c_float), _ptr(attn, ctypes.c_double),
+                                       _ptr(out, ctypes.c_double),
+                                       _ptr(out_abs, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (tables inconsistent with Nv?)")
+    return (out, out_abs) if with_abs else out
+
+
+def backward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
+             grad_output, with_abs=False, lib=None):
+    """Core backward in double. Returns (grad_value, grad_locations,
+    grad_weights), followed by their absolute term sums when ``with_abs``."""
+    dims, value, shapes, lsi, loc, attn = _prep(value, spatial_shapes, level_start_index,
+                                                sampling_locations, attention_weights)
+    B, Nv, M, D, L, Nq, K = dims
+    g = np.ascontiguousarray(grad_output, dtype=np.float64).reshape(B, Nq, M, D)
+    gv = np.empty((B, Nv, M, D), np.float64)
+    gl = np.empty((B, Nq, M, L, K, 2), np.float64)
+    ga = np.empty((B, Nq, M, L, K), np.float64)
+    gva = np.empty_like(gv) if with_abs else None
+    gla = np.empty_like(gl) if with_abs else None
+    gaa = np.empty_like(ga) if with_abs else None
+    rc = (lib or library()).msda_oracle_backward(*dims, _ptr(value, ctypes.c_double),
+                                        _ptr(shapes, ctypes.c_int64), _ptr(lsi, ctypes.c_int64),
+                                        _ptr(loc, ctypes.c_float), _ptr(attn, ctypes.c_double),
+                                        _ptr(g, ctypes.c_double), _ptr(gv, ctypes.c_double),
+                                        _ptr(gl, ctypes.c_double), _ptr(ga, ctypes.c_double),
+                                        _ptr(gva, ctypes.c_double), _ptr(gla, ctypes.c_double),
+                                        _ptr(gaa, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (tables inconsistent with Nv?)")
+    if with_abs:
+        return gv, gl, ga, gva, gla, gaa
+    return gv, gl, ga

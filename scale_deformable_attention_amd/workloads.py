@@ -1,0 +1,188 @@
+"""Seeded synthetic inputs for the multi-scale deformable attention core.
+
+This module is shared by the CPU oracle's tests, the GPU parity tests and the
+benchmark. It holds none of the core's arithmetic (no coordinate map, no
+interpolation, no weighted sum): it only draws random numbers with numpy and
+assembles the six tensors the core takes.
+
+Two model-side steps that sit *before* the core are used to shape realistic
+inputs, both as the DETR-to-Deformable-DETR article (cf-1.com, section 3.2)
+describes them:
+  * sampling locations = reference point + offset / (W_l, H_l), with raw
+    offsets drawn in level-l pixels;
+  * attention weights = softmax of logits over the L*K samples of one
+    (query, head) (also the CSDN MSDA explainer, section 3, note 3).
+
+Reference points: encoder queries are the pixel centres of every level,
+normalized to [0, 1] (cf-1.com section 3.2: position plus half a pixel); the
+decoder and the tiny case draw them uniformly.
+
+Shapes are those of the 800x1333 and 1920x1080 feature pyramids at strides
+8/16/32/64 with the Deformable-DETR defaults M=8 heads, L=4 levels, K=4
+points, d_model 256 (discosf.com section 2.2; cf-1.com section 3.3). Values,
+offsets, logits and upstream gradients are normal draws; they stand in for
+real activations (no dataset is used).
+
+Draw order per workload (numpy PCG64, seed fixed per workload): value,
+reference points (when random), offsets, logits, upstream gradient.
+"""
+from dataclasses import dataclass, field
+from typing import Optional, Tuple
+
+import numpy as np
+
+PYRAMID_800x1333 = ((100, 167), (50, 84), (25, 42), (13, 21))
+PYRAMID_1920x1080 = ((135, 240), (68, 120), (34, 60), (17, 30))
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic workload of the core.
+
+    ref: "grid" (every pixel of every level is a query, Nq = Nv),
+         "uniform" (U[0,1]^2) or "inner" (U[0.05,0.95]^2).
+    sigma_px: standard deviation of the sampling offsets, in level-l pixels.
+    """
+    name: str
+    B: int
+    M: int
+    D: int
+    K: int
+    shapes: Tuple[Tuple[int, int], ...]
+    ref: str
+    sigma_px: float
+    Nq: Optional[int] = None
+    value_dtype: str = "f32"
+    backward: bool = False
+    seed: int = 0
+    note: str = field(default="", compare=False)
+
+    @property
+    def L(self):
+        return len(self.shapes)
+
+    @property
+    def Nv(self):
+        return int(sum(h * w for h, w in self.shapes))
+
+    @property
+    def num_queries(self):
+        return self.Nv if self.ref == "grid" else int(self.Nq)
+
+    @property
+    def points(self):
+        """Sampled points per pass, B*Nq*M*L*K (the metric's unit)."""
+        return self.B * self.num_queries * self.M * self.L * self.K
+
+    def level_start_index(self):
+        starts, s = [], 0
+        for h, w in self.shapes:
+            starts.append(s)
+            s += h * w
+        return np.asarray(starts, np.int64)
+
+    def scaled(self, **changes):
+        """A copy with some fields changed (used to make small test cases)."""
+        d = {k: getattr(self, k) for k in self.__dataclass_fields__}
+        d.update(changes)
+        return Workload(**d)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", B=1, M=2, D=8, K=2, shapes=((8, 8), (4, 4)), ref="uniform",
+                     sigma_px=1.0, Nq=16, backward=True, seed=1001,
+                     note="tiny fp32 fwd+bwd"),
+    "encoder": Workload("encoder", B=2, M=8, D=32, K=4, shapes=PYRAMID_800x1333, ref="grid",
+                        sigma_px=2.0, seed=1002,
+                        note="800x1333 encoder self-attention, fp32, forward"),
+    "decoder": Workload("decoder", B=8, M=8, D=32, K=4, shapes=PYRAMID_800x1333, ref="inner",
+                        sigma_px=4.0, Nq=300, backward=True, seed=1003,
+                        note="800x1333 decoder cross-attention, 300 queries, fp32 fwd+bwd"),
+    "hires_bf16": Workload("hires_bf16", B=2, M=8, D=32, K=8, shapes=PYRAMID_1920x1080,
+                           ref="grid", sigma_px=3.0, value_dtype="bf16", seed=1004,
+                           note="1920x1080 encoder, bf16 value, fp32 accumulate, forward"),
+    "encoder_train": Workload("encoder_train", B=4, M=8, D=32, K=4, shapes=PYRAMID_800x1333,
+                              ref="grid", sigma_px=8.0, backward=True, seed=1005,
+                              note="800x1333 encoder training step, fp32 fwd+bwd"),
+}
+
+
+def bf16_round(x):
+    """Round float32 to the nearest bfloat16 (ties to even). Returns the bf16
+    bit patterns as uint16. NaN stays NaN (quiet)."""
+    u = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(np.asarray(x, np.float32))
+    if nan.any():
+        rounded[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+    return rounded
+
+
+def bf16_to_f32(bits):
+    """Exact widening of bf16 bit patterns (uint16) to float32."""
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _reference_points(w, rng):
+    """Normalized reference point of every query, [Nq, 2] as (x, y)."""
+    if w.ref == "grid":
+        refs = []
+        for h, wd in w.shapes:
+            jj, ii = np.meshgrid((np.arange(wd) + 0.5) / wd, (np.arange(h) + 0.5) / h)
+            refs.append(np.stack([jj.reshape(-1), ii.reshape(-1)], -1))
+        return np.concatenate(refs, 0)
+    lo, hi = (0.0, 1.0) if w.ref == "uniform" else (0.05, 0.95)
+    return rng.uniform(lo, hi, size=(w.Nq, 2))
+
+
+def generate(w: Workload, batch_slice=None):
+    """Draw the inputs of one workload.
+
+    Returns a dict of numpy arrays:
+      value            [B,Nv,M,D] float32 (for bf16 workloads: the bf16-rounded
+                       values widened to float32, exactly what the GPU reads)
+      value_bf16       [B,Nv,M,D] uint16 bf16 bits (bf16 workloads only)
+      value_f32_orig   the unrounded float32 draws (bf16 workloads only)
+      spatial_shapes   [L,2] int64 (H, W)
+      level_start_index[L] int64
+      sampling_locations [B,Nq,M,L,K,2] float32
+      attention_weights  [B,Nq,M,L,K] float32
+      grad_output      [B,Nq,M*D] float32
+      reference_points [Nq,2] float64 (x, y) normalized
+    ``batch_slice`` (a slice over B) keeps only those batch entries; the draws
+    are made for the full batch first so a slice is a true sub-sample.
+    """
+    rng = np.random.default_rng(w.seed)
+    B, M, D, L, K, Nv, Nq = w.B, w.M, w.D, w.L, w.K, w.Nv, w.num_queries
+    value = rng.standard_normal((B, Nv, M, D), dtype=np.float32)
+    ref = _reference_points(w, rng)                                   # [Nq, 2]
+    offsets = rng.standard_normal((B, Nq, M, L, K, 2)) * w.sigma_px    # level pixels
+    logits = rng.standard_normal((B, Nq, M, L * K))
+    grad_output = rng.standard_normal((B, Nq, M * D), dtype=np.float32)
+
+    wh = np.asarray([[wd, h] for h, wd in w.shapes], np.float64)       # [L, 2] as (W, H)
+    loc = ref[None, :, None, None, None, :] + offsets / wh[None, None, None, :, None, :]
+    e = np.exp(logits - logits.max(-1, keepdims=True))
+    attn = (e / e.sum(-1, keepdims=True)).reshape(B, Nq, M, L, K)
+
+    out = {
+        "spatial_shapes": np.asarray(w.shapes, np.int64).reshape(L, 2),
+        "level_start_index": w.level_start_index(),
+        "sampling_locations": loc.astype(np.float32),
+        "attention_weights": attn.astype(np.float32),
+        "grad_output": grad_output,
+        "reference_points": ref,
+    }
+    if w.value_dtype == "bf16":
+        bits = bf16_round(value)
+        out["value_bf16"] = bits
+        out["value_f32_orig"] = value
+        out["value"] = bf16_to_f32(bits)
+    else:
+        out["value"] = value
+    if batch_slice is not None:
+        for key in ("value", "value_bf16", "value_f32_orig", "sampling_locations",
+                    "attention_weights", "grad_output"):
+            if key in out:
+                out[key] = np.ascontiguousarray(out[key][batch_slice])
+    return out

@@ -1,0 +1,445 @@
+"""Pins of the CPU oracle: checks that fix what the oracle computes without
+comparing it with itself.
+
+Each pin takes an oracle library handle (``None`` = the in-tree build) and
+raises AssertionError when the oracle disagrees with what the pages and the
+mathematics fix. The same functions run against deliberately broken builds of
+the oracle in ``test_oracle_mutants.py``, which shows that a plausible mistake
+(a dropped term, a wrong sign, a swapped axis, a wrong pixel convention) is
+caught by at least one of them.
+
+Conventions being pinned (pages on deformable attention):
+  * the core sum over heads' levels and points, weighted by A
+    (discosf.com tutorial, section 2.2; cf-1.com article, section 3.1);
+  * cell-centre coordinates x = u*W - 0.5 (grid_sample, align_corners=False:
+    cf-1.com 5.3, CSDN explainer section 3 note 2);
+  * bilinear interpolation, zero outside the level, gradients through the
+    weights (discosf.com 2.1, 2.2, 3.2; cf-1.com 5.3 zeros padding);
+  * flattened levels with (H, W) rows and start indices (cf-1.com 3.3);
+  * locations as (x, y) = (width, height) (offset normalizer stacked (W, H),
+    cf-1.com 3.2).
+"""
+import os
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- helpers
+def level_tables(shapes):
+    shapes = np.asarray(shapes, np.int64).reshape(-1, 2)
+    lsi = np.concatenate([[0], np.cumsum(shapes[:, 0] * shapes[:, 1])[:-1]]).astype(np.int64)
+    return shapes, lsi
+
+
+def coord32(u, n):
+    """The single-precision fused multiply-add u*n - 0.5, correctly rounded.
+    u is float32 and n a small integer, so u*n - 0.5 is exact in double and one
+    rounding to float32 gives the correctly rounded fma."""
+    return (np.asarray(u, np.float32).astype(np.float64) * n - 0.5).astype(np.float32)
+
+
+def random_case(rng, B=2, M=3, D=5, shapes=((5, 7), (3, 4), (2, 2)), Nq=6, K=3,
+                lo=-0.15, hi=1.15):
+    """Random inputs in a box around [0,1]^2 (so some corners fall outside)."""
+    shapes, lsi = level_tables(shapes)
+    L = shapes.shape[0]
+    Nv = int((shapes[:, 0] * shapes[:, 1]).sum())
+    value = rng.standard_normal((B, Nv, M, D))
+    loc = rng.uniform(lo, hi, size=(B, Nq, M, L, K, 2)).astype(np.float32)
+    attn = rng.standard_normal((B, Nq, M, L, K))
+    g = rng.standard_normal((B, Nq, M, D))
+    return value, shapes, lsi, loc, attn, g
+
+
+def fwd(lib, value, shapes, lsi, loc, attn):
+    return oracle.forward(value, shapes, lsi, loc, attn, lib=lib)
+
+
+def bwd(lib, value, shapes, lsi, loc, attn, g):
+    return oracle.backward(value, shapes, lsi, loc, attn, g, lib=lib)
+
+
+def _close(a, b, tol, what):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    scale = max(1.0, np.max(np.abs(b)) if b.size else 0.0)
+    assert err <= tol * scale, f"{what}: max |diff| {err:.3e} > {tol:.1e} * {scale:.3g}"
+
+
+# ----------------------------------------------------------------------------- pins
+def pin_golden_hand_worked(lib=None):
+    """Hand-worked 2x2 samples (tests/golden/bilinear_2x2_hand.txt)."""
+    rows = np.loadtxt(os.path.join(GOLDEN, "bilinear_2x2_hand.txt"), comments="#")
+    shapes, lsi = level_tables([(2, 2)])
+    value = np.array([1.0, 2.0, 3.0, 4.0]).reshape(1, 4, 1, 1)
+    for u, v, a, g, out, gu, gv, ga in rows:
+        loc = np.array([u, v], np.float32).reshape(1, 1, 1, 1, 1, 2)
+        attn = np.array([a]).reshape(1, 1, 1, 1, 1)
+        go = np.array([g]).reshape(1, 1, 1, 1)
+        o = fwd(lib, value, shapes, lsi, loc, attn)
+        _, gl, gat = bwd(lib, value, shapes, lsi, loc, attn, go)
+        got = (o.item(), gl[..., 0].item(), gl[..., 1].item(), gat.item())
+        np.testing.assert_allclose(got, (out, gu, gv, ga), rtol=0, atol=1e-12,
+                                   err_msg=f"golden sample u={u} v={v}")
+
+
+def pin_pixel_centres(lib=None):
+    """Sampling exactly at a pixel centre with a one-hot weight returns that
+    pixel's value: fixes the level offsets, the (x, y) order, the row/column
+    strides and the half-pixel convention. Power-of-two levels make it exact;
+    other widths leave the fp32 coordinate at most an ulp off an integer."""
+    rng = np.random.default_rng(11)
+    for shp, exact in ((((8, 8), (4, 4), (2, 16)), True), (((5, 7), (3, 11), (1, 1)), False)):
+        shapes, lsi = level_tables(shp)
+        L = len(shp)
+        Nv = int((shapes[:, 0] * shapes[:, 1]).sum())
+        B, M, D, K, Nq = 2, 3, 4, 2, 12
+        value = rng.standard_normal((B, Nv, M, D))
+        loc = np.zeros((B, Nq, M, L, K, 2), np.float32)
+        attn = np.zeros((B, Nq, M, L, K))
+        expect = np.zeros((B, Nq, M, D))
+        for b in range(B):
+            for q in range(Nq):
+                for m in range(M):
+                    l = rng.integers(L)
+                    k = rng.integers(K)
+                    H, W = shapes[l]
+                    i, j = rng.integers(H), rng.integers(W)          # row i, column j
+                    loc[b, q, m, l, k] = ((j + 0.5) / W, (i + 0.5) / H)
+                    attn[b, q, m, l, k] = 1.0
+                    expect[b, q, m] = value[b, lsi[l] + i * W + j, m]
+        out = fwd(lib, value, shapes, lsi, loc, attn)
+        if exact:
+            assert np.array_equal(out, expect), "pixel-centre sample is not the pixel value"
+        else:
+            _close(out, expect, 1e-6, "pixel-centre sample (non power-of-two level)")
+
+
+def pin_constant_field(lib=None):
+    """A constant field is returned unchanged when every corner is inside and the
+    weights sum to one; the location gradient vanishes; the weight gradient is
+    g . c for every sample."""
+    rng = np.random.default_rng(12)
+    shapes, lsi = level_tables(((6, 9), (3, 5)))
+    L = 2
+    B, M, D, K, Nq = 2, 2, 3, 3, 7
+    Nv = int((shapes[:, 0] * shapes[:, 1]).sum())
+    c = rng.standard_normal((M, D))
+    value = np.broadcast_to(c, (B, Nv, M, D)).copy()
+    # in-bounds: x in [0, W-1), y in [0, H-1)
+    loc = np.empty((B, Nq, M, L, K, 2), np.float32)
+    for l in range(L):
+        H, W = shapes[l]
+        loc[:, :, :, l, :, 0] = (rng.uniform(0.0, W - 1 - 1e-3, (B, Nq, M, K)) + 0.5) / W
+        loc[:, :, :, l, :, 1] = (rng.uniform(0.0, H - 1 - 1e-3, (B, Nq, M, K)) + 0.5) / H
+    logits = rng.standard_normal((B, Nq, M, L * K))
+    attn = (np.exp(logits) / np.exp(logits).sum(-1, keepdims=True)).reshape(B, Nq, M, L, K)
+    g = rng.standard_normal((B, Nq, M, D))
+    out = fwd(lib, value, shapes, lsi, loc, attn)
+    _close(out, np.broadcast_to(c, out.shape), 1e-13, "constant field")
+    _, gl, ga = bwd(lib, value, shapes, lsi, loc, attn, g)
+    _close(gl, np.zeros_like(gl), 1e-12, "location gradient on a constant field")
+    expect_ga = np.einsum("bqmd,md->bqm", g, c)[..., None, None] * np.ones((L, K))
+    _close(ga, expect_ga, 1e-12, "weight gradient on a constant field")
+
+
+def pin_bilinear_field(lib=None):
+    """Bilinear interpolation reproduces any field alpha + beta x + gamma y +
+    delta x y exactly (inside the level), and its location gradient is the
+    field's own derivative times W (or H) and A."""
+    rng = np.random.default_rng(13)
+    shapes, lsi = level_tables(((6, 9), (4, 3), (7, 5)))
+    L = shapes.shape[0]
+    B, M, D, K, Nq = 2, 2, 3, 2, 9
+    Nv = int((shapes[:, 0] * shapes[:, 1]).sum())
+    coef = rng.standard_normal((B, L, M, D, 4))                 # alpha, beta, gamma, delta
+    value = np.empty((B, Nv, M, D))
+    for l in range(L):
+        H, W = shapes[l]
+        yy, xx = np.meshgrid(np.arange(H), np.arange(W), indexing="ij")
+        xx, yy = xx.reshape(-1), yy.reshape(-1)
+        for b in range(B):
+            a0, bx, cy, dxy = np.moveaxis(coef[b, l], -1, 0)    # each [M, D]
+            value[b, lsi[l]:lsi[l] + H * W] = (a0 + bx * xx[:, None, None] + cy * yy[:, None, None]
+                                               + dxy * (xx * yy)[:, None, None])
+    loc = np.empty((B, Nq, M, L, K, 2), np.float32)
+    for l in range(L):
+        H, W = shapes[l]
+        loc[:, :, :, l, :, 0] = (rng.uniform(1e-3, W - 1 - 1e-3, (B, Nq, M, K)) + 0.5) / W
+        loc[:, :, :, l, :, 1] = (rng.uniform(1e-3, H - 1 - 1e-3, (B, Nq, M, K)) + 0.5) / H
+    attn = rng.standard_normal((B, Nq, M, L, K))
+    g = rng.standard_normal((B, Nq, M, D))
+    out = fwd(lib, value, shapes, lsi, loc, attn)
+    _, gl, ga = bwd(lib, value, shapes, lsi, loc, attn, g)
+    exp_out = np.zeros((B, Nq, M, D))
+    exp_ga = np.zeros((B, Nq, M, L, K))
+    exp_gl = np.zeros((B, Nq, M, L, K, 2))
+    for l in range(L):
+        H, W = shapes[l]
+        x = coord32(loc[..., l, :, 0], W).astype(np.float64)    # [B,Nq,M,K]
+        y = coord32(loc[..., l, :, 1], H).astype(np.float64)
+        a0, bx, cy, dxy = [coef[:, l, :, :, i][:, None, :, None, :] for i in range(4)]
+        s = a0 + bx * x[..., None] + cy * y[..., None] + dxy * (x * y)[..., None]   # [B,Nq,M,K,D]
+        a = attn[..., l, :]
+        exp_out += np.einsum("bqmk,bqmkd->bqmd", a, s)
+        gq = g[:, :, :, None, :]
+        exp_ga[..., l, :] = (gq * s).sum(-1)
+        exp_gl[..., l, :, 0] = W * a * (gq * (bx + dxy * y[..., None])).sum(-1)
+        exp_gl[..., l, :, 1] = H * a * (gq * (cy + dxy * x[..., None])).sum(-1)
+    _close(out, exp_out, 1e-12, "bilinear field, forward")
+    _close(ga, exp_ga, 1e-12, "bilinear field, weight gradient")
+    _close(gl, exp_gl, 1e-11, "bilinear field, location gradient")
+
+
+def pin_out_of_bounds(lib=None):
+    """Zero padding per corner: a sample whose four corners are all outside the
+    level contributes nothing and receives zero gradients; a sample straddling
+    the left edge keeps only the inside column's weight (no renormalization);
+    non-finite locations count as outside."""
+    shapes, lsi = level_tables(((4, 6),))
+    H, W = 4, 6
+    B, M, D, K = 1, 1, 2, 1
+    value = np.arange(1, 1 + 24 * D, dtype=np.float64).reshape(B, 24, M, D)
+    # all-outside samples: x <= -1 - eps, x >= W, y <= -1 - eps, y >= H, NaN, Inf
+    far = [(-1.02 / W, 0.5), ((W + 0.01 + 0.5) / W, 0.5), (0.5, -0.3),
+           (0.5, (H + 0.2 + 0.5) / H), (np.nan, 0.5), (0.5, np.inf), (-np.inf, np.nan),
+           (1e30, 0.5), (-1e30, -1e30)]
+    for u, v in far:
+        loc = np.array([u, v], np.float32).reshape(1, 1, 1, 1, 1, 2)
+        attn = np.ones((1, 1, 1, 1, 1))
+        g = np.ones((1, 1, 1, D))
+        out = fwd(lib, value, shapes, lsi, loc, attn)
+        gv, gl, ga = bwd(lib, value, shapes, lsi, loc, attn, g)
+        assert np.all(out == 0.0), f"outside sample ({u},{v}) contributed {out}"
+        assert np.all(gv == 0.0) and np.all(gl == 0.0) and np.all(ga == 0.0), \
+            f"outside sample ({u},{v}) has a nonzero gradient"
+    # straddling the left edge: x = -0.25 -> only column 0 with weight 0.75
+    row = 2
+    u, v = np.float32(0.25 / W), np.float32((row + 0.5) / H)   # x = -0.25, y = row
+    loc = np.array([u, v], np.float32).reshape(1, 1, 1, 1, 1, 2)
+    out = fwd(lib, value, shapes, lsi, loc, np.full((1, 1, 1, 1, 1), 2.0))
+    expect = 2.0 * 0.75 * value[0, row * W + 0, 0]
+    np.testing.assert_allclose(out.reshape(-1), expect, rtol=1e-15, atol=0,
+                               err_msg="edge sample must keep the in-level weight only")
+
+
+def pin_linearity(lib=None):
+    """The output is linear in the value field and in the weights: scaling
+    either by 2 scales it exactly; adding fields adds outputs."""
+    rng = np.random.default_rng(14)
+    value, shapes, lsi, loc, attn, _ = random_case(rng)
+    o = fwd(lib, value, shapes, lsi, loc, attn)
+    assert np.array_equal(fwd(lib, 2 * value, shapes, lsi, loc, attn), 2 * o)
+    assert np.array_equal(fwd(lib, value, shapes, lsi, loc, 2 * attn), 2 * o)
+    v2 = rng.standard_normal(value.shape)
+    _close(fwd(lib, value + v2, shapes, lsi, loc, attn), o + fwd(lib, v2, shapes, lsi, loc, attn),
+           1e-13, "additivity in the value field")
+
+
+def _grid_sample_reference(value, shapes, lsi, loc, attn, g):
+    """Per-level torch grid_sample (bilinear, zeros padding, align_corners
+    False), weighted by A and summed, in float64 with autograd -- the library
+    routine the cf-1.com fallback (section 5.3) names. The grid is rebuilt from
+    the single-precision pixel coordinates so that both sides sample the same
+    point."""
+    import torch
+    import torch.nn.functional as F
+    B, Nv, M, D = value.shape
+    _, Nq, _, L, K, _ = loc.shape
+    V = torch.tensor(value, dtype=torch.float64, requires_grad=True)
+    A = torch.tensor(attn, dtype=torch.float64, requires_grad=True)
+    # normalized location reproducing the fp32 pixel coordinate: u' = (x32 + 0.5) / W
+    u_in = np.empty(loc.shape, np.float64)
+    for l in range(L):
+        H, W = shapes[l]
+        u_in[..., l, :, 0] = (coord32(loc[..., l, :, 0], W).astype(np.float64) + 0.5) / W
+        u_in[..., l, :, 1] = (coord32(loc[..., l, :, 1], H).astype(np.float64) + 0.5) / H
+    U = torch.tensor(u_in, requires_grad=True)
+    out = torch.zeros(B, Nq, M, D, dtype=torch.float64)
+    for l in range(L):
+        H, W = int(shapes[l][0]), int(shapes[l][1])
+        v_l = V[:, lsi[l]:lsi[l] + H * W]                               # [B, HW, M, D]
+        v_l = v_l.permute(0, 2, 3, 1).reshape(B * M, D, H, W)
+        grid = 2.0 * U[:, :, :, l] - 1.0                                # [B, Nq, M, K, 2]
+        grid = grid.permute(0, 2, 1, 3, 4).reshape(B * M, Nq, K, 2)
+        s = F.grid_sample(v_l, grid, mode="bilinear", padding_mode="zeros",
+                          align_corners=False)                          # [B*M, D, Nq, K]
+        s = s.reshape(B, M, D, Nq, K).permute(0, 3, 1, 4, 2)            # [B, Nq, M, K, D]
+        out = out + (A[:, :, :, l, :, None] * s).sum(3)
+    G = torch.tensor(g, dtype=torch.float64)
+    (out * G).sum().backward()
+    return (out.detach().numpy(), V.grad.numpy(), U.grad.numpy(), A.grad.numpy())
+
+
+def pin_grid_sample(lib=None):
+    """Forward and backward equal the per-level grid_sample formulation
+    (library routine, independent code) on random inputs with out-of-level
+    samples."""
+    for seed in (15, 16):
+        rng = np.random.default_rng(seed)
+        value, shapes, lsi, loc, attn, g = random_case(rng)
+        ro, rgv, rgl, rga = _grid_sample_reference(value, shapes, lsi, loc, attn, g)
+        o = fwd(lib, value, shapes, lsi, loc, attn)
+        gv, gl, ga = bwd(lib, value, shapes, lsi, loc, attn, g)
+        _close(o, ro, 1e-12, "forward vs grid_sample")
+        _close(gv, rgv, 1e-12, "value gradient vs grid_sample")
+        _close(ga, rga, 1e-12, "weight gradient vs grid_sample")
+        _close(gl, rgl, 1e-10, "location gradient vs grid_sample")
+
+
+def _tent_dense(value, shapes, lsi, loc, attn, g):
+    """Brute force without floor(): every pixel n of level l is weighted by the
+    tent kernel max(0, 1-|x-x_n|) * max(0, 1-|y-y_n|); the output is the
+    dense weighted sum over all Nv pixels. Gradients by differentiating the
+    tent kernel (valid away from kinks)."""
+    B, Nv, M, D = value.shape
+    _, Nq, _, L, K, _ = loc.shape
+    out = np.zeros((B, Nq, M, D))
+    gv = np.zeros_like(value)
+    gl = np.zeros(loc.shape)
+    ga = np.zeros(attn.shape)
+    for l in range(L):
+        H, W = shapes[l]
+        yy, xx = np.meshgrid(np.arange(H), np.arange(W), indexing="ij")
+        xn, yn = xx.reshape(-1).astype(np.float64), yy.reshape(-1).astype(np.float64)
+        vl = value[:, lsi[l]:lsi[l] + H * W]                          # [B, HW, M, D]
+        x = coord32(loc[..., l, :, 0], W).astype(np.float64)[..., None]   # [B,Nq,M,K,1]
+        y = coord32(loc[..., l, :, 1], H).astype(np.float64)[..., None]
+        tx = np.maximum(0.0, 1.0 - np.abs(x - xn))
+        ty = np.maximum(0.0, 1.0 - np.abs(y - yn))
+        dtx = np.where(np.abs(x - xn) < 1.0, -np.sign(x - xn), 0.0)
+        dty = np.where(np.abs(y - yn) < 1.0, -np.sign(y - yn), 0.0)
+        wt = tx * ty                                                  # [B,Nq,M,K,HW]
+        a = attn[..., l, :]                                           # [B,Nq,M,K]
+        s = np.einsum("bqmkn,bnmd->bqmkd", wt, vl)
+        out += np.einsum("bqmk,bqmkd->bqmd", a, s)
+        gs = np.einsum("bqmd,bqmkd->bqmk", g, s)
+        ga[..., l, :] = gs
+        gdot = np.einsum("bqmd,bnmd->bqmn", g, vl)[:, :, :, None, :]  # [B,Nq,M,1,HW]
+        gl[..., l, :, 0] = W * a * (dtx * ty * gdot).sum(-1)
+        gl[..., l, :, 1] = H * a * (tx * dty * gdot).sum(-1)
+        gv[:, lsi[l]:lsi[l] + H * W] += np.einsum("bqmk,bqmkn,bqmd->bnmd", a, wt, g)
+    return out, gv, gl, ga
+
+
+def pin_brute_force(lib=None):
+    """Dense tent-kernel brute force over every pixel (no floor, no corner
+    enumeration) on tiny inputs."""
+    for seed in (17, 18, 19):
+        rng = np.random.default_rng(seed)
+        value, shapes, lsi, loc, attn, g = random_case(rng, lo=-0.3, hi=1.3)
+        ro, rgv, rgl, rga = _tent_dense(value, shapes, lsi, loc, attn, g)
+        o = fwd(lib, value, shapes, lsi, loc, attn)
+        gv, gl, ga = bwd(lib, value, shapes, lsi, loc, attn, g)
+        _close(o, ro, 1e-12, "forward vs tent brute force")
+        _close(gv, rgv, 1e-12, "value gradient vs tent brute force")
+        _close(ga, rga, 1e-12, "weight gradient vs tent brute force")
+        _close(gl, rgl, 1e-11, "location gradient vs tent brute force")
+
+
+def pin_finite_differences(lib=None):
+    """Analytic gradients equal finite differences of L = sum(g * out).
+    L is linear in the value and the weights (central differences are exact);
+    inside one cell it is linear in x at fixed y, so the difference quotient
+    over the actual fp32 coordinates is exact too."""
+    rng = np.random.default_rng(20)
+    value, shapes, lsi, loc, attn, g = random_case(rng, B=1, M=2, D=3, Nq=3, K=2,
+                                                   shapes=((4, 5), (3, 3)))
+    loss = lambda v, lc, a: float((fwd(lib, v, shapes, lsi, lc, a) * g).sum())  # noqa: E731
+    gv, gl, ga = bwd(lib, value, shapes, lsi, loc, attn, g)
+    # value and weights
+    for idx in np.ndindex(*value.shape):
+        vp, vm = value.copy(), value.copy()
+        vp[idx] += 0.5
+        vm[idx] -= 0.5
+        fd = loss(vp, loc, attn) - loss(vm, loc, attn)
+        assert abs(fd - gv[idx]) <= 1e-12 * max(1.0, abs(fd)), f"d/dvalue{idx}"
+    for idx in np.ndindex(*attn.shape):
+        ap, am = attn.copy(), attn.copy()
+        ap[idx] += 0.5
+        am[idx] -= 0.5
+        fd = loss(value, loc, ap) - loss(value, loc, am)
+        assert abs(fd - ga[idx]) <= 1e-12 * max(1.0, abs(fd)), f"d/dweight{idx}"
+    # locations: step 2^-12 in normalized units, skipped when the step crosses a cell
+    h = np.float32(2.0 ** -12)
+    checked = 0
+    for idx in np.ndindex(*loc.shape):
+        l, axis = idx[3], idx[5]
+        n = shapes[l][1] if axis == 0 else shapes[l][0]
+        lp, lm = loc.copy(), loc.copy()
+        lp[idx] = np.float32(loc[idx] + h)
+        lm[idx] = np.float32(loc[idx] - h)
+        xp, xm = coord32(lp[idx], n), coord32(lm[idx], n)
+        if np.floor(xp) != np.floor(xm) or np.floor(xm) != np.floor(coord32(loc[idx], n)):
+            continue
+        fd = (loss(value, lp, attn) - loss(value, lm, attn)) / (float(xp) - float(xm)) * n
+        assert abs(fd - gl[idx]) <= 1e-9 * max(1.0, abs(fd)), f"d/dloc{idx}: {fd} vs {gl[idx]}"
+        checked += 1
+    assert checked > loc.size // 2, "too few location coordinates checked"
+
+
+def pin_single_scale_resampling(lib=None):
+    """With one level, one point and one head, the core is plain bilinear
+    resampling of one image with zero padding: scipy.ndimage.map_coordinates
+    (order 1, mode 'grid-constant', cval 0)."""
+    from scipy import ndimage
+    rng = np.random.default_rng(21)
+    H, W, D, Nq = 7, 10, 3, 50
+    shapes, lsi = level_tables(((H, W),))
+    value = rng.standard_normal((1, H * W, 1, D))
+    loc = rng.uniform(-0.2, 1.2, size=(1, Nq, 1, 1, 1, 2)).astype(np.float32)
+    attn = np.ones((1, Nq, 1, 1, 1))
+    out = fwd(lib, value, shapes, lsi, loc, attn)[0, :, 0]           # [Nq, D]
+    x = coord32(loc[0, :, 0, 0, 0, 0], W).astype(np.float64)
+    y = coord32(loc[0, :, 0, 0, 0, 1], H).astype(np.float64)
+    for d in range(D):
+        img = value[0, :, 0, d].reshape(H, W)
+        ref = ndimage.map_coordinates(img, [y, x], order=1, mode="grid-constant", cval=0.0,
+                                      prefilter=False)
+        _close(out[:, d], ref, 1e-12, "single-scale resampling vs map_coordinates")
+
+
+def pin_scatter_conservation(lib=None):
+    """Summing the value gradient over all pixels gives, per (b, m, d),
+    sum over samples of A * (sum of the inside corners' weights) * g; with
+    every corner inside and softmax weights that is sum_q g."""
+    rng = np.random.default_rng(22)
+    shapes, lsi = level_tables(((6, 8), (3, 4)))
+    B, M, D, K, Nq, L = 2, 2, 4, 3, 10, 2
+    Nv = int((shapes[:, 0] * shapes[:, 1]).sum())
+    value = rng.standard_normal((B, Nv, M, D))
+    loc = np.empty((B, Nq, M, L, K, 2), np.float32)
+    for l in range(L):
+        H, W = shapes[l]
+        loc[..., l, :, 0] = (rng.uniform(0, W - 1 - 1e-3, (B, Nq, M, K)) + 0.5) / W
+        loc[..., l, :, 1] = (rng.uniform(0, H - 1 - 1e-3, (B, Nq, M, K)) + 0.5) / H
+    logits = rng.standard_normal((B, Nq, M, L * K))
+    attn = (np.exp(logits) / np.exp(logits).sum(-1, keepdims=True)).reshape(B, Nq, M, L, K)
+    g = rng.standard_normal((B, Nq, M, D))
+    gv, _, _ = bwd(lib, value, shapes, lsi, loc, attn, g)
+    _close(gv.sum(1), g.sum(1), 1e-12, "value-gradient conservation")
+
+
+def pin_permutation(lib=None):
+    """Permuting queries, heads or batch entries (with their locations and
+    weights) permutes the outputs the same way."""
+    rng = np.random.default_rng(23)
+    value, shapes, lsi, loc, attn, g = random_case(rng)
+    o = fwd(lib, value, shapes, lsi, loc, attn)
+    pq = rng.permutation(loc.shape[1])
+    assert np.array_equal(fwd(lib, value, shapes, lsi, loc[:, pq], attn[:, pq]), o[:, pq])
+    pm = rng.permutation(value.shape[2])
+    assert np.array_equal(fwd(lib, value[:, :, pm], shapes, lsi, loc[:, :, pm], attn[:, :, pm]),
+                          o[:, :, pm])
+    pb = rng.permutation(value.shape[0])
+    assert np.array_equal(fwd(lib, value[pb], shapes, lsi, loc[pb], attn[pb]), o[pb])
+
+
+ALL_PINS = [pin_golden_hand_worked, pin_pixel_centres, pin_constant_field, pin_bilinear_field,
+            pin_out_of_bounds, pin_linearity, pin_grid_sample, pin_brute_force,
+            pin_finite_differences, pin_single_scale_resampling, pin_scatter_conservation,
+            pin_permutation]

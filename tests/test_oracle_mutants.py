@@ -1,0 +1,74 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in a copy of the oracle's C source (on the CPU,
+in a temporary directory), builds it, and runs the pins against that build in
+a child process. The planted mistake must make at least one pin fail (or the
+child crash). The in-tree oracle is never modified.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SOURCE = os.path.join(ROOT, "oracle", "msda_oracle.c")
+
+MUTANTS = {
+    "no_half_pixel": ("fmaf(u, (float)W, -0.5f)", "fmaf(u, (float)W, 0.0f)"),
+    "corner_aligned_scale": ("fmaf(u, (float)W, -0.5f)", "u * (float)(W - 1)"),
+    "swapped_axes": ("*x = (double)fmaf(u, (float)W, -0.5f);\n    *y = (double)fmaf(v, (float)H, -0.5f);",
+                     "*x = (double)fmaf(u, (float)H, -0.5f);\n    *y = (double)fmaf(v, (float)W, -0.5f);"),
+    "swapped_x_weights": ("const double wx = dx ? fx : 1.0 - fx;", "const double wx = dx ? 1.0 - fx : fx;"),
+    "swapped_y_weights": ("const double wy = dy ? fy : 1.0 - fy;", "const double wy = dy ? 1.0 - fy : fy;"),
+    "bounds_off_by_one": ("(xc < (double)W)", "(xc <= (double)W - 0.0 + 0.0 && xc < (double)W + 1.0)"),
+    "no_row_bound": ("&& (yc >= 0.0) ", "&& 1 "),
+    "row_stride_H": ("start + (int64_t)yc * W + (int64_t)xc", "start + (int64_t)yc * (W > 1 ? W - 1 : 1) + (int64_t)xc"),
+    "no_level_start": ("bilinear_corners(x, y, H, W, lsi[l], c);", "bilinear_corners(x, y, H, W, 0, c);"),
+    "forward_drops_weight": ("const double t = a * c[i].w * v[d];", "const double t = c[i].w * v[d];"),
+    "forward_wrong_head": ("const double *v = value + ((b * Nv + c[i].row) * M + m) * D;",
+                           "const double *v = value + ((b * Nv + c[i].row) * M + (M - 1 - m)) * D;"),
+    "dx_sign": ("k->dw_dx = (dx ? 1.0 : -1.0) * wy;", "k->dw_dx = (dx ? -1.0 : 1.0) * wy;"),
+    "dy_uses_wrong_factor": ("k->dw_dy = (dy ? 1.0 : -1.0) * wx;", "k->dw_dy = (dy ? 1.0 : -1.0) * wy;"),
+    "loc_grad_chain_H_for_x": ("grad_loc[2 * p] = a * gx * (double)W;", "grad_loc[2 * p] = a * gx * (double)H;"),
+    "loc_grad_drops_A": ("grad_loc[2 * p + 1] = a * gy * (double)H;", "grad_loc[2 * p + 1] = gy * (double)H;"),
+    "attn_grad_drops_g": ("ga += g[d] * s;", "ga += s;"),
+    "value_grad_drops_A": ("const double t = a * c[i].w * g[d];", "const double t = c[i].w * g[d];"),
+    "value_grad_wrong_corner_weight": ("const double t = a * c[i].w * g[d];", "const double t = a * c[3 - i].w * g[d];"),
+}
+
+CHILD = r"""
+import sys
+sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
+import oracle, pins
+lib = oracle.library({lib!r})
+for pin in pins.ALL_PINS:
+    try:
+        pin(lib)
+    except Exception as e:
+        print("CAUGHT", pin.__name__, type(e).__name__)
+        sys.exit(0)
+print("SURVIVED")
+sys.exit(3)
+"""
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name):
+    old, new = MUTANTS[name]
+    src = open(SOURCE).read()
+    assert old in src, f"mutation site for {name} not found in the oracle source"
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "mutant.c")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        lib = os.path.join(tmp, "libmutant.so")
+        subprocess.run(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
+                        path, "-o", lib, "-lm"], check=True)
+        child = CHILD.format(root=ROOT, tests=os.path.join(ROOT, "tests"), lib=lib)
+        r = subprocess.run([sys.executable, "-c", child], capture_output=True, text=True,
+                           timeout=300)
+    # a crash (negative return code) also counts as caught
+    assert r.returncode != 3, f"mutant {name} survived every pin:\n{r.stdout}\n{r.stderr}"
+    assert r.returncode == 0 or r.returncode < 0, f"child failed: {r.stdout}\n{r.stderr}"
