@@ -1,0 +1,205 @@
+"""Benchmark of the deformable attention core on one MI355X.
+
+One step = one pass of the whole hot path over one batch: msda_forward, then
+msda_backward (grad_value zero fill + the gather/scatter backward kernel),
+on the 800x1333 encoder training workload (B=4, M=8, D=32, L=4 levels
+(100,167),(50,84),(25,42),(13,21), K=4, Nq=Nv=22223, offsets N(0, 8 px),
+fp32). Inputs are synthetic (seeded), resident in HBM before timing starts.
+
+Prints ONE JSON line: points/s over the K timed steps (points =
+B*Nq*M*L*K per step), the roofline of the dominant kernel (the backward
+gather/scatter kernel) measured live with HIP events on the launch stream, and
+the CPU oracle's rate on the host (a bounded sample of the same workload).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+METRIC = "sampled points/sec (B·Nq·M·L·K) fwd+bwd; achieved HBM GB/s vs peak"
+
+
+def algorithmic_bytes(w, value_bytes_per_elem=4):
+    """Compulsory bytes of each launch (each input read once, each output
+    written once). Per sampled point: location 8 B + weight 4 B (+ their
+    gradients 8 B + 4 B in the backward). Per (b,q,m): D*4 B of output (or
+    upstream gradient). Per value element: read once (+ grad_value written
+    once in the backward)."""
+    P = w.points
+    T = w.B * w.num_queries * w.M
+    V = w.B * w.Nv * w.M * w.D
+    fwd = V * value_bytes_per_elem + P * 12 + T * w.D * 4
+    bwd_kernel = V * value_bytes_per_elem + P * 12 + T * w.D * 4 + V * 4 + P * 12
+    zero_fill = V * 4
+    return {"forward": fwd, "backward": bwd_kernel, "zero_fill": zero_fill,
+            "step": fwd + bwd_kernel}
+
+
+def cpu_baseline(w, x, budget_s):
+    """The oracle as it stands (single thread) on a bounded sample: whole batch
+    entries of the workload, forward + backward, until the budget is used."""
+    import oracle
+    done_points, t_total, batches = 0, 0.0, 0
+    per_batch = w.points // w.B
+    for b in range(w.B):
+        sl = slice(b, b + 1)
+        args = (x["value"][sl], x["spatial_shapes"], x["level_start_index"],
+                x["sampling_locations"][sl], x["attention_weights"][sl])
+        t0 = time.perf_counter()
+        oracle.forward(*args)
+        oracle.backward(*args, x["grad_output"][sl])
+        t_total += time.perf_counter() - t0
+        done_points += per_batch
+        batches += 1
+        if t_total >= budget_s:
+            break
+    return {"value": done_points / t_total, "unit": "points/s", "cores": 1, "kind": "oracle",
+            "sample": f"{batches} of {w.B} batch entries of the same workload, forward + "
+                      f"backward, {done_points} points in {t_total:.1f} s, single thread, "
+                      f"double accumulation"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="encoder_train")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline sample")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the core runs on a single MI355X; sharding across "
+              "GPUs (batch or head split) is described in DESIGN.md but not run here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import scale_deformable_attention_amd as msda
+    from scale_deformable_attention_amd import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    msda.library()
+    x = wl.generate(w)
+    if w.value_dtype == "bf16":
+        value = torch.from_numpy(x["value_bf16"].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        value = torch.from_numpy(x["value"]).to(dev)
+    shapes = torch.from_numpy(x["spatial_shapes"]).to(dev)
+    lsi = torch.from_numpy(x["level_start_index"]).to(dev)
+    loc = torch.from_numpy(x["sampling_locations"]).to(dev)
+    attn = torch.from_numpy(x["attention_weights"]).to(dev)
+    gout = torch.from_numpy(x["grad_output"]).to(dev)
+    out = torch.empty(w.B, w.num_queries, w.M * w.D, device=dev)
+    gv = torch.empty(w.B, w.Nv, w.M, w.D, device=dev)
+    gl = torch.empty_like(loc)
+    ga = torch.empty_like(attn)
+    backward = w.backward
+
+    def step():
+        msda.msda_forward(value, shapes, lsi, loc, attn, output=out)
+        if backward:
+            msda.msda_backward(value, shapes, lsi, loc, attn, gout, grad_value=gv,
+                               grad_sampling_locations=gl, grad_attention_weights=ga)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)   # the library launches on this stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for e in ev:
+        e[0].record(stream)
+        msda.msda_forward(value, shapes, lsi, loc, attn, output=out)
+        e[1].record(stream)
+        if backward:
+            msda.msda_backward(value, shapes, lsi, loc, attn, gout, grad_value=gv,
+                               grad_sampling_locations=gl, grad_attention_weights=ga)
+        e[2].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_entry_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) if backward else 0.0
+
+    # the zero fill alone, live on the same stream: msda_backward with no
+    # queries launches only the fill of grad_value (same size as in the step)
+    zero_ms = 0.0
+    if backward:
+        loc0 = torch.empty(w.B, 0, w.M, w.L, w.K, 2, device=dev)
+        attn0 = torch.empty(w.B, 0, w.M, w.L, w.K, device=dev)
+        g0 = torch.empty(w.B, 0, w.M * w.D, device=dev)
+        zf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for _ in range(args.warmup):
+            msda.msda_backward(value, shapes, lsi, loc0, attn0, g0, grad_value=gv)
+        torch.cuda.synchronize()
+        for e in zf:
+            e[0].record(stream)
+            msda.msda_backward(value, shapes, lsi, loc0, attn0, g0, grad_value=gv)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        zero_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in zf]))
+        # leave the real gradients in place for anyone inspecting them
+        step()
+        torch.cuda.synchronize()
+
+    ms_per_step = total_ms / args.steps
+    pts_per_s = w.points / (ms_per_step * 1e-3)
+    ab = algorithmic_bytes(w, 2 if w.value_dtype == "bf16" else 4)
+    if backward:
+        dom_name, dom_ms = "msda_bwd_kernel", max(bwd_entry_ms - zero_ms, 1e-9)
+        dom_bytes = ab["backward"]
+    else:
+        dom_name, dom_ms, dom_bytes = "msda_fwd_kernel", fwd_ms, ab["forward"]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    step_gbs = (ab["step"] if backward else ab["forward"]) / (ms_per_step * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": pts_per_s,
+        "unit": "points/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.value_dtype == "f32" else "bf16 value, f32 math",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.note}; B={w.B} M={w.M} D={w.D} L={w.L} K={w.K} "
+                               f"Nq=Nv={w.Nv} shapes={list(w.shapes)} offsets N(0,{w.sigma_px} px)",
+                   "points_per_step": w.points, "global_batch": w.B, "parallelism": "none"},
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes": dom_bytes, "avg_ms": dom_ms},
+        "step_roofline": {"algorithmic_bytes": ab["step"] if backward else ab["forward"],
+                          "achieved": step_gbs, "frac": step_gbs / HBM_PEAK_GBS},
+        "kernels_ms": {"forward": fwd_ms, "backward_entry": bwd_entry_ms,
+                       "zero_fill": zero_ms, "backward_kernel": bwd_entry_ms - zero_ms},
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * msda.h -- C ABI of the MI355X (gfx950) multi-scale deformable attention core.
+ *
+ * The core is the step of multi-scale deformable attention that sits between
+ * the value projection and the output projection: for every query q, head m,
+ * level l and point k it samples the flattened multi-level value tensor at a
+ * learned location and sums the samples weighted by A_mlqk:
+ *
+ *   out[b,q,m,:] = sum_l sum_k A[b,q,m,l,k] * bilinear_l,m( phi_l(loc[b,q,m,l,k]) )
+ *
+ * Sources (pages on deformable attention):
+ *   - the MSDeformAttn equation: deformable-attention tutorial (discosf.com),
+ *     section 2.2; DETR-to-Deformable-DETR article (cf-1.com), section 3.1;
+ *     CSDN MSDA explainer, section 2 (core formula);
+ *   - phi_l, the cell-centre map of a normalized location to level pixels,
+ *     x = u*W_l - 0.5, y = v*H_l - 0.5 (grid_sample with align_corners=False
+ *     in the cf-1.com fallback, section 5.3; CSDN explainer section 3 note 2);
+ *   - bilinear interpolation over the four surrounding pixels, with zero for
+ *     pixels outside the level (discosf.com sections 2.1, 2.2 and 3.2;
+ *     padding_mode 'zeros' in cf-1.com 5.3);
+ *   - the flattened multi-level layout with spatial_shapes rows (H, W) and
+ *     level_start_index (cf-1.com section 3.3);
+ *   - the gradients of the same expression, flowing through the bilinear
+ *     weights (discosf.com section 3.2).
+ *
+ * Layouts: dense, row-major, contiguous.
+ *   value               [B, Nv, M, D]        value_dtype (fp32 or bf16)
+ *   spatial_shapes      [L, 2] int64         rows (H_l, W_l)
+ *   level_start_index   [L] int64            first row of level l in Nv
+ *   sampling_locations  [B, Nq, M, L, K, 2]  fp32, (x, y) normalized to [0,1]
+ *                                            (any value is accepted: outside
+ *                                            the level reads as zero; NaN and
+ *                                            Inf read as outside)
+ *   attention_weights   [B, Nq, M, L, K]     fp32, used as given
+ *   output, grad_output [B, Nq, M*D]         fp32, heads concatenated
+ *   grad_value          [B, Nv, M, D]        fp32 (whatever value_dtype is)
+ *   grad_sampling_locations [B, Nq, M, L, K, 2] fp32
+ *   grad_attention_weights  [B, Nq, M, L, K]    fp32
+ *
+ * Ownership: every tensor pointer is a DEVICE pointer owned by the caller; a
+ * pointer to a tensor with no elements may be NULL.
+ * The library allocates nothing, keeps no pointer after a call returns, holds
+ * no state and may be called from several host threads. All work is enqueued
+ * on `stream` (0 = the null stream) with no host synchronization; results are
+ * ready when the stream reaches them. Outputs are overwritten, never
+ * accumulated into.
+ *
+ * Errors: arguments are checked on the host before anything is enqueued; a
+ * failed check launches nothing and returns MSDA_ERROR_INVALID_VALUE or
+ * MSDA_ERROR_NOT_SUPPORTED. A launch failure returns MSDA_ERROR_LAUNCH.
+ * The level tables live on the device and are NOT read back (that would cost
+ * a synchronization): the caller guarantees H_l, W_l >= 1, sum H_l*W_l == Nv
+ * and level_start_index = the prefix sums. msda_check_tables checks a host
+ * copy of them.
+ */
+#ifndef MSDA_H_
+#define MSDA_H_
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSDA_VERSION_MAJOR 0
+#define MSDA_VERSION_MINOR 1
+#define MSDA_VERSION_PATCH 0
+
+/* Largest number of feature levels the kernels accept. */
+#define MSDA_MAX_LEVELS 16
+
+typedef enum {
+    MSDA_DTYPE_F32 = 0,  /* value stored as IEEE binary32            */
+    MSDA_DTYPE_BF16 = 1  /* value stored as bfloat16 (fp32 math)      */
+} msda_dtype_t;
+
+typedef enum {
+    MSDA_SUCCESS = 0,
+    MSDA_ERROR_INVALID_VALUE = 1, /* NULL/unaligned pointer, negative or inconsistent size */
+    MSDA_ERROR_NOT_SUPPORTED = 2, /* valid request outside what the kernels implement      */
+    MSDA_ERROR_LAUNCH = 3         /* the HIP runtime refused a launch                      */
+} msda_status_t;
+
+/* Problem sizes. B, Nq and K may be 0 (empty work; outputs are still
+ * written: zeros where the sum is empty). M >= 1, L in [1, MSDA_MAX_LEVELS],
+ * Nv >= 1, D in {8, 16, 32, 64}. */
+typedef struct {
+    int64_t B;  /* batch                       */
+    int64_t Nv; /* value rows = sum H_l * W_l  */
+    int64_t M;  /* heads                       */
+    int64_t D;  /* channels per head           */
+    int64_t L;  /* levels                      */
+    int64_t Nq; /* queries                     */
+    int64_t K;  /* points per head and level   */
+} msda_dims_t;
+
+/*
+ * Forward: output[b,q,m*D+d] = sum_{l,k} A * sum_{corners c inside level l}
+ *                              w_c * value[b, s_l + y_c*W_l + x_c, m, d]
+ * computed in fp32 (bf16 values are widened exactly).
+ *
+ * Pointer requirements: value and output 16-byte aligned; sampling_locations
+ * 8-byte aligned; the rest 4-byte aligned (int64 tables 8-byte).
+ * Size limit: the value tensor must be smaller than 2 GiB (32-bit buffer
+ * offsets); larger requests return MSDA_ERROR_NOT_SUPPORTED (split the batch).
+ */
+msda_status_t msda_forward(const msda_dims_t *dims, msda_dtype_t value_dtype,
+                           const void *value, const int64_t *spatial_shapes,
+                           const int64_t *level_start_index, const float *sampling_locations,
+                           const float *attention_weights, float *output, hipStream_t stream);
+
+/*
+ * Backward of msda_forward for the upstream gradient grad_output:
+ *   grad_attention_weights[b,q,m,l,k]  = sum_d g[d] * s[d]
+ *   grad_sampling_locations[...,0]     = A * W_l * sum_d g[d] * ds[d]/dx
+ *   grad_sampling_locations[...,1]     = A * H_l * sum_d g[d] * ds[d]/dy
+ *   grad_value[b,row_c,m,d]           += A * w_c * g[d]   (corners inside)
+ * where g = grad_output[b,q,m*D:(m+1)*D] and s is the bilinear sample. At an
+ * exact integer pixel coordinate the derivative is the one of the cell that
+ * floor() selects (the right-sided derivative).
+ *
+ * grad_value is zero-filled by the library on `stream` and then accumulated
+ * with fp32 atomics, so its low bits may differ from run to run (summation
+ * order). Any of the three gradient pointers may be NULL to skip that
+ * gradient. Alignment: value, grad_output and grad_value 16-byte;
+ * sampling_locations and grad_sampling_locations 8-byte; others 4-byte.
+ * Size limit: grad_value (fp32, same shape as value) smaller than 2 GiB.
+ */
+msda_status_t msda_backward(const msda_dims_t *dims, msda_dtype_t value_dtype,
+                            const void *value, const int64_t *spatial_shapes,
+                            const int64_t *level_start_index, const float *sampling_locations,
+                            const float *attention_weights, const float *grad_output,
+                            float *grad_value, float *grad_sampling_locations,
+                            float *grad_attention_weights, hipStream_t stream);
+
+/* Host-side check of a HOST copy of the level tables against Nv: every
+ * H_l, W_l >= 1, level_start_index the prefix sums, sum H_l*W_l == Nv.
+ * Returns MSDA_SUCCESS or MSDA_ERROR_INVALID_VALUE. No HIP call. */
+msda_status_t msda_check_tables(const int64_t *host_spatial_shapes,
+                                const int64_t *host_level_start_index, int64_t L, int64_t Nv);
+
+/* Static description of a status code (never NULL). */
+const char *msda_status_string(msda_status_t status);
+
+/* MAJOR*10000 + MINOR*100 + PATCH. */
+int msda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSDA_H_ */

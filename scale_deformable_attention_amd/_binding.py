@@ -1,0 +1,215 @@
+"""ctypes binding of libmsda.so (include/msda.h): argument marshalling only.
+
+Every step of the core runs in the library's HIP kernels; this module checks
+tensor shapes, dtypes and devices, allocates outputs with torch (device memory
+is torch's), passes raw device pointers and the current HIP stream, and turns
+a non-zero status into an exception. There is no fallback path: without the
+built library every call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsda.so")
+
+MSDA_DTYPE_F32 = 0
+MSDA_DTYPE_BF16 = 1
+STATUS = {0: "MSDA_SUCCESS", 1: "MSDA_ERROR_INVALID_VALUE", 2: "MSDA_ERROR_NOT_SUPPORTED",
+          3: "MSDA_ERROR_LAUNCH"}
+
+
+class MsdaDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("B", "Nv", "M", "D", "L", "Nq", "K")]
+
+
+class MsdaError(RuntimeError):
+    def __init__(self, status, where):
+        super().__init__(f"{where}: {STATUS.get(status, status)} "
+                         f"({library().msda_status_string(status).decode()})")
+        self.status = status
+
+
+_LIB = None
+
+
+def library():
+    """Load libmsda.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(f"{LIBRARY} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(LIBRARY)
+        vp, i64p, fp = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+        lib.msda_forward.restype = ctypes.c_int
+        lib.msda_forward.argtypes = [ctypes.POINTER(MsdaDims), ctypes.c_int, vp, i64p, i64p, fp,
+                                     fp, fp, vp]
+        lib.msda_backward.restype = ctypes.c_int
+        lib.msda_backward.argtypes = [ctypes.POINTER(MsdaDims), ctypes.c_int, vp, i64p, i64p, fp,
+                                      fp, fp, fp, fp, fp, vp]
+        lib.msda_check_tables.restype = ctypes.c_int
+        lib.msda_check_tables.argtypes = [i64p, i64p, ctypes.c_int64, ctypes.c_int64]
+        lib.msda_status_string.restype = ctypes.c_char_p
+        lib.msda_status_string.argtypes = [ctypes.c_int]
+        lib.msda_version.restype = ctypes.c_int
+        lib.msda_version.argtypes = []
+        _LIB = lib
+    return _LIB
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dims(value, spatial_shapes, sampling_locations, attention_weights):
+    if value.dim() != 4:
+        raise ValueError("value must be [B, Nv, M, D]")
+    if sampling_locations.dim() != 6 or sampling_locations.shape[-1] != 2:
+        raise ValueError("sampling_locations must be [B, Nq, M, L, K, 2]")
+    B, Nv, M, D = value.shape
+    Bq, Nq, Mq, L, K, _ = sampling_locations.shape
+    if (Bq, Mq) != (B, M):
+        raise ValueError("sampling_locations batch/head sizes differ from value's")
+    if tuple(attention_weights.shape) != (B, Nq, M, L, K):
+        raise ValueError("attention_weights must be [B, Nq, M, L, K]")
+    if tuple(spatial_shapes.shape) != (L, 2):
+        raise ValueError("spatial_shapes must be [L, 2]")
+    return MsdaDims(B, Nv, M, D, L, Nq, K)
+
+
+def _check(t, name, dtypes, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _value_dtype(value):
+    if value.dtype == torch.float32:
+        return MSDA_DTYPE_F32
+    if value.dtype == torch.bfloat16:
+        return MSDA_DTYPE_BF16
+    raise ValueError(f"value dtype {value.dtype} is not supported (float32 or bfloat16)")
+
+
+def _common(value, spatial_shapes, level_start_index, sampling_locations, attention_weights):
+    dev = value.device
+    if dev.type != "cuda":
+        raise ValueError("value must be a GPU tensor")
+    _check(value, "value", (torch.float32, torch.bfloat16), dev)
+    _check(spatial_shapes, "spatial_shapes", (torch.int64,), dev)
+    _check(level_start_index, "level_start_index", (torch.int64,), dev)
+    _check(sampling_locations, "sampling_locations", (torch.float32,), dev)
+    _check(attention_weights, "attention_weights", (torch.float32,), dev)
+    dims = _dims(value, spatial_shapes, sampling_locations, attention_weights)
+    if tuple(level_start_index.shape) != (dims.L,):
+        raise ValueError("level_start_index must be [L]")
+    return dev, dims
+
+
+def msda_forward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
+                 output=None, stream=None):
+    """Core forward (include/msda.h msda_forward). Returns output [B, Nq, M*D]
+    (fp32); ``output`` may be passed to write into an existing tensor."""
+    dev, dims = _common(value, spatial_shapes, level_start_index, sampling_locations,
+                        attention_weights)
+    if output is None:
+        output = torch.empty((dims.B, dims.Nq, dims.M * dims.D), dtype=torch.float32, device=dev)
+    else:
+        _check(output, "output", (torch.float32,), dev)
+        if output.numel() != dims.B * dims.Nq * dims.M * dims.D:
+            raise ValueError("output has the wrong number of elements")
+    st = library().msda_forward(ctypes.byref(dims), _value_dtype(value), _ptr(value),
+                                _ptr(spatial_shapes), _ptr(level_start_index),
+                                _ptr(sampling_locations), _ptr(attention_weights), _ptr(output),
+                                _stream(dev, stream))
+    if st != 0:
+        raise MsdaError(st, "msda_forward")
+    return output
+
+
+def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
+                  grad_output, grad_value=None, grad_sampling_locations=None,
+                  grad_attention_weights=None, needs=(True, True, True), stream=None):
+    """Core backward (include/msda.h msda_backward). Returns (grad_value,
+    grad_sampling_locations, grad_attention_weights), fp32; an entry of
+    ``needs`` set to False skips (and returns None for) that gradient."""
+    dev, dims = _common(value, spatial_shapes, level_start_index, sampling_locations,
+                        attention_weights)
+    _check(grad_output, "grad_output", (torch.float32,), dev)
+    if grad_output.numel() != dims.B * dims.Nq * dims.M * dims.D:
+        raise ValueError("grad_output has the wrong number of elements")
+    outs = []
+    for need, given, shape, name in (
+            (needs[0], grad_value, (dims.B, dims.Nv, dims.M, dims.D), "grad_value"),
+            (needs[1], grad_sampling_locations, tuple(sampling_locations.shape),
+             "grad_sampling_locations"),
+            (needs[2], grad_attention_weights, tuple(attention_weights.shape),
+             "grad_attention_weights")):
+        if not need:
+            outs.append(None)
+        elif given is None:
+            outs.append(torch.empty(shape, dtype=torch.float32, device=dev))
+        else:
+            _check(given, name, (torch.float32,), dev)
+            if tuple(given.shape) != shape:
+                raise ValueError(f"{name} must have shape {shape}")
+            outs.append(given)
+    st = library().msda_backward(ctypes.byref(dims), _value_dtype(value), _ptr(value),
+                                 _ptr(spatial_shapes), _ptr(level_start_index),
+                                 _ptr(sampling_locations), _ptr(attention_weights),
+                                 _ptr(grad_output), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
+                                 _stream(dev, stream))
+    if st != 0:
+        raise MsdaError(st, "msda_backward")
+    return tuple(outs)
+
+
+def msda_check_tables(spatial_shapes, level_start_index, Nv):
+    """Host check of the level tables (include/msda.h msda_check_tables)."""
+    import numpy as np
+    s = np.ascontiguousarray(np.asarray(spatial_shapes, np.int64).reshape(-1, 2))
+    i = np.ascontiguousarray(np.asarray(level_start_index, np.int64).reshape(-1))
+    return library().msda_check_tables(s.ctypes.data, i.ctypes.data, s.shape[0], int(Nv))
+
+
+def msda_version():
+    return library().msda_version()
+
+
+class MSDeformAttnFunction(torch.autograd.Function):
+    """Autograd wrapper: forward and backward both run in the HIP library."""
+
+    @staticmethod
+    def forward(ctx, value, spatial_shapes, level_start_index, sampling_locations,
+                attention_weights):
+        ctx.save_for_backward(value, spatial_shapes, level_start_index, sampling_locations,
+                              attention_weights)
+        return msda_forward(value, spatial_shapes, level_start_index, sampling_locations,
+                            attention_weights)
+
+    @staticmethod
+    def backward(ctx, grad_output):
+        value, shapes, lsi, loc, attn = ctx.saved_tensors
+        needs = (ctx.needs_input_grad[0], ctx.needs_input_grad[3], ctx.needs_input_grad[4])
+        gv, gl, ga = msda_backward(value, shapes, lsi, loc, attn, grad_output.contiguous(),
+                                   needs=needs)
+        if gv is not None and value.dtype != torch.float32:
+            gv = gv.to(value.dtype)
+        return gv, None, None, gl, ga
+
+
+def ms_deform_attn(value, spatial_shapes, level_start_index, sampling_locations,
+                   attention_weights):
+    """Differentiable core: output [B, Nq, M*D]."""
+    return MSDeformAttnFunction.apply(value, spatial_shapes, level_start_index,
+                                      sampling_locations, attention_weights)

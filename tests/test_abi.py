@@ -1,0 +1,118 @@
+"""The C-ABI library loads and exports what include/msda.h declares, and its
+host-side argument checks reject bad calls before anything reaches a GPU.
+Runs without a GPU: every call here returns before the first HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import scale_deformable_attention_amd as msda
+from scale_deformable_attention_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["msda_backward", "msda_check_tables", "msda_forward",
+                                    "msda_status_string", "msda_version"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = msda.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported by libmsda.so"
+
+
+def test_version_and_status_strings():
+    lib = msda.library()
+    assert lib.msda_version() == 100
+    for s in range(4):
+        assert len(lib.msda_status_string(s)) > 0
+    assert lib.msda_status_string(99) == b"unknown status"
+
+
+FAKE = ctypes.c_void_p(0x10000)   # aligned, never dereferenced: checks return first
+
+
+def fwd_status(dims, dtype=0, **ptrs):
+    p = dict(value=FAKE, shapes=FAKE, lsi=FAKE, loc=FAKE, attn=FAKE, out=FAKE)
+    p.update(ptrs)
+    return msda.library().msda_forward(
+        None if dims is None else ctypes.byref(dims), dtype, p["value"], p["shapes"], p["lsi"],
+        p["loc"], p["attn"], p["out"], None)
+
+
+def bwd_status(dims, dtype=0, **ptrs):
+    p = dict(value=FAKE, shapes=FAKE, lsi=FAKE, loc=FAKE, attn=FAKE, gout=FAKE, gv=FAKE,
+             gl=FAKE, ga=FAKE)
+    p.update(ptrs)
+    return msda.library().msda_backward(
+        None if dims is None else ctypes.byref(dims), dtype, p["value"], p["shapes"], p["lsi"],
+        p["loc"], p["attn"], p["gout"], p["gv"], p["gl"], p["ga"], None)
+
+
+def dims(**kw):
+    d = dict(B=1, Nv=80, M=2, D=8, L=2, Nq=16, K=2)
+    d.update(kw)
+    return _binding.MsdaDims(*[d[k] for k in ("B", "Nv", "M", "D", "L", "Nq", "K")])
+
+
+INVALID, UNSUPPORTED = 1, 2
+
+
+@pytest.mark.parametrize("status_fn", [fwd_status, bwd_status])
+def test_invalid_sizes(status_fn):
+    assert status_fn(None) == INVALID
+    for bad in (dict(B=-1), dict(Nq=-3), dict(K=-1), dict(M=0), dict(Nv=0), dict(L=0),
+                dict(D=0)):
+        assert status_fn(dims(**bad)) == INVALID, bad
+    assert status_fn(dims(), dtype=7) == INVALID
+
+
+@pytest.mark.parametrize("status_fn", [fwd_status, bwd_status])
+def test_unsupported_sizes(status_fn):
+    for d in (4, 12, 24, 128):
+        assert status_fn(dims(D=d)) == UNSUPPORTED, d
+    assert status_fn(dims(L=17, Nv=17)) == UNSUPPORTED
+    # value tensor of 2 GiB or more
+    assert status_fn(dims(B=4, Nv=2 ** 22, M=8, D=64)) == UNSUPPORTED
+    # too many tuples for 32-bit indexing
+    assert status_fn(dims(B=2 ** 12, Nq=2 ** 16, M=16)) == UNSUPPORTED
+
+
+def test_null_and_misaligned_pointers():
+    for key in ("value", "shapes", "lsi", "loc", "attn", "out"):
+        assert fwd_status(dims(), **{key: None}) == INVALID, key
+    for key in ("value", "shapes", "lsi", "loc", "attn", "gout"):
+        assert bwd_status(dims(), **{key: None}) == INVALID, key
+    odd = ctypes.c_void_p(0x10004)        # 4-byte but not 8/16-byte aligned
+    for key in ("value", "out", "loc", "shapes", "lsi"):
+        assert fwd_status(dims(), **{key: odd}) == INVALID, key
+    for key in ("value", "gout", "gv", "loc", "gl"):
+        assert bwd_status(dims(), **{key: odd}) == INVALID, key
+    assert fwd_status(dims(), attn=ctypes.c_void_p(0x10002)) == INVALID
+
+
+def test_check_tables():
+    assert msda.msda_check_tables([[8, 8], [4, 4]], [0, 64], 80) == 0
+    assert msda.msda_check_tables([[8, 8], [4, 4]], [0, 63], 80) == INVALID
+    assert msda.msda_check_tables([[8, 8], [4, 4]], [0, 64], 81) == INVALID
+    assert msda.msda_check_tables([[8, 0], [4, 4]], [0, 0], 16) == INVALID
+    assert msda.msda_check_tables(np.zeros((17, 2), np.int64) + 1, np.arange(17), 17) == INVALID
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    v = torch.zeros(1, 80, 2, 8)
+    with pytest.raises(ValueError):
+        msda.msda_forward(v, torch.zeros(2, 2, dtype=torch.int64), torch.zeros(2, dtype=torch.int64),
+                          torch.zeros(1, 16, 2, 2, 2, 2), torch.zeros(1, 16, 2, 2, 2))

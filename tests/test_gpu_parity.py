@@ -1,0 +1,288 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on
+the same seeded inputs, element by element.
+
+Tolerance (per element, r = oracle, x = GPU, S = the oracle's sum of the
+absolute values of the terms making up r):
+    fp32 value:  |x - r| <= 1e-5 * |r| + 1e-5 * S
+    bf16 value:  |x - r| <= 2e-2 * |r| + 1e-5 * S   (oracle fed the same bf16 values)
+A single fp32 sum of n terms carries a relative error of at most about
+n * 2^-24 of S; the S term bounds that for every sum the kernels form, and the
+|r| term is the requested relative tolerance. Outputs whose sum is empty must
+be exactly 0 (S = 0).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from scale_deformable_attention_amd import workloads as wl
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+RTOL = {"f32": 1e-5, "bf16": 2e-2}
+STOL = 1e-5
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import scale_deformable_attention_amd as msda
+    msda.library()   # raises if the HIP library is missing: no fallback
+    return torch.device("cuda:0")
+
+
+def to_gpu(x, value_dtype):
+    dev = _dev()
+    if value_dtype == "bf16":
+        value = torch.from_numpy(x["value_bf16"].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        value = torch.from_numpy(x["value"]).to(dev)
+    t = {k: torch.from_numpy(np.ascontiguousarray(x[k])).to(dev)
+         for k in ("spatial_shapes", "level_start_index", "sampling_locations",
+                   "attention_weights", "grad_output")}
+    t["value"] = value
+    return t
+
+
+def gpu_forward(t):
+    import scale_deformable_attention_amd as msda
+    out = msda.msda_forward(t["value"], t["spatial_shapes"], t["level_start_index"],
+                            t["sampling_locations"], t["attention_weights"])
+    torch.cuda.synchronize()
+    return out
+
+
+def gpu_backward(t, needs=(True, True, True)):
+    import scale_deformable_attention_amd as msda
+    res = msda.msda_backward(t["value"], t["spatial_shapes"], t["level_start_index"],
+                             t["sampling_locations"], t["attention_weights"], t["grad_output"],
+                             needs=needs)
+    torch.cuda.synchronize()
+    return res
+
+
+def check(name, got, ref, ref_abs, rtol):
+    got = np.asarray(got, np.float64).reshape(ref.shape)
+    err = np.abs(got - ref)
+    bound = rtol * np.abs(ref) + STOL * ref_abs
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.flatnonzero(bad.reshape(-1))[:5]
+        raise AssertionError(
+            f"{name}: {bad.sum()} of {bad.size} elements outside tolerance; first at flat "
+            f"{i.tolist()}: gpu {got.reshape(-1)[i]} oracle {ref.reshape(-1)[i]} "
+            f"abs-sum {ref_abs.reshape(-1)[i]}")
+    denom = np.abs(ref) + ref_abs
+    rel = float(np.max(np.where(denom > 0, err / np.where(denom > 0, denom, 1), 0)))
+    print(f"  {name}: max |gpu-oracle| / (|r| + S) = {rel:.2e}", flush=True)
+
+
+def parity(w, backward=True, batch_slice=None, x=None):
+    print(f"[parity] {w.name}: B={w.B} M={w.M} D={w.D} L={w.L} K={w.K} Nq={w.num_queries} "
+          f"{w.value_dtype} shapes={w.shapes}", flush=True)
+    x = x if x is not None else wl.generate(w, batch_slice=batch_slice)
+    t = to_gpu(x, w.value_dtype)
+    rtol = RTOL[w.value_dtype]
+    out = gpu_forward(t).cpu().numpy()
+    ref, ref_abs = oracle.forward(x["value"], x["spatial_shapes"], x["level_start_index"],
+                                  x["sampling_locations"], x["attention_weights"], with_abs=True)
+    check("output", out, ref, ref_abs, rtol)
+    if backward:
+        gv, gl, ga = [g.cpu().numpy() for g in gpu_backward(t)]
+        B, Nq = x["sampling_locations"].shape[:2]
+        rgv, rgl, rga, agv, agl, aga = oracle.backward(
+            x["value"], x["spatial_shapes"], x["level_start_index"], x["sampling_locations"],
+            x["attention_weights"], x["grad_output"], with_abs=True)
+        check("grad_value", gv, rgv, agv, rtol)
+        check("grad_sampling_locations", gl, rgl, agl, rtol)
+        check("grad_attention_weights", ga, rga, aga, rtol)
+    return x, t
+
+
+# ---------------------------------------------------------------- small cases
+def test_tiny_workload():
+    parity(wl.WORKLOADS["tiny"])
+
+
+SMALL_PYRAMID = ((13, 21), (7, 11), (4, 6), (2, 3))
+
+
+@pytest.mark.parametrize("value_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [8, 16, 32, 64])
+def test_every_head_width(D, value_dtype):
+    # ragged: tuple count not a multiple of any block's tuples, L*K = 9 not a
+    # multiple of the lanes per tuple
+    w = wl.Workload(f"small_D{D}_{value_dtype}", B=3, M=5, D=D, K=3, shapes=SMALL_PYRAMID[:3],
+                    ref="uniform", sigma_px=2.0, Nq=37, value_dtype=value_dtype, seed=77 + D)
+    parity(w)
+
+
+def test_encoder_pyramid_small_grid():
+    w = wl.Workload("small_encoder", B=2, M=8, D=32, K=4, shapes=SMALL_PYRAMID, ref="grid",
+                    sigma_px=3.0, seed=78)
+    parity(w)
+
+
+def test_single_level_single_point():
+    w = wl.Workload("single_scale", B=2, M=1, D=16, K=1, shapes=((9, 14),), ref="uniform",
+                    sigma_px=5.0, Nq=101, seed=79)
+    parity(w)
+
+
+def test_many_points_and_levels():
+    shapes = tuple((3 + i, 2 + 2 * i) for i in range(16))
+    w = wl.Workload("sixteen_levels", B=1, M=2, D=8, K=5, shapes=shapes, ref="uniform",
+                    sigma_px=1.5, Nq=23, seed=80)
+    parity(w)
+
+
+def test_far_outside_and_non_finite_locations():
+    w = wl.Workload("far", B=2, M=4, D=32, K=4, shapes=SMALL_PYRAMID, ref="uniform",
+                    sigma_px=40.0, Nq=50, seed=81)
+    x = wl.generate(w)
+    loc = x["sampling_locations"]
+    flat = loc.reshape(-1, 2)
+    flat[0::7, 0] = np.nan
+    flat[3::11, 1] = np.inf
+    flat[5::13, 0] = -np.inf
+    flat[6::17] = 1e30
+    flat[8::19] = -1.0 / 64       # just outside on the left/top of the coarsest levels
+    parity(w, x=x)
+
+
+def test_pixel_centres_return_pixels_exactly():
+    # power-of-two level: the coordinate map lands exactly on the pixel
+    rng = np.random.default_rng(3)
+    B, M, D, K = 2, 4, 32, 1
+    shapes = np.array([[16, 32], [8, 8]], np.int64)
+    lsi = np.array([0, 512], np.int64)
+    Nv, Nq, L = 576, 64, 2
+    value = rng.standard_normal((B, Nv, M, D), dtype=np.float32)
+    loc = np.zeros((B, Nq, M, L, K, 2), np.float32)
+    attn = np.zeros((B, Nq, M, L, K), np.float32)
+    expect = np.zeros((B, Nq, M, D), np.float32)
+    for b in range(B):
+        for q in range(Nq):
+            for m in range(M):
+                l = (q + m) % 2
+                H, W = shapes[l]
+                i, j = rng.integers(H), rng.integers(W)
+                loc[b, q, m, l, 0] = ((j + 0.5) / W, (i + 0.5) / H)
+                attn[b, q, m, l, 0] = 1.0
+                expect[b, q, m] = value[b, lsi[l] + i * W + j, m]
+    x = dict(value=value, spatial_shapes=shapes, level_start_index=lsi, sampling_locations=loc,
+             attention_weights=attn, grad_output=np.zeros((B, Nq, M * D), np.float32))
+    out = gpu_forward(to_gpu(x, "f32")).cpu().numpy()
+    assert np.array_equal(out.reshape(expect.shape), expect)
+
+
+def test_empty_work():
+    dev = _dev()
+    import scale_deformable_attention_amd as msda
+    shapes = torch.tensor([[4, 4]], dtype=torch.int64, device=dev)
+    lsi = torch.tensor([0], dtype=torch.int64, device=dev)
+    value = torch.randn(2, 16, 2, 8, device=dev)
+    # K = 0: the sum is empty, output is zeros, gradients zeros
+    loc = torch.rand(2, 5, 2, 1, 0, 2, device=dev)
+    attn = torch.rand(2, 5, 2, 1, 0, device=dev)
+    out = msda.msda_forward(value, shapes, lsi, loc, attn)
+    gv, gl, ga = msda.msda_backward(value, shapes, lsi, loc, attn, torch.randn(2, 5, 16, device=dev))
+    torch.cuda.synchronize()
+    assert out.shape == (2, 5, 16) and torch.all(out == 0)
+    assert torch.all(gv == 0) and gl.numel() == 0 and ga.numel() == 0
+    # Nq = 0: nothing to compute, grad_value still zeroed
+    loc = torch.rand(2, 0, 2, 1, 3, 2, device=dev)
+    attn = torch.rand(2, 0, 2, 1, 3, device=dev)
+    out = msda.msda_forward(value, shapes, lsi, loc, attn)
+    gv = torch.full_like(value, 7.0)
+    msda.msda_backward(value, shapes, lsi, loc, attn, torch.zeros(2, 0, 16, device=dev),
+                       grad_value=gv)
+    torch.cuda.synchronize()
+    assert out.numel() == 0 and torch.all(gv == 0)
+
+
+def test_skipped_gradients_and_overwrite():
+    w = wl.WORKLOADS["tiny"]
+    x = wl.generate(w)
+    t = to_gpu(x, "f32")
+    gv_all, gl_all, ga_all = gpu_backward(t)
+    import scale_deformable_attention_amd as msda
+    for needs in ((True, False, False), (False, True, False), (False, False, True)):
+        got = gpu_backward(t, needs=needs)
+        for n, g, ref in zip(needs, got, (gv_all, gl_all, ga_all)):
+            if n:
+                assert torch.allclose(g, ref, rtol=1e-6, atol=1e-6)
+            else:
+                assert g is None
+    # outputs are overwritten, not accumulated into
+    gv = torch.full_like(gv_all, 123.0)
+    gl = torch.full_like(gl_all, -5.0)
+    ga = torch.full_like(ga_all, 9.0)
+    msda.msda_backward(t["value"], t["spatial_shapes"], t["level_start_index"],
+                       t["sampling_locations"], t["attention_weights"], t["grad_output"],
+                       grad_value=gv, grad_sampling_locations=gl, grad_attention_weights=ga)
+    torch.cuda.synchronize()
+    assert torch.allclose(gv, gv_all, rtol=1e-6, atol=1e-6)
+    assert torch.allclose(gl, gl_all) and torch.allclose(ga, ga_all)
+
+
+def test_forward_is_deterministic_and_stream_ordered():
+    w = wl.WORKLOADS["encoder"].scaled(B=1, shapes=SMALL_PYRAMID)
+    x = wl.generate(w)
+    t = to_gpu(x, "f32")
+    import scale_deformable_attention_amd as msda
+    a = gpu_forward(t)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = msda.msda_forward(t["value"], t["spatial_shapes"], t["level_start_index"],
+                              t["sampling_locations"], t["attention_weights"])
+    s.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_autograd_function_matches_oracle():
+    import scale_deformable_attention_amd as msda
+    w = wl.WORKLOADS["tiny"]
+    x = wl.generate(w)
+    t = to_gpu(x, "f32")
+    v = t["value"].clone().requires_grad_(True)
+    loc = t["sampling_locations"].clone().requires_grad_(True)
+    attn = t["attention_weights"].clone().requires_grad_(True)
+    out = msda.ms_deform_attn(v, t["spatial_shapes"], t["level_start_index"], loc, attn)
+    (out * t["grad_output"]).sum().backward()
+    rgv, rgl, rga, agv, agl, aga = oracle.backward(
+        x["value"], x["spatial_shapes"], x["level_start_index"], x["sampling_locations"],
+        x["attention_weights"], x["grad_output"], with_abs=True)
+    check("autograd grad_value", v.grad.cpu().numpy(), rgv, agv, 1e-5)
+    check("autograd grad_loc", loc.grad.cpu().numpy(), rgl, agl, 1e-5)
+    check("autograd grad_attn", attn.grad.cpu().numpy(), rga, aga, 1e-5)
+
+
+# ---------------------------------------------------------------- full-size workloads
+def test_full_encoder_forward():
+    parity(wl.WORKLOADS["encoder"], backward=False)
+
+
+def test_full_decoder_forward_backward():
+    parity(wl.WORKLOADS["decoder"])
+
+
+def test_full_hires_bf16_forward():
+    w = wl.WORKLOADS["hires_bf16"]
+    x, t = parity(w, backward=False)
+    # report (not gate) the storage error against the unrounded fp32 values
+    ref32 = oracle.forward(x["value_f32_orig"], x["spatial_shapes"], x["level_start_index"],
+                           x["sampling_locations"], x["attention_weights"])
+    out = gpu_forward(t).cpu().numpy().reshape(ref32.shape)
+    print(f"  bf16 storage error vs fp32 values: max abs {np.max(np.abs(out - ref32)):.3e}")
+
+
+def test_full_encoder_training_step():
+    x, t = parity(wl.WORKLOADS["encoder_train"])
+    # value-gradient conservation on the GPU result (any size): summed over
+    # pixels it equals sum_q A * (inside weight) * g, which the oracle confirms
+    gv, _, _ = gpu_backward(t, needs=(True, False, False))
+    rgv, _, _ = oracle.backward(x["value"], x["spatial_shapes"], x["level_start_index"],
+                                x["sampling_locations"], x["attention_weights"], x["grad_output"])
+    np.testing.assert_allclose(gv.sum(1).cpu().numpy(), rgv.sum(1), rtol=1e-4, atol=1e-3)
