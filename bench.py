@@ -1,14 +1,15 @@
 """Benchmark of the deformable attention core on one MI355X.
 
 One step = one pass of the whole hot path over one batch: msda_forward, then
-msda_backward (grad_value zero fill + the gather/scatter backward kernel),
+msda_backward (binning + tile-owner grad_value kernels and the location/weight
+gradient kernel),
 on the 800x1333 encoder training workload (B=4, M=8, D=32, L=4 levels
 (100,167),(50,84),(25,42),(13,21), K=4, Nq=Nv=22223, offsets N(0, 8 px),
 fp32). Inputs are synthetic (seeded), resident in HBM before timing starts.
 
 Prints ONE JSON line: points/s over the K timed steps (points =
-B*Nq*M*L*K per step), the roofline of the dominant kernel (the backward
-gather/scatter kernel) measured live with HIP events on the launch stream, and
+B*Nq*M*L*K per step), the roofline of the dominant kernel measured live with HIP
+events on the launch stream, and
 the CPU oracle's rate on the host (a bounded sample of the same workload).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -38,10 +39,15 @@ def algorithmic_bytes(w, value_bytes_per_elem=4):
     T = w.B * w.num_queries * w.M
     V = w.B * w.Nv * w.M * w.D
     fwd = V * value_bytes_per_elem + P * 12 + T * w.D * 4
-    bwd_kernel = V * value_bytes_per_elem + P * 12 + T * w.D * 4 + V * 4 + P * 12
-    zero_fill = V * 4
-    return {"forward": fwd, "backward": bwd_kernel, "zero_fill": zero_fill,
-            "step": fwd + bwd_kernel}
+    # location/weight gradients: value, locations, weights, upstream gradient
+    # in; their gradients (12 B per point) out
+    bwd_point = V * value_bytes_per_elem + P * 12 + T * w.D * 4 + P * 12
+    # grad_value: locations, weights, upstream gradient in; grad_value out
+    bwd_value = P * 12 + T * w.D * 4 + V * 4
+    # the whole backward reads each input once and writes each gradient once
+    bwd = V * value_bytes_per_elem + P * 12 + T * w.D * 4 + V * 4 + P * 12
+    return {"forward": fwd, "bwd_point": bwd_point, "bwd_value": bwd_value, "backward": bwd,
+            "step": fwd + bwd}
 
 
 def cpu_baseline(w, x, budget_s):
@@ -105,71 +111,75 @@ def main():
     gv = torch.empty(w.B, w.Nv, w.M, w.D, device=dev)
     gl = torch.empty_like(loc)
     ga = torch.empty_like(attn)
+    ws = torch.empty(max(msda.msda_backward_workspace_size(value, loc), 1), dtype=torch.uint8,
+                     device=dev)
     backward = w.backward
 
-    def step():
+    def fwd():
         msda.msda_forward(value, shapes, lsi, loc, attn, output=out)
+
+    def bwd(needs=(True, True, True)):
+        msda.msda_backward(value, shapes, lsi, loc, attn, gout, grad_value=gv,
+                           grad_sampling_locations=gl, grad_attention_weights=ga, needs=needs,
+                           workspace=ws)
+
+    def step():
+        fwd()
         if backward:
-            msda.msda_backward(value, shapes, lsi, loc, attn, gout, grad_value=gv,
-                               grad_sampling_locations=gl, grad_attention_weights=ga)
+            bwd()
+
+    stream = torch.cuda.current_stream(dev)   # the library launches on this stream
+
+    def timed(fn, n):
+        """Average ms of fn over n calls, HIP events on the launch stream."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream(dev)   # the library launches on this stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # the timed region: exactly K steps
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
-    for e in ev:
-        e[0].record(stream)
-        msda.msda_forward(value, shapes, lsi, loc, attn, output=out)
-        e[1].record(stream)
-        if backward:
-            msda.msda_backward(value, shapes, lsi, loc, attn, gout, grad_value=gv,
-                               grad_sampling_locations=gl, grad_attention_weights=ga)
-        e[2].record(stream)
+    for _ in range(args.steps):
+        step()
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(stop)
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    bwd_entry_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) if backward else 0.0
 
-    # the zero fill alone, live on the same stream: msda_backward with no
-    # queries launches only the fill of grad_value (same size as in the step)
-    zero_ms = 0.0
+    # each kernel on its own (same inputs, same stream): the forward kernel;
+    # the backward with only the location/weight gradients (the point kernel);
+    # the backward with only grad_value (bin + tile kernels)
+    kernels = {"msda_fwd_kernel": timed(fwd, args.steps)}
     if backward:
-        loc0 = torch.empty(w.B, 0, w.M, w.L, w.K, 2, device=dev)
-        attn0 = torch.empty(w.B, 0, w.M, w.L, w.K, device=dev)
-        g0 = torch.empty(w.B, 0, w.M * w.D, device=dev)
-        zf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        for _ in range(args.warmup):
-            msda.msda_backward(value, shapes, lsi, loc0, attn0, g0, grad_value=gv)
-        torch.cuda.synchronize()
-        for e in zf:
-            e[0].record(stream)
-            msda.msda_backward(value, shapes, lsi, loc0, attn0, g0, grad_value=gv)
-            e[1].record(stream)
-        torch.cuda.synchronize()
-        zero_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in zf]))
-        # leave the real gradients in place for anyone inspecting them
-        step()
+        kernels["msda_bwd_point_kernel"] = timed(lambda: bwd((False, True, True)), args.steps)
+        kernels["msda_bin_kernel+msda_tile_kernel"] = timed(lambda: bwd((True, False, False)),
+                                                            args.steps)
+        step()   # leave a full set of gradients in place
         torch.cuda.synchronize()
 
     ms_per_step = total_ms / args.steps
     pts_per_s = w.points / (ms_per_step * 1e-3)
     ab = algorithmic_bytes(w, 2 if w.value_dtype == "bf16" else 4)
-    if backward:
-        dom_name, dom_ms = "msda_bwd_kernel", max(bwd_entry_ms - zero_ms, 1e-9)
-        dom_bytes = ab["backward"]
-    else:
-        dom_name, dom_ms, dom_bytes = "msda_fwd_kernel", fwd_ms, ab["forward"]
+    kernel_bytes = {"msda_fwd_kernel": ab["forward"],
+                    "msda_bwd_point_kernel": ab["bwd_point"],
+                    "msda_bin_kernel+msda_tile_kernel": ab["bwd_value"]}
+    dom_name = max(kernels, key=kernels.get)
+    dom_ms, dom_bytes = kernels[dom_name], kernel_bytes[dom_name]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    step_gbs = (ab["step"] if backward else ab["forward"]) / (ms_per_step * 1e-3) / 1e9
+    step_bytes = ab["step"] if backward else ab["forward"]
+    step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -185,15 +195,15 @@ def main():
         "dtype": "f32" if w.value_dtype == "f32" else "bf16 value, f32 math",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.note}; B={w.B} M={w.M} D={w.D} L={w.L} K={w.K} "
-                               f"Nq=Nv={w.Nv} shapes={list(w.shapes)} offsets N(0,{w.sigma_px} px)",
+                               f"Nq={w.num_queries} Nv={w.Nv} shapes={list(w.shapes)} "
+                               f"offsets N(0,{w.sigma_px} px)",
                    "points_per_step": w.points, "global_batch": w.B, "parallelism": "none"},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None, "algorithmic_bytes": dom_bytes, "avg_ms": dom_ms},
-        "step_roofline": {"algorithmic_bytes": ab["step"] if backward else ab["forward"],
-                          "achieved": step_gbs, "frac": step_gbs / HBM_PEAK_GBS},
-        "kernels_ms": {"forward": fwd_ms, "backward_entry": bwd_entry_ms,
-                       "zero_fill": zero_ms, "backward_kernel": bwd_entry_ms - zero_ms},
+        "step_roofline": {"algorithmic_bytes": step_bytes, "achieved": step_gbs,
+                          "frac": step_gbs / HBM_PEAK_GBS},
+        "kernels_ms": kernels,
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:

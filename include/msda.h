@@ -38,9 +38,10 @@
  *   grad_attention_weights  [B, Nq, M, L, K]    fp32
  *
  * Ownership: every tensor pointer is a DEVICE pointer owned by the caller; a
- * pointer to a tensor with no elements may be NULL.
- * The library allocates nothing, keeps no pointer after a call returns, holds
- * no state and may be called from several host threads. All work is enqueued
+ * pointer to a tensor with no elements may be NULL. Scratch memory, where a
+ * call needs any, is a caller-provided workspace argument. The library
+ * allocates nothing, keeps no pointer after a call returns, holds no state
+ * and may be called from several host threads. All work is enqueued
  * on `stream` (0 = the null stream) with no host synchronization; results are
  * ready when the stream reaches them. Outputs are overwritten, never
  * accumulated into.
@@ -56,6 +57,7 @@
 #ifndef MSDA_H_
 #define MSDA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
@@ -65,7 +67,7 @@ extern "C" {
 #endif
 
 #define MSDA_VERSION_MAJOR 0
-#define MSDA_VERSION_MINOR 1
+#define MSDA_VERSION_MINOR 2
 #define MSDA_VERSION_PATCH 0
 
 /* Largest number of feature levels the kernels accept. */
@@ -116,24 +118,41 @@ msda_status_t msda_forward(const msda_dims_t *dims, msda_dtype_t value_dtype,
  *   grad_attention_weights[b,q,m,l,k]  = sum_d g[d] * s[d]
  *   grad_sampling_locations[...,0]     = A * W_l * sum_d g[d] * ds[d]/dx
  *   grad_sampling_locations[...,1]     = A * H_l * sum_d g[d] * ds[d]/dy
- *   grad_value[b,row_c,m,d]           += A * w_c * g[d]   (corners inside)
+ *   grad_value[b,row_c,m,d]            = sum over the samples whose corner c is
+ *                                        that pixel of A * w_c * g[d]
  * where g = grad_output[b,q,m*D:(m+1)*D] and s is the bilinear sample. At an
  * exact integer pixel coordinate the derivative is the one of the cell that
  * floor() selects (the right-sided derivative).
  *
- * grad_value is zero-filled by the library on `stream` and then accumulated
- * with fp32 atomics, so its low bits may differ from run to run (summation
- * order). Any of the three gradient pointers may be NULL to skip that
- * gradient. Alignment: value, grad_output and grad_value 16-byte;
- * sampling_locations and grad_sampling_locations 8-byte; others 4-byte.
- * Size limit: grad_value (fp32, same shape as value) smaller than 2 GiB.
+ * grad_value is computed without atomics: every element is written exactly
+ * once (zero where no sample lands); the fp32 summation order of one element
+ * may change from run to run, so its low bits may too. Any of the three
+ * gradient pointers may be NULL to skip that gradient.
+ *
+ * workspace: device scratch owned by the caller, needed only when grad_value
+ * is not NULL: at least msda_backward_workspace_size() bytes, 256-byte
+ * aligned, contents irrelevant on entry and clobbered on exit. It must not be
+ * used by other work until the stream has passed this call. Too small a
+ * workspace returns MSDA_ERROR_INVALID_VALUE.
+ *
+ * Alignment: value, grad_output and grad_value 16-byte; sampling_locations
+ * and grad_sampling_locations 8-byte; others 4-byte.
+ * Size limit: grad_value (fp32, same shape as value) and grad_output smaller
+ * than 2 GiB each.
  */
 msda_status_t msda_backward(const msda_dims_t *dims, msda_dtype_t value_dtype,
                             const void *value, const int64_t *spatial_shapes,
                             const int64_t *level_start_index, const float *sampling_locations,
                             const float *attention_weights, const float *grad_output,
                             float *grad_value, float *grad_sampling_locations,
-                            float *grad_attention_weights, hipStream_t stream);
+                            float *grad_attention_weights, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace msda_backward needs for these sizes (a function of the
+ * sizes alone, not of the level shapes or data). Returns the same status the
+ * backward's size checks would. No HIP call. */
+msda_status_t msda_backward_workspace_size(const msda_dims_t *dims, msda_dtype_t value_dtype,
+                                           size_t *bytes);
 
 /* Host-side check of a HOST copy of the level tables against Nv: every
  * H_l, W_l >= 1, level_start_index the prefix sums, sum H_l*W_l == Nv.

@@ -5,9 +5,10 @@ package is its Python binding. Importing the package does not load the
 library; the first call does, and raises if it has not been built.
 """
 from ._binding import (MSDA_DTYPE_BF16, MSDA_DTYPE_F32, MsdaError, MSDeformAttnFunction,
-                       library, ms_deform_attn, msda_backward, msda_check_tables, msda_forward,
+                       library, ms_deform_attn, msda_backward, msda_backward_workspace_size,
+                       msda_check_tables, msda_forward,
                        msda_version)
 
-__all__ = ["msda_forward", "msda_backward", "msda_check_tables", "msda_version", "library",
+__all__ = ["msda_forward", "msda_backward", "msda_backward_workspace_size", "msda_check_tables", "msda_version", "library",
            "ms_deform_attn", "MSDeformAttnFunction", "MsdaError", "MSDA_DTYPE_F32",
            "MSDA_DTYPE_BF16"]

@@ -47,7 +47,10 @@ def library():
                                      fp, fp, vp]
         lib.msda_backward.restype = ctypes.c_int
         lib.msda_backward.argtypes = [ctypes.POINTER(MsdaDims), ctypes.c_int, vp, i64p, i64p, fp,
-                                      fp, fp, fp, fp, fp, vp]
+                                      fp, fp, fp, fp, fp, vp, ctypes.c_size_t, vp]
+        lib.msda_backward_workspace_size.restype = ctypes.c_int
+        lib.msda_backward_workspace_size.argtypes = [ctypes.POINTER(MsdaDims), ctypes.c_int,
+                                                     ctypes.POINTER(ctypes.c_size_t)]
         lib.msda_check_tables.restype = ctypes.c_int
         lib.msda_check_tables.argtypes = [i64p, i64p, ctypes.c_int64, ctypes.c_int64]
         lib.msda_status_string.restype = ctypes.c_char_p
@@ -137,12 +140,28 @@ def msda_forward(value, spatial_shapes, level_start_index, sampling_locations, a
     return output
 
 
+def msda_backward_workspace_size(value, sampling_locations, D=None):
+    """Workspace bytes msda_backward needs for these tensors' sizes."""
+    B, Nv, M, Dv = value.shape
+    _, Nq, _, L, K, _ = sampling_locations.shape
+    dims = MsdaDims(B, Nv, M, Dv, L, Nq, K)
+    n = ctypes.c_size_t(0)
+    st = library().msda_backward_workspace_size(ctypes.byref(dims), _value_dtype(value),
+                                                ctypes.byref(n))
+    if st != 0:
+        raise MsdaError(st, "msda_backward_workspace_size")
+    return n.value
+
+
 def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
                   grad_output, grad_value=None, grad_sampling_locations=None,
-                  grad_attention_weights=None, needs=(True, True, True), stream=None):
+                  grad_attention_weights=None, needs=(True, True, True), workspace=None,
+                  stream=None):
     """Core backward (include/msda.h msda_backward). Returns (grad_value,
     grad_sampling_locations, grad_attention_weights), fp32; an entry of
-    ``needs`` set to False skips (and returns None for) that gradient."""
+    ``needs`` set to False skips (and returns None for) that gradient.
+    ``workspace`` (a uint8 GPU tensor of at least msda_backward_workspace_size
+    bytes) is allocated here when not given and grad_value is needed."""
     dev, dims = _common(value, spatial_shapes, level_start_index, sampling_locations,
                         attention_weights)
     _check(grad_output, "grad_output", (torch.float32,), dev)
@@ -164,10 +183,25 @@ def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, 
             if tuple(given.shape) != shape:
                 raise ValueError(f"{name} must have shape {shape}")
             outs.append(given)
+    ws_bytes = 0
+    if outs[0] is not None:
+        n = ctypes.c_size_t(0)
+        st = library().msda_backward_workspace_size(ctypes.byref(dims), _value_dtype(value),
+                                                    ctypes.byref(n))
+        if st != 0:
+            raise MsdaError(st, "msda_backward_workspace_size")
+        if workspace is None:
+            workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+        elif workspace.device != dev or workspace.numel() * workspace.element_size() < n.value:
+            raise ValueError(f"workspace must be a {n.value}-byte tensor on {dev}")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    else:
+        workspace = None
     st = library().msda_backward(ctypes.byref(dims), _value_dtype(value), _ptr(value),
                                  _ptr(spatial_shapes), _ptr(level_start_index),
                                  _ptr(sampling_locations), _ptr(attention_weights),
                                  _ptr(grad_output), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
+                                 _ptr(workspace), ctypes.c_size_t(ws_bytes),
                                  _stream(dev, stream))
     if st != 0:
         raise MsdaError(st, "msda_backward")

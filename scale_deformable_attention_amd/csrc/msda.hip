@@ -24,8 +24,9 @@
 //    hardware answers with zeros: no branch, no clamp, no out-of-range access;
 //  * the backward reduces the four per-corner dot products g.v_c across the
 //    group with DPP, and the record's owner lane turns them into the weight
-//    and location gradients; grad_value is scattered with fp32 buffer atomics
-//    (also dropped by the hardware for outside corners).
+//    and location gradients; grad_value is built without atomics by binning
+//    the points into pixel tiles and letting one block own each tile (see the
+//    backward section).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -54,6 +55,7 @@ struct bf16_t {
 // miscompiles __builtin_bit_cast applied directly to an element of an
 // ext_vector_type value (it reads element 0 whatever the index).
 __device__ inline float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ inline uint32_t as_uint(float f) { return __builtin_bit_cast(uint32_t, f); }
 
 template <typename T>
 struct Elem;
@@ -99,10 +101,16 @@ struct Params {
     float* grad_value;
     float* grad_loc;
     float* grad_attn;
-    int Nv, M, L, Nq, K, LK;
+    int B, Nv, M, L, Nq, K, LK;
     int T;                    // tuples B*Nq*M
     uint32_t value_bytes;     // record count of the value buffer
-    uint32_t grad_value_bytes;
+    // grad_value binning (backward only)
+    int nW;                   // bin blocks per (b, m)
+    int Qc;                   // queries per bin block
+    int t_stride;             // row stride of the per-block tile table
+    uint32_t slab_per_block;  // point-index capacity of one bin block's slab
+    uint2* table;             // [B*M*nW][t_stride] (count, offset)
+    float4* slab;             // [B*M*nW][slab_per_block] (tuple bits, x, y, A) entries
 };
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -191,8 +199,31 @@ __device__ inline uint32_t tuple_base_bytes(const Params& p, int t, int row_byte
     return (uint32_t)b * (uint32_t)p.Nv * (uint32_t)row_bytes + (uint32_t)m * (uint32_t)head_bytes;
 }
 
+// ------------------------------------------------------------------ work order
+// Workgroups are handed to the 8 XCDs round-robin (block i runs on XCD i % 8)
+// and each XCD has its own L2. The tuple kernels therefore walk tuples in
+// (b, m, q) order and give each XCD one contiguous share of that order: an
+// XCD then works through one (b, m) value plane at a time (2.8 MB at the
+// 800x1333 pyramid, D = 32 fp32), which its 4 MB L2 holds, and consecutive
+// queries of one head sample neighbouring rows.
+__device__ inline int xcd_block() {
+    const int blk = blockIdx.x, nblk = gridDim.x;
+    const int x = blk % 8, i = blk / 8, per = nblk / 8, rem = nblk % 8;
+    return x * per + (x < rem ? x : rem) + i;
+}
+
+// Position in the (b, m, q) work order -> index of the tuple in memory order
+// ((b * Nq + q) * M + m).
+__device__ inline int tuple_of(const Params& p, int logical) {
+    const int bm = logical / p.Nq;
+    const int q = logical - bm * p.Nq;
+    const int b = bm / p.M;
+    const int m = bm - b * p.M;
+    return (b * p.Nq + q) * p.M + m;
+}
+
 // ------------------------------------------------------------------ forward
-struct FwdRecord {
+struct alignas(16) FwdRecord {
     uint32_t off[4];
     float w[4];   // A * bilinear weight, 0 for corners outside
 };
@@ -208,19 +239,21 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int tuple0 = (blockIdx.x * kWavesPerBlock + wave) * TPW;
+    const int tuple0 = (xcd_block() * kWavesPerBlock + wave) * TPW;   // work-order position
     if (tuple0 >= p.T) return;  // wave-uniform; no block barrier follows
     const uint32_t row_bytes = (uint32_t)p.M * kRowBytesPerHead;
     const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(p.value, p.value_bytes);
 
     // phase-1 role: this lane builds records of tuple t1 = tuple0 + lane % TPW
-    const int t1 = tuple0 + lane % TPW;
+    const int t1w = tuple0 + lane % TPW;
+    const int t1 = t1w < p.T ? tuple_of(p, t1w) : 0;
     const int jrow = lane / TPW;
-    const bool t1_ok = t1 < p.T;
+    const bool t1_ok = t1w < p.T;
     const uint32_t base1 = t1_ok ? tuple_base_bytes(p, t1, row_bytes, kRowBytesPerHead) : 0;
     // phase-2 role: this lane accumulates channels [r*PL, r*PL+PL) of tuple t2
     const int g = lane / G, r = lane % G;
-    const int t2 = tuple0 + g;
+    const int t2w = tuple0 + g;
+    const int t2 = t2w < p.T ? tuple_of(p, t2w) : p.T;
 
     float acc[PL];
 #pragma unroll
@@ -278,38 +311,57 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
 }
 
 // ------------------------------------------------------------------ backward
-struct BwdRecord {
+//
+// The backward runs as up to three kernels, none of which uses a float atomic
+// (on this GPU those serialize: an fp32 atomic costs a whole cache-line
+// request at the memory side, and LDS fp32 atomics are slower still).
+//
+//  1. msda_bwd_point_kernel: the weight and location gradients. Same tuple
+//     mapping as the forward; per point the group gathers the four corner rows,
+//     forms the four dot products g . v_c, reduces them across the group with
+//     DPP, and the record's owner lane finishes the point.
+//  2. msda_bin_kernel: sorts the points into buckets by the grad_value tiles
+//     (TH x TW pixels of one (b, m, level)) their inside-the-level corners land
+//     in. A block owns a range of queries of one (b, m); it counts per tile with
+//     LDS integer atomics (fast), scans, writes its per-tile (count, offset)
+//     row to the workspace and the point indices to its own slab. No global
+//     atomics: every block writes only its own rows.
+//  3. msda_tile_kernel: one block owns one tile. It collects the tile's points
+//     from every slab of its (b, m), sorts them by cell (counting sort in LDS),
+//     and lane group c sweeps pixel column c top to bottom: the cells left of
+//     and at the column feed it, two rows at a time, and the column's pixel
+//     sums live in registers. Every grad_value element is then written exactly
+//     once with a plain store (zeros where nothing lands), so no fill pass.
+
+struct alignas(16) PointRecord {
     uint32_t off[4];
-    float aw[4];  // A * bilinear weight, 0 for corners outside
-    float dot[4]; // sum_d g[d] * v_c[d], filled by the gathering group
+    float dot[4];  // sum_d g[d] * v_c[d], filled by the gathering group
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(kBlock) void msda_bwd_kernel(Params p) {
+__global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
     using S = Shape<T, D>;
     constexpr int G = S::G, TPW = S::TPW, PL = S::kPerLane;
     constexpr int kRowBytesPerHead = D * Elem<T>::kBytes;
-    // grad_value is fp32: its byte offsets are the value offsets times this
-    constexpr int kGradScale = 4 / Elem<T>::kBytes;
     __shared__ int4 levels[MSDA_MAX_LEVELS];
-    __shared__ BwdRecord records[kWavesPerBlock][kWave];
+    __shared__ PointRecord records[kWavesPerBlock][kWave];
     load_levels(p, levels);
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int tuple0 = (blockIdx.x * kWavesPerBlock + wave) * TPW;
+    const int tuple0 = (xcd_block() * kWavesPerBlock + wave) * TPW;   // work-order position
     if (tuple0 >= p.T) return;
     const uint32_t row_bytes = (uint32_t)p.M * kRowBytesPerHead;
     const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(p.value, p.value_bytes);
-    const __amdgpu_buffer_rsrc_t grsrc =
-        make_rsrc(p.grad_value, p.grad_value ? p.grad_value_bytes : 0u);
 
-    const int t1 = tuple0 + lane % TPW;
+    const int t1w = tuple0 + lane % TPW;
+    const int t1 = t1w < p.T ? tuple_of(p, t1w) : 0;
     const int jrow = lane / TPW;
-    const bool t1_ok = t1 < p.T;
+    const bool t1_ok = t1w < p.T;
     const uint32_t base1 = t1_ok ? tuple_base_bytes(p, t1, row_bytes, kRowBytesPerHead) : 0;
     const int g = lane / G, r = lane % G;
-    const int t2 = tuple0 + g;
+    const int t2w = tuple0 + g;
+    const int t2 = t2w < p.T ? tuple_of(p, t2w) : p.T;
 
     // upstream gradient of the group's tuple, this lane's channels
     float go[PL];
@@ -329,13 +381,13 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(Params p) {
     }
 
     for (int jc = 0; jc < p.LK; jc += G) {
-        // phase 1: this lane's point -> record; keep what phase 3 needs
+        // phase 1: this lane's point -> corner offsets in LDS; keep the rest
         const int j = jc + jrow;
         const bool mine = t1_ok && j < p.LK;
         size_t pt = 0;
         float a = 0.0f, Hf = 0.0f, Wf = 0.0f;
         Geometry geo;
-        BwdRecord rec;
+        PointRecord rec;
         if (mine) {
             const int l = (unsigned)j / (unsigned)p.K;
             const int4 lv = levels[l];
@@ -345,36 +397,27 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(Params p) {
             Hf = (float)lv.x;
             Wf = (float)lv.y;
             geo = point_geometry(uv.x, uv.y, lv, base1, row_bytes);
-            const float ay0 = a * (1.0f - geo.fy), ay1 = a * geo.fy;
-            const float w[4] = {ay0 * (1.0f - geo.fx), ay0 * geo.fx, ay1 * (1.0f - geo.fx),
-                                ay1 * geo.fx};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                rec.off[c] = geo.off[c];
-                rec.aw[c] = geo.valid[c] ? w[c] : 0.0f;
-                rec.dot[c] = 0.0f;
-            }
         } else {
             geo.fx = geo.fy = 0.0f;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 geo.valid[c] = false;
                 geo.off[c] = kOutside;
-                rec.off[c] = kOutside;
-                rec.aw[c] = 0.0f;
-                rec.dot[c] = 0.0f;
             }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            rec.off[c] = geo.off[c];
+            rec.dot[c] = 0.0f;
         }
         records[wave][lane] = rec;
         wave_sync();
-        // phase 2: gather, per-corner dot products, grad_value scatter
+        // phase 2: gather and per-corner dot products, reduced over the group
 #pragma unroll
         for (int i = 0; i < G; ++i) {
             const int slot = i * TPW + g;
-            const uint32_t off[4] = {records[wave][slot].off[0], records[wave][slot].off[1],
-                                     records[wave][slot].off[2], records[wave][slot].off[3]};
-            const float aw[4] = {records[wave][slot].aw[0], records[wave][slot].aw[1],
-                                 records[wave][slot].aw[2], records[wave][slot].aw[3]};
+            const uint4 offs = *reinterpret_cast<const uint4*>(records[wave][slot].off);
+            const uint32_t off[4] = {offs.x, offs.y, offs.z, offs.w};
             float dot[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -386,28 +429,19 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(Params p) {
 #pragma unroll
                 for (int e = 0; e < PL; ++e) s = fmaf(go[e], v[e], s);
                 dot[c] = s;
-                if (p.grad_value) {
-                    const uint32_t goff = off[c] * kGradScale + (uint32_t)r * (PL * 4);
-#pragma unroll
-                    for (int e = 0; e < PL; ++e)
-                        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(aw[c] * go[e], grsrc,
-                                                                        goff + 4u * e, 0, 0);
-                }
             }
 #pragma unroll
             for (int c = 0; c < 4; ++c) dot[c] = group_sum<G>(dot[c]);
-            if (r == 0) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) records[wave][slot].dot[c] = dot[c];
-            }
+            if (r == 0)
+                *reinterpret_cast<float4*>(records[wave][slot].dot) =
+                    make_float4(dot[0], dot[1], dot[2], dot[3]);
         }
         wave_sync();
-        // phase 3: the record's owner turns the four dot products into the
-        // weight and location gradients of its point
+        // phase 3: the record's owner turns the dot products into the weight
+        // and location gradients of its point
         if (mine) {
-            float dot[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) dot[c] = records[wave][lane].dot[c];
+            const float4 d4 = *reinterpret_cast<const float4*>(records[wave][lane].dot);
+            const float dot[4] = {d4.x, d4.y, d4.z, d4.w};
             const float fx = geo.fx, fy = geo.fy;
             const float w[4] = {(1.0f - fx) * (1.0f - fy), fx * (1.0f - fy), (1.0f - fx) * fy,
                                 fx * fy};
@@ -430,15 +464,369 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_kernel(Params p) {
     }
 }
 
-__global__ __launch_bounds__(kBlock) void zero_fill_kernel(float4* dst, int64_t n4) {
-    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n4;
-         i += (int64_t)gridDim.x * kBlock)
-        dst[i] = z;
+// ---- grad_value tiles
+constexpr int kTileH = 4;           // pixel rows per tile
+constexpr int kBinRange = 4096;     // tile counters a bin block keeps in LDS at once
+constexpr int kChunk = 2048;        // entries a tile block sorts in LDS at once
+constexpr int kMaxSlabs = 32;       // bin blocks per (b, m) at most (a power of two)
+constexpr int kUnroll = 16;         // entries in flight per lane group in the sweep
+constexpr int kRecUnroll = 4;       // entries per thread in flight when building records
+
+// A tile is kTileH x TW pixels; lane group c of a tile block owns pixel column
+// c, with 4 fp32 channels per lane.
+template <int D>
+struct TileShape {
+    static constexpr int PL = 4;
+    static constexpr int G = D / PL;
+    static constexpr int TW = kBlock / G;
+    static constexpr int kCells = (kTileH + 1) * (TW + 1);
+    static_assert(TW >= 16 && (TW & (TW - 1)) == 0, "tile width");
+};
+
+struct LevelTiles {
+    int H, W, start, tile_base, ntx, pad0, pad1, pad2;
+};
+
+// Per-level tile grid of one (b, m): thread 0 fills the table, everyone waits.
+template <int TW>
+__device__ inline void setup_tiles(const Params& p, LevelTiles* lt, int* total) {
+    if (threadIdx.x == 0) {
+        int base = 0;
+        for (int l = 0; l < p.L; ++l) {
+            LevelTiles t;
+            t.H = (int)p.shapes[2 * l];
+            t.W = (int)p.shapes[2 * l + 1];
+            t.start = (int)p.lsi[l];
+            t.tile_base = base;
+            t.ntx = (t.W + TW - 1) / TW;
+            t.pad0 = t.pad1 = t.pad2 = 0;
+            lt[l] = t;
+            base += ((t.H + kTileH - 1) / kTileH) * t.ntx;
+        }
+        *total = base;
+    }
+    __syncthreads();
+}
+
+// Exclusive scan of a[0, n) into o[0, n) by the whole block; returns the total.
+// scratch holds kBlock words. a and o may alias.
+__device__ inline uint32_t block_exclusive_scan(const uint32_t* a, uint32_t* o, int n,
+                                                uint32_t* scratch) {
+    const int tid = threadIdx.x;
+    const int per = (n + kBlock - 1) / kBlock;
+    const int lo = min(tid * per, n), hi = min(lo + per, n);
+    uint32_t s = 0;
+    for (int i = lo; i < hi; ++i) s += a[i];
+    scratch[tid] = s;
+    __syncthreads();
+    for (int d = 1; d < kBlock; d <<= 1) {
+        const uint32_t v = tid >= d ? scratch[tid - d] : 0u;
+        __syncthreads();
+        scratch[tid] += v;
+        __syncthreads();
+    }
+    uint32_t run = scratch[tid] - s;
+    const uint32_t total = scratch[kBlock - 1];
+    for (int i = lo; i < hi; ++i) {
+        const uint32_t v = a[i];
+        o[i] = run;
+        run += v;
+    }
+    __syncthreads();
+    return total;
+}
+
+// Corner pixels of a point at level lt: the distinct tiles (local indices in
+// the (b, m)) that its inside-the-level corners fall in. Returns how many.
+template <int TW>
+__device__ inline int point_tiles(float u, float v, const LevelTiles& lt, int* tiles) {
+    const float Hf = (float)lt.H, Wf = (float)lt.W;
+    const float x = fmaf(u, Wf, -0.5f);
+    const float y = fmaf(v, Hf, -0.5f);
+    const float x0f = floorf(x), y0f = floorf(y);
+    const bool vx0 = (x0f >= 0.0f) && (x0f < Wf);
+    const bool vx1 = (x0f >= -1.0f) && (x0f < Wf - 1.0f);
+    const bool vy0 = (y0f >= 0.0f) && (y0f < Hf);
+    const bool vy1 = (y0f >= -1.0f) && (y0f < Hf - 1.0f);
+    const int x0 = (int)fminf(fmaxf(x0f, -1.0f), Wf);
+    const int y0 = (int)fminf(fmaxf(y0f, -1.0f), Hf);
+    const bool valid[4] = {vx0 && vy0, vx1 && vy0, vx0 && vy1, vx1 && vy1};
+    int n = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        if (!valid[c]) continue;
+        const int ty = (y0 + (c >> 1)) / kTileH, tx = (x0 + (c & 1)) / TW;  // corners are >= 0
+        const int t = lt.tile_base + ty * lt.ntx + tx;
+        bool dup = false;
+        for (int k = 0; k < n; ++k) dup |= tiles[k] == t;
+        if (!dup) tiles[n++] = t;
+    }
+    return n;
+}
+
+// Walks the points of one bin block (queries [q_begin, ...) of one (b, m)) with
+// a stride of kBlock, keeping the query offset, point slot j, level l and
+// global point index up to date without a division per point.
+struct PointWalk {
+    int i, qo, j, l, dq, dj, LK, K;
+    size_t pt;
+    size_t tuple0;  // (b*Nq + q_begin)*M + m
+    int M;
+    __device__ PointWalk(const Params& p, int tid, int q_begin, int b, int m)
+        : i(tid), LK(p.LK > 0 ? p.LK : 1), K(p.K > 0 ? p.K : 1), M(p.M) {
+        qo = i / LK;
+        j = i - qo * LK;
+        l = j / K;
+        dq = kBlock / LK;
+        dj = kBlock - dq * LK;
+        tuple0 = ((size_t)b * p.Nq + q_begin) * p.M + m;
+        pt = (tuple0 + (size_t)qo * M) * LK + j;
+    }
+    __device__ void next() {
+        i += kBlock;
+        qo += dq;
+        j += dj;
+        if (j >= LK) {
+            j -= LK;
+            ++qo;
+        }
+        while (l > 0 && l * K > j) --l;
+        while ((l + 1) * K <= j) ++l;
+        pt = (tuple0 + (size_t)qo * M) * LK + j;
+    }
+};
+
+template <int D>
+__global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
+    using TS = TileShape<D>;
+    __shared__ LevelTiles lt[MSDA_MAX_LEVELS];
+    __shared__ int s_tiles;
+    __shared__ uint32_t cnt[kBinRange];
+    __shared__ uint32_t off[kBinRange];
+    __shared__ uint32_t scratch[kBlock];
+    setup_tiles<TS::TW>(p, lt, &s_tiles);
+    // tables inconsistent with Nv could exceed the row: drop those tiles
+    // rather than write past the workspace
+    const int T = min(s_tiles, p.t_stride);
+    const int tid = threadIdx.x;
+    const int bm = blockIdx.x / p.nW, w = blockIdx.x - bm * p.nW;
+    const int b = bm / p.M, m = bm - b * p.M;
+    const int q_begin = min(w * p.Qc, p.Nq), q_end = min(q_begin + p.Qc, p.Nq);
+    const int npts = (q_end - q_begin) * p.LK;
+    uint2* row = p.table + (size_t)blockIdx.x * p.t_stride;
+    float4* slab = p.slab + (size_t)blockIdx.x * p.slab_per_block;
+    uint32_t base = 0;
+    for (int r0 = 0; r0 < T; r0 += kBinRange) {
+        const int rn = min(kBinRange, T - r0);
+        for (int i = tid; i < rn; i += kBlock) cnt[i] = 0;
+        __syncthreads();
+        for (PointWalk it(p, tid, q_begin, b, m); it.i < npts; it.next()) {
+            const float2 uv = *reinterpret_cast<const float2*>(p.loc + 2 * it.pt);
+            int tiles[4];
+            const int n = point_tiles<TS::TW>(uv.x, uv.y, lt[it.l], tiles);
+            for (int k = 0; k < n; ++k)
+                if (tiles[k] >= r0 && tiles[k] < r0 + rn) atomicAdd(&cnt[tiles[k] - r0], 1u);
+        }
+        __syncthreads();
+        const uint32_t total = block_exclusive_scan(cnt, off, rn, scratch);
+        for (int i = tid; i < rn; i += kBlock) row[r0 + i] = make_uint2(cnt[i], base + off[i]);
+        __syncthreads();
+        for (int i = tid; i < rn; i += kBlock) cnt[i] = 0;
+        __syncthreads();
+        for (PointWalk it(p, tid, q_begin, b, m); it.i < npts; it.next()) {
+            const float2 uv = *reinterpret_cast<const float2*>(p.loc + 2 * it.pt);
+            int tiles[4];
+            const int n = point_tiles<TS::TW>(uv.x, uv.y, lt[it.l], tiles);
+            if (n == 0) continue;
+            // the entry carries all the tile kernel needs: the tuple (its
+            // upstream-gradient row), the fp32 pixel coordinates (cell and
+            // fractions follow from them exactly as here) and the weight
+            const LevelTiles& L_ = lt[it.l];
+            const float4 rec = make_float4(as_float((uint32_t)(it.pt / (size_t)p.LK)),
+                                           fmaf(uv.x, (float)L_.W, -0.5f),
+                                           fmaf(uv.y, (float)L_.H, -0.5f), p.attn[it.pt]);
+            for (int k = 0; k < n; ++k) {
+                if (tiles[k] < r0 || tiles[k] >= r0 + rn) continue;
+                const uint32_t slot = base + off[tiles[k] - r0] + atomicAdd(&cnt[tiles[k] - r0], 1u);
+                slab[slot] = rec;
+            }
+        }
+        base += total;
+        __syncthreads();
+    }
+}
+
+// One work item = one tile of one (b, m). Work items run coarse levels first
+// (the most points per pixel, the longest lists), and consecutive items step
+// through (b, m) so that a block keeps one (b, m) residue mod 8 (one XCD, one
+// L2) when the grid and B*M are multiples of 8.
+template <int D>
+__global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
+    using TS = TileShape<D>;
+    constexpr int TW = TS::TW, G = TS::G, kCells = TS::kCells;
+    __shared__ LevelTiles lt[MSDA_MAX_LEVELS];
+    __shared__ int s_tiles;
+    __shared__ uint32_t wcnt[kMaxSlabs], wstart[kMaxSlabs], woff[kMaxSlabs];
+    __shared__ float4 rec[kChunk];        // (grad_out float index bits, A*(1-fy), A*fy, fx)
+    __shared__ uint16_t cell_of[kChunk];
+    __shared__ uint16_t sorted[kChunk];
+    __shared__ uint32_t cstart[kCells + 1];
+    __shared__ uint32_t ccount[kCells + 1];
+    __shared__ uint32_t scratch[kBlock];
+    setup_tiles<TW>(p, lt, &s_tiles);
+    const int T = min(s_tiles, p.t_stride);
+    const int tid = threadIdx.x;
+    const int BM = p.B * p.M;
+    const int col = tid / G, r = tid % G;
+
+    // XCD-affine schedule (the grid is a multiple of 8): with 8 or more
+    // (b, m), XCD x takes the (b, m) = x (mod 8) one after the other, so its
+    // L2 holds one (b, m)'s upstream-gradient rows at a time; within one
+    // (b, m) the coarse levels (the most points per pixel) go first. With
+    // fewer (b, m) the items are dealt round-robin.
+    const int xcd = blockIdx.x % 8, jx = blockIdx.x / 8, nj = gridDim.x / 8;
+    const int nbm_x = BM >= 8 ? (BM - xcd + 7) / 8 : 0;
+    const int items = BM >= 8 ? nbm_x * T : (BM * T - xcd + 7) / 8;
+    for (int k = jx; k < items; k += nj) {
+        int bm, tl;
+        if (BM >= 8) {
+            bm = xcd + 8 * (k / T);
+            tl = T - 1 - k % T;
+        } else {
+            const int it = xcd + 8 * k;
+            bm = it % BM;
+            tl = T - 1 - it / BM;
+        }
+        int l = 0;
+        while (l + 1 < p.L && lt[l + 1].tile_base <= tl) ++l;
+        const LevelTiles L_ = lt[l];
+        const int ty = (tl - L_.tile_base) / L_.ntx, tx = (tl - L_.tile_base) - ty * L_.ntx;
+        const int y_base = ty * kTileH, x_base = tx * TW;
+        const int b = bm / p.M, m = bm - b * p.M;
+
+        // this tile's entries in every slab of (b, m)
+        for (int w = tid; w < p.nW; w += kBlock) {
+            const uint2 e = p.table[((size_t)bm * p.nW + w) * p.t_stride + tl];
+            wcnt[w] = e.x;
+            woff[w] = e.y;
+        }
+        __syncthreads();
+        const uint32_t E = block_exclusive_scan(wcnt, wstart, p.nW, scratch);
+
+        float4 acc[kTileH];
+#pragma unroll
+        for (int y = 0; y < kTileH; ++y) acc[y] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+        for (uint32_t c0 = 0; c0 < E; c0 += kChunk) {
+            const int n = (int)min((uint32_t)kChunk, E - c0);
+            for (int i = tid; i <= kCells; i += kBlock) ccount[i] = 0;
+            __syncthreads();
+            // records of this chunk, histogram by cell; kRecUnroll entries per
+            // thread in flight
+            for (int e0 = tid; e0 < n; e0 += kRecUnroll * kBlock) {
+                float4 ent[kRecUnroll];
+#pragma unroll
+                for (int u = 0; u < kRecUnroll; ++u) {
+                    const uint32_t ge = c0 + min(e0 + u * kBlock, n - 1);
+                    int lo = 0;   // last slab whose start <= ge (nW <= kMaxSlabs)
+#pragma unroll
+                    for (int step = kMaxSlabs / 2; step > 0; step >>= 1)
+                        if (lo + step < p.nW && wstart[lo + step] <= ge) lo += step;
+                    ent[u] = p.slab[((size_t)bm * p.nW + lo) * p.slab_per_block + woff[lo] +
+                                    (ge - wstart[lo])];
+                }
+#pragma unroll
+                for (int u = 0; u < kRecUnroll; ++u) {
+                    const int e = e0 + u * kBlock;
+                    if (e >= n) continue;
+                    const float x = ent[u].y, y = ent[u].z, a = ent[u].w;
+                    const float x0f = floorf(x), y0f = floorf(y);
+                    const float fx = x - x0f, fy = y - y0f;
+                    // an entry has a corner in this tile, so its cell is within
+                    // one pixel of it; clamp anyway to stay in bounds
+                    const int cy = min(max((int)y0f - y_base, -1), kTileH - 1);
+                    const int cx = min(max((int)x0f - x_base, -1), TW - 1);
+                    const int cell = (cy + 1) * (TW + 1) + (cx + 1);
+                    rec[e] = make_float4(as_float(as_uint(ent[u].x) * (uint32_t)D), a * (1.0f - fy),
+                                         a * fy, fx);
+                    cell_of[e] = (uint16_t)cell;
+                    atomicAdd(&ccount[cell], 1u);
+                }
+            }
+            __syncthreads();
+            block_exclusive_scan(ccount, cstart, kCells + 1, scratch);
+            for (int i = tid; i <= kCells; i += kBlock) ccount[i] = 0;
+            __syncthreads();
+            for (int e = tid; e < n; e += kBlock) {
+                const int c = cell_of[e];
+                sorted[cstart[c] + atomicAdd(&ccount[c], 1u)] = (uint16_t)e;
+            }
+            __syncthreads();
+            // column sweep: cells (y0, col-1) and (y0, col) feed pixel column
+            // col; their ids are consecutive, so their entries form one sorted
+            // range [s, e) that splits at the second cell's start. kUnroll
+            // entries are in flight at once (indices past the end are clamped
+            // to the last entry and weighted 0).
+#pragma unroll
+            for (int cr = 0; cr <= kTileH; ++cr) {   // cell row cy = cr - 1
+                const int lc = cr * (TW + 1) + col;
+                const uint32_t s0 = cstart[lc], split = cstart[lc + 1];
+                const uint32_t e = split + ccount[lc + 1];
+                for (uint32_t k = s0; k < e; k += kUnroll) {
+                    float4 gv[kUnroll];
+                    float wt[kUnroll], wb[kUnroll];
+#pragma unroll
+                    for (int u = 0; u < kUnroll; ++u) {
+                        const uint32_t i = min(k + u, e - 1);
+                        const float4 rv = rec[sorted[i]];
+                        gv[u] = *reinterpret_cast<const float4*>(p.grad_out + as_uint(rv.x) + r * 4);
+                        // the cell left of the column gives its right corners
+                        // (fx), the cell at the column its left corners (1 - fx)
+                        const float wx = i >= split ? 1.0f - rv.w : rv.w;
+                        const bool live = k + u < e;
+                        wt[u] = live ? rv.y * wx : 0.0f;
+                        wb[u] = live ? rv.z * wx : 0.0f;
+                    }
+#pragma unroll
+                    for (int u = 0; u < kUnroll; ++u) {
+                        // a cell in cell row cr has its top corners on pixel row
+                        // cr - 1 and its bottom corners on pixel row cr
+                        if (cr >= 1) {
+                            acc[cr - 1].x = fmaf(wt[u], gv[u].x, acc[cr - 1].x);
+                            acc[cr - 1].y = fmaf(wt[u], gv[u].y, acc[cr - 1].y);
+                            acc[cr - 1].z = fmaf(wt[u], gv[u].z, acc[cr - 1].z);
+                            acc[cr - 1].w = fmaf(wt[u], gv[u].w, acc[cr - 1].w);
+                        }
+                        if (cr < kTileH) {
+                            acc[cr].x = fmaf(wb[u], gv[u].x, acc[cr].x);
+                            acc[cr].y = fmaf(wb[u], gv[u].y, acc[cr].y);
+                            acc[cr].z = fmaf(wb[u], gv[u].z, acc[cr].z);
+                            acc[cr].w = fmaf(wb[u], gv[u].w, acc[cr].w);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        // every pixel of the tile that is inside the level, written once
+        const int x = x_base + col;
+        if (x < L_.W) {
+#pragma unroll
+            for (int yy = 0; yy < kTileH; ++yy) {
+                const int y = y_base + yy;
+                if (y < L_.H) {
+                    const size_t rowi = (size_t)b * p.Nv + L_.start + (size_t)y * L_.W + x;
+                    *reinterpret_cast<float4*>(p.grad_value + (rowi * p.M + m) * D + r * 4) = acc[yy];
+                }
+            }
+        }
+        __syncthreads();
+    }
 }
 
 // ------------------------------------------------------------------ host side
 constexpr int64_t k2GiB = int64_t(1) << 31;
+constexpr size_t kWorkspaceAlign = 256;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -446,8 +834,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 bool mul_le(int64_t a, int64_t b, int64_t limit) { return a == 0 || b <= limit / a; }
 
 // Host checks shared by both entry points. Every offset the kernels form is
-// 32-bit: the value (and fp32 grad_value) tensors must stay below 2 GiB and the
-// tuple count below 2^31 minus a block.
+// 32-bit: the value, grad_value and output tensors must stay below 2 GiB, the
+// point count below 2^31.
 msda_status_t check_dims(const msda_dims_t* d, msda_dtype_t dt, bool backward) {
     if (!d) return MSDA_ERROR_INVALID_VALUE;
     if (d->B < 0 || d->Nq < 0 || d->K < 0 || d->M < 1 || d->Nv < 1 || d->L < 1 || d->D < 1)
@@ -456,14 +844,54 @@ msda_status_t check_dims(const msda_dims_t* d, msda_dtype_t dt, bool backward) {
     if (d->L > MSDA_MAX_LEVELS) return MSDA_ERROR_NOT_SUPPORTED;
     if (d->D != 8 && d->D != 16 && d->D != 32 && d->D != 64) return MSDA_ERROR_NOT_SUPPORTED;
     const int64_t lim = k2GiB - 1;
-    const int64_t elem = (backward || dt == MSDA_DTYPE_F32) ? 4 : 2;  // widest buffer
+    const int64_t elem = (backward || dt == MSDA_DTYPE_F32) ? 4 : 2;  // widest value-shaped buffer
     if (!mul_le(d->Nv, d->M, lim) || !mul_le(d->Nv * d->M, d->D * elem, lim) ||
         !mul_le(d->B, d->Nv * d->M * d->D * elem, lim))
         return MSDA_ERROR_NOT_SUPPORTED;
-    if (!mul_le(d->Nq, d->M, lim) || !mul_le(d->B, d->Nq * d->M, lim - 1024))
+    // output / grad_output bytes
+    if (!mul_le(d->Nq, d->M, lim) || !mul_le(d->Nq * d->M, d->D * 4, lim) ||
+        !mul_le(d->B, d->Nq * d->M * d->D * 4, lim))
         return MSDA_ERROR_NOT_SUPPORTED;
-    if (!mul_le(d->L, d->K, lim / 2)) return MSDA_ERROR_NOT_SUPPORTED;
+    // points (x2 for the location pairs)
+    if (!mul_le(d->L, d->K, lim / 2) || !mul_le(d->B * d->Nq * d->M, d->L * d->K * 2, lim))
+        return MSDA_ERROR_NOT_SUPPORTED;
     return MSDA_SUCCESS;
+}
+
+// Workspace of the grad_value path (bin + tile kernels): per (b, m), nW bin
+// blocks each own Qc queries, a row of (count, offset) per tile and a slab of
+// 16-byte entries (at most 4 per point: one per corner tile). The
+// tile count of one (b, m) is bounded from Nv and L alone: a level of H x W
+// pixels has ceil(H/4) ceil(W/TW) tiles (TW >= 16), which is at most
+// H/4 + 3/4 when W <= TW and at most (H+3) W / (2 TW) <= H W / 8 otherwise,
+// so sum_l <= Nv/4 + L.
+struct BwdPlan {
+    int64_t nW = 0, Qc = 0, t_stride = 0, slab_per_block = 0;
+    size_t table_off = 0, slab_off = 0, bytes = 0;
+};
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+BwdPlan plan_backward(const msda_dims_t* d) {
+    BwdPlan pl;
+    const int64_t BM = d->B * d->M;
+    if (BM == 0) return pl;
+    // about 2048 bin blocks in total, at most kMaxSlabs per (b, m)
+    int64_t nW = (2048 + BM - 1) / BM;
+    nW = nW < 1 ? 1 : (nW > kMaxSlabs ? kMaxSlabs : nW);
+    if (d->Nq > 0 && nW > d->Nq) nW = d->Nq;
+    const int64_t Qc = d->Nq > 0 ? (d->Nq + nW - 1) / nW : 0;
+    pl.nW = Qc > 0 ? (d->Nq + Qc - 1) / Qc : 1;
+    pl.Qc = Qc;
+    pl.t_stride = (d->Nv + 3) / 4 + d->L;
+    static_assert(kTileH == 4, "the tile-count bound above assumes 4-row tiles");
+    pl.slab_per_block = round_up((size_t)(4 * Qc * d->L * d->K), 64);
+    const size_t table_bytes = (size_t)(BM * pl.nW * pl.t_stride) * sizeof(uint2);
+    const size_t slab_bytes = (size_t)(BM * pl.nW * pl.slab_per_block) * sizeof(float4);
+    pl.table_off = 0;
+    pl.slab_off = round_up(table_bytes, kWorkspaceAlign);
+    pl.bytes = pl.slab_off + round_up(slab_bytes, kWorkspaceAlign);
+    return pl;
 }
 
 Params make_params(const msda_dims_t* d, msda_dtype_t dt, const void* value, const int64_t* shapes,
@@ -474,6 +902,7 @@ Params make_params(const msda_dims_t* d, msda_dtype_t dt, const void* value, con
     p.lsi = lsi;
     p.loc = loc;
     p.attn = attn;
+    p.B = (int)d->B;
     p.Nv = (int)d->Nv;
     p.M = (int)d->M;
     p.L = (int)d->L;
@@ -483,7 +912,6 @@ Params make_params(const msda_dims_t* d, msda_dtype_t dt, const void* value, con
     p.T = (int)(d->B * d->Nq * d->M);
     const int64_t elems = d->B * d->Nv * d->M * d->D;
     p.value_bytes = (uint32_t)(elems * (dt == MSDA_DTYPE_BF16 ? 2 : 4));
-    p.grad_value_bytes = (uint32_t)(elems * 4);
     return p;
 }
 
@@ -499,11 +927,6 @@ Sizes sizes_of(const msda_dims_t* d) {
     return s;
 }
 
-template <typename T, int D>
-int tuples_per_block() {
-    return Shape<T, D>::TPW * kWavesPerBlock;
-}
-
 msda_status_t launch(const void* kernel, int64_t blocks, Params& p, hipStream_t stream) {
     if (blocks <= 0) return MSDA_SUCCESS;
     void* args[] = {&p};
@@ -511,30 +934,36 @@ msda_status_t launch(const void* kernel, int64_t blocks, Params& p, hipStream_t 
     return e == hipSuccess ? MSDA_SUCCESS : MSDA_ERROR_LAUNCH;
 }
 
+// Kernels of one (value type, D) instantiation.
+struct Kernels {
+    const void* fwd = nullptr;
+    const void* point = nullptr;
+    const void* bin = nullptr;
+    const void* tile = nullptr;
+    int tuples_per_block = 0;
+};
+
 template <typename T, int D>
-const void* fwd_kernel() {
-    return reinterpret_cast<const void*>(&msda_fwd_kernel<T, D>);
-}
-template <typename T, int D>
-const void* bwd_kernel() {
-    return reinterpret_cast<const void*>(&msda_bwd_kernel<T, D>);
+Kernels kernels_for() {
+    Kernels k;
+    k.fwd = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D>);
+    k.point = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D>);
+    k.bin = reinterpret_cast<const void*>(&msda_bin_kernel<D>);
+    k.tile = reinterpret_cast<const void*>(&msda_tile_kernel<D>);
+    k.tuples_per_block = Shape<T, D>::TPW * kWavesPerBlock;
+    return k;
 }
 
-// Picks the instantiation for (value type, D); returns its tuples per block.
-template <bool kBackward>
-const void* pick(msda_dtype_t dt, int64_t D, int* tpb) {
-#define MSDA_PICK(T, DD)                                                          \
-    if (D == DD) {                                                                \
-        *tpb = tuples_per_block<T, DD>();                                         \
-        return kBackward ? bwd_kernel<T, DD>() : fwd_kernel<T, DD>();             \
-    }
+Kernels pick(msda_dtype_t dt, int64_t D) {
+#define MSDA_PICK(T, DD) \
+    if (D == DD) return kernels_for<T, DD>();
     if (dt == MSDA_DTYPE_F32) {
         MSDA_PICK(float, 8) MSDA_PICK(float, 16) MSDA_PICK(float, 32) MSDA_PICK(float, 64)
     } else {
         MSDA_PICK(bf16_t, 8) MSDA_PICK(bf16_t, 16) MSDA_PICK(bf16_t, 32) MSDA_PICK(bf16_t, 64)
     }
 #undef MSDA_PICK
-    return nullptr;
+    return Kernels();
 }
 
 }  // namespace
@@ -560,10 +989,18 @@ msda_status_t msda_forward(const msda_dims_t* dims, msda_dtype_t value_dtype, co
                            sampling_locations, attention_weights);
     p.out = output;
     if (p.T == 0) return MSDA_SUCCESS;
-    int tpb = 0;
-    const void* k = pick<false>(value_dtype, dims->D, &tpb);
-    if (!k) return MSDA_ERROR_NOT_SUPPORTED;
-    return launch(k, ((int64_t)p.T + tpb - 1) / tpb, p, stream);
+    const Kernels k = pick(value_dtype, dims->D);
+    if (!k.fwd) return MSDA_ERROR_NOT_SUPPORTED;
+    return launch(k.fwd, ((int64_t)p.T + k.tuples_per_block - 1) / k.tuples_per_block, p, stream);
+}
+
+msda_status_t msda_backward_workspace_size(const msda_dims_t* dims, msda_dtype_t value_dtype,
+                                           size_t* bytes) {
+    if (!bytes) return MSDA_ERROR_INVALID_VALUE;
+    const msda_status_t st = check_dims(dims, value_dtype, true);
+    if (st != MSDA_SUCCESS) return st;
+    *bytes = plan_backward(dims).bytes;
+    return MSDA_SUCCESS;
 }
 
 msda_status_t msda_backward(const msda_dims_t* dims, msda_dtype_t value_dtype, const void* value,
@@ -571,7 +1008,7 @@ msda_status_t msda_backward(const msda_dims_t* dims, msda_dtype_t value_dtype, c
                             const float* sampling_locations, const float* attention_weights,
                             const float* grad_output, float* grad_value,
                             float* grad_sampling_locations, float* grad_attention_weights,
-                            hipStream_t stream) {
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
     const msda_status_t st = check_dims(dims, value_dtype, true);
     if (st != MSDA_SUCCESS) return st;
     const Sizes n = sizes_of(dims);
@@ -581,7 +1018,11 @@ msda_status_t msda_backward(const msda_dims_t* dims, msda_dtype_t value_dtype, c
     if (!aligned(value, 16) || !aligned(grad_output, 16) || !aligned(grad_value, 16) ||
         !aligned(sampling_locations, 8) || !aligned(grad_sampling_locations, 8) ||
         !aligned(attention_weights, 4) || !aligned(grad_attention_weights, 4) ||
-        !aligned(spatial_shapes, 8) || !aligned(level_start_index, 8))
+        !aligned(spatial_shapes, 8) || !aligned(level_start_index, 8) ||
+        !aligned(workspace, kWorkspaceAlign))
+        return MSDA_ERROR_INVALID_VALUE;
+    const BwdPlan pl = plan_backward(dims);
+    if (grad_value && n.value && (!workspace || workspace_bytes < pl.bytes))
         return MSDA_ERROR_INVALID_VALUE;
     Params p = make_params(dims, value_dtype, value, spatial_shapes, level_start_index,
                            sampling_locations, attention_weights);
@@ -589,23 +1030,27 @@ msda_status_t msda_backward(const msda_dims_t* dims, msda_dtype_t value_dtype, c
     p.grad_value = grad_value;
     p.grad_loc = grad_sampling_locations;
     p.grad_attn = grad_attention_weights;
-    int tpb = 0;
-    const void* k = pick<true>(value_dtype, dims->D, &tpb);
-    if (!k) return MSDA_ERROR_NOT_SUPPORTED;
+    const Kernels k = pick(value_dtype, dims->D);
+    if (!k.point) return MSDA_ERROR_NOT_SUPPORTED;
     if (grad_value && n.value) {
-        // fill kernel rather than a memset node: safe inside captured graphs
-        const int64_t n4 = n.value / 4;
-        const int64_t blocks = n4 / kBlock < 4096 ? (n4 + kBlock - 1) / kBlock : 4096;
-        float4* dst = reinterpret_cast<float4*>(grad_value);
-        int64_t count = n4;
-        void* args[] = {&dst, &count};
-        if (hipLaunchKernel(reinterpret_cast<const void*>(&zero_fill_kernel),
-                            dim3((unsigned)blocks), dim3(kBlock), args, 0, stream) != hipSuccess)
-            return MSDA_ERROR_LAUNCH;
+        p.nW = (int)pl.nW;
+        p.Qc = (int)pl.Qc;
+        p.t_stride = (int)pl.t_stride;
+        p.slab_per_block = (uint32_t)pl.slab_per_block;
+        p.table = reinterpret_cast<uint2*>(static_cast<char*>(workspace) + pl.table_off);
+        p.slab = reinterpret_cast<float4*>(static_cast<char*>(workspace) + pl.slab_off);
+        const int64_t BM = dims->B * dims->M;
+        msda_status_t s = launch(k.bin, BM * pl.nW, p, stream);
+        if (s != MSDA_SUCCESS) return s;
+        // persistent: blocks loop over the (b, m, tile) work items; the grid
+        // is a multiple of 8 for the XCD-affine schedule
+        const int64_t items = BM * pl.t_stride;
+        const int64_t grid = items < 2048 ? ((items + 7) / 8) * 8 : 2048;
+        s = launch(k.tile, grid, p, stream);
+        if (s != MSDA_SUCCESS) return s;
     }
-    if (p.T == 0 || (!grad_value && !grad_sampling_locations && !grad_attention_weights))
-        return MSDA_SUCCESS;
-    return launch(k, ((int64_t)p.T + tpb - 1) / tpb, p, stream);
+    if (p.T == 0 || (!grad_sampling_locations && !grad_attention_weights)) return MSDA_SUCCESS;
+    return launch(k.point, ((int64_t)p.T + k.tuples_per_block - 1) / k.tuples_per_block, p, stream);
 }
 
 msda_status_t msda_check_tables(const int64_t* host_spatial_shapes,
@@ -626,7 +1071,7 @@ msda_status_t msda_check_tables(const int64_t* host_spatial_shapes,
 const char* msda_status_string(msda_status_t status) {
     switch (status) {
         case MSDA_SUCCESS: return "success";
-        case MSDA_ERROR_INVALID_VALUE: return "invalid value (pointer, alignment or size)";
+        case MSDA_ERROR_INVALID_VALUE: return "invalid value (pointer, alignment, size or workspace)";
         case MSDA_ERROR_NOT_SUPPORTED: return "not supported (D, level count or tensor size)";
         case MSDA_ERROR_LAUNCH: return "kernel launch failed";
     }

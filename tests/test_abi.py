@@ -22,8 +22,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["msda_backward", "msda_check_tables", "msda_forward",
-                                    "msda_status_string", "msda_version"]
+    assert declared_functions() == ["msda_backward", "msda_backward_workspace_size",
+                                    "msda_check_tables", "msda_forward", "msda_status_string",
+                                    "msda_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -34,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = msda.library()
-    assert lib.msda_version() == 100
+    assert lib.msda_version() == 200
     for s in range(4):
         assert len(lib.msda_status_string(s)) > 0
     assert lib.msda_status_string(99) == b"unknown status"
@@ -51,13 +52,14 @@ def fwd_status(dims, dtype=0, **ptrs):
         p["loc"], p["attn"], p["out"], None)
 
 
-def bwd_status(dims, dtype=0, **ptrs):
+def bwd_status(dims, dtype=0, ws_bytes=1 << 40, **ptrs):
     p = dict(value=FAKE, shapes=FAKE, lsi=FAKE, loc=FAKE, attn=FAKE, gout=FAKE, gv=FAKE,
-             gl=FAKE, ga=FAKE)
+             gl=FAKE, ga=FAKE, ws=FAKE)
     p.update(ptrs)
     return msda.library().msda_backward(
         None if dims is None else ctypes.byref(dims), dtype, p["value"], p["shapes"], p["lsi"],
-        p["loc"], p["attn"], p["gout"], p["gv"], p["gl"], p["ga"], None)
+        p["loc"], p["attn"], p["gout"], p["gv"], p["gl"], p["ga"], p["ws"],
+        ctypes.c_size_t(ws_bytes), None)
 
 
 def dims(**kw):
@@ -100,6 +102,29 @@ def test_null_and_misaligned_pointers():
     for key in ("value", "gout", "gv", "loc", "gl"):
         assert bwd_status(dims(), **{key: odd}) == INVALID, key
     assert fwd_status(dims(), attn=ctypes.c_void_p(0x10002)) == INVALID
+
+
+def workspace_size(d, dtype=0):
+    n = ctypes.c_size_t(0)
+    st = msda.library().msda_backward_workspace_size(ctypes.byref(d), dtype, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_and_checks():
+    st, n = workspace_size(dims())
+    assert st == 0 and n > 0 and n % 256 == 0
+    # grows with the point count, needs no level shapes
+    st2, n2 = workspace_size(dims(Nq=1600))
+    assert st2 == 0 and n2 > n
+    assert workspace_size(dims(D=12))[0] == UNSUPPORTED
+    assert msda.library().msda_backward_workspace_size(ctypes.byref(dims()), 0, None) == INVALID
+    # too small, missing or misaligned workspace is rejected before any launch
+    assert bwd_status(dims(), ws_bytes=n - 1) == INVALID
+    assert bwd_status(dims(), ws=None) == INVALID
+    assert bwd_status(dims(), ws=ctypes.c_void_p(0x10010)) == INVALID
+    # no grad_value: no workspace needed (the call then launches, so only the
+    # argument check is exercised here with a bad dims to stop before it)
+    assert bwd_status(dims(D=12), gv=None, ws=None, ws_bytes=0) == UNSUPPORTED
 
 
 def test_check_tables():

@@ -191,6 +191,14 @@ def test_empty_work():
     torch.cuda.synchronize()
     assert out.shape == (2, 5, 16) and torch.all(out == 0)
     assert torch.all(gv == 0) and gl.numel() == 0 and ga.numel() == 0
+    # B = 0: everything empty
+    value0 = torch.randn(0, 16, 2, 8, device=dev)
+    loc0 = torch.rand(0, 5, 2, 1, 3, 2, device=dev)
+    attn0 = torch.rand(0, 5, 2, 1, 3, device=dev)
+    out0 = msda.msda_forward(value0, shapes, lsi, loc0, attn0)
+    g0 = msda.msda_backward(value0, shapes, lsi, loc0, attn0, torch.zeros(0, 5, 16, device=dev))
+    torch.cuda.synchronize()
+    assert out0.numel() == 0 and all(g.numel() == 0 for g in g0)
     # Nq = 0: nothing to compute, grad_value still zeroed
     loc = torch.rand(2, 0, 2, 1, 3, 2, device=dev)
     attn = torch.rand(2, 0, 2, 1, 3, device=dev)
