@@ -467,9 +467,9 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
 // ---- grad_value tiles
 constexpr int kTileH = 4;           // pixel rows per tile
 constexpr int kBinRange = 4096;     // tile counters a bin block keeps in LDS at once
-constexpr int kChunk = 2048;        // entries a tile block sorts in LDS at once
+constexpr int kChunk = 1024;        // entries a tile block sorts in LDS at once
 constexpr int kMaxSlabs = 32;       // bin blocks per (b, m) at most (a power of two)
-constexpr int kUnroll = 16;         // entries in flight per lane group in the sweep
+constexpr int kUnroll = 8;          // entries in flight per lane group in the sweep
 constexpr int kRecUnroll = 4;       // entries per thread in flight when building records
 
 // A tile is kTileH x TW pixels; lane group c of a tile block owns pixel column
@@ -508,38 +508,44 @@ __device__ inline void setup_tiles(const Params& p, LevelTiles* lt, int* total) 
     __syncthreads();
 }
 
-// Exclusive scan of a[0, n) into o[0, n) by the whole block; returns the total.
-// scratch holds kBlock words. a and o may alias.
+// Exclusive scan of a[0, n) into o[0, n) by the whole block; returns the total
+// to every thread. Wave 0 does the work (each lane a contiguous segment, then a
+// shuffle scan of the 64 segment sums); the rest wait at the barriers.
+// a and o may alias; scratch holds one word.
 __device__ inline uint32_t block_exclusive_scan(const uint32_t* a, uint32_t* o, int n,
                                                 uint32_t* scratch) {
-    const int tid = threadIdx.x;
-    const int per = (n + kBlock - 1) / kBlock;
-    const int lo = min(tid * per, n), hi = min(lo + per, n);
-    uint32_t s = 0;
-    for (int i = lo; i < hi; ++i) s += a[i];
-    scratch[tid] = s;
     __syncthreads();
-    for (int d = 1; d < kBlock; d <<= 1) {
-        const uint32_t v = tid >= d ? scratch[tid - d] : 0u;
-        __syncthreads();
-        scratch[tid] += v;
-        __syncthreads();
-    }
-    uint32_t run = scratch[tid] - s;
-    const uint32_t total = scratch[kBlock - 1];
-    for (int i = lo; i < hi; ++i) {
-        const uint32_t v = a[i];
-        o[i] = run;
-        run += v;
+    if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        const int per = (n + kWave - 1) / kWave;
+        const int lo = min(lane * per, n), hi = min(lo + per, n);
+        uint32_t s = 0;
+        for (int i = lo; i < hi; ++i) s += a[i];
+        uint32_t incl = s;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const uint32_t up = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += up;
+        }
+        uint32_t run = incl - s;
+        for (int i = lo; i < hi; ++i) {
+            const uint32_t v = a[i];
+            o[i] = run;
+            run += v;
+        }
+        if (lane == kWave - 1) scratch[0] = incl;
     }
     __syncthreads();
-    return total;
+    return scratch[0];
 }
 
-// Corner pixels of a point at level lt: the distinct tiles (local indices in
-// the (b, m)) that its inside-the-level corners fall in. Returns how many.
+// The distinct tiles (local indices in the (b, m)) that a point's
+// inside-the-level corners fall in, without loops or branches: tile[c] is the
+// tile of corner c (0: (y0,x0), 1: (y0,x0+1), 2: (y0+1,x0), 3: (y0+1,x0+1))
+// and emit[c] says whether corner c is inside the level and is the first
+// corner of its tile.
 template <int TW>
-__device__ inline int point_tiles(float u, float v, const LevelTiles& lt, int* tiles) {
+__device__ inline void point_tiles(float u, float v, const LevelTiles& lt, int* tile, bool* emit) {
     const float Hf = (float)lt.H, Wf = (float)lt.W;
     const float x = fmaf(u, Wf, -0.5f);
     const float y = fmaf(v, Hf, -0.5f);
@@ -550,37 +556,49 @@ __device__ inline int point_tiles(float u, float v, const LevelTiles& lt, int* t
     const bool vy1 = (y0f >= -1.0f) && (y0f < Hf - 1.0f);
     const int x0 = (int)fminf(fmaxf(x0f, -1.0f), Wf);
     const int y0 = (int)fminf(fmaxf(y0f, -1.0f), Hf);
-    const bool valid[4] = {vx0 && vy0, vx1 && vy0, vx0 && vy1, vx1 && vy1};
-    int n = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        if (!valid[c]) continue;
-        const int ty = (y0 + (c >> 1)) / kTileH, tx = (x0 + (c & 1)) / TW;  // corners are >= 0
-        const int t = lt.tile_base + ty * lt.ntx + tx;
-        bool dup = false;
-        for (int k = 0; k < n; ++k) dup |= tiles[k] == t;
-        if (!dup) tiles[n++] = t;
-    }
-    return n;
+    // tile coordinates of the two columns and rows (only used where valid,
+    // i.e. where the pixel coordinate is >= 0)
+    const int tx0 = max(x0, 0) / TW, tx1 = (x0 + 1) / TW;
+    const int ty0 = max(y0, 0) / kTileH, ty1 = (y0 + 1) / kTileH;
+    const bool v00 = vx0 && vy0, v01 = vx1 && vy0, v10 = vx0 && vy1, v11 = vx1 && vy1;
+    const bool same_x = tx0 == tx1, same_y = ty0 == ty1;
+    emit[0] = v00;
+    emit[1] = v01 && !(v00 && same_x);
+    emit[2] = v10 && !(v00 && same_y);
+    emit[3] = v11 && !(v01 && same_y) && !(v10 && same_x) && !(v00 && same_x && same_y);
+    const int r0 = lt.tile_base + ty0 * lt.ntx, r1 = lt.tile_base + ty1 * lt.ntx;
+    tile[0] = r0 + tx0;
+    tile[1] = r0 + tx1;
+    tile[2] = r1 + tx0;
+    tile[3] = r1 + tx1;
 }
 
 // Walks the points of one bin block (queries [q_begin, ...) of one (b, m)) with
-// a stride of kBlock, keeping the query offset, point slot j, level l and
-// global point index up to date without a division per point.
+// a stride of kBlock, keeping the query offset, point slot j, level l, tuple
+// and global point index up to date without a division per point.
 struct PointWalk {
     int i, qo, j, l, dq, dj, LK, K;
-    size_t pt;
+    float invK;
+    size_t t, pt;
     size_t tuple0;  // (b*Nq + q_begin)*M + m
     int M;
     __device__ PointWalk(const Params& p, int tid, int q_begin, int b, int m)
         : i(tid), LK(p.LK > 0 ? p.LK : 1), K(p.K > 0 ? p.K : 1), M(p.M) {
+        invK = 1.0f / (float)K;
         qo = i / LK;
         j = i - qo * LK;
-        l = j / K;
         dq = kBlock / LK;
         dj = kBlock - dq * LK;
         tuple0 = ((size_t)b * p.Nq + q_begin) * p.M + m;
-        pt = (tuple0 + (size_t)qo * M) * LK + j;
+        update();
+    }
+    __device__ void update() {
+        // j / K through the reciprocal, corrected by one step either way
+        l = (int)((float)j * invK);
+        l -= (l * K > j);
+        l += ((l + 1) * K <= j);
+        t = tuple0 + (size_t)qo * M;
+        pt = t * LK + j;
     }
     __device__ void next() {
         i += kBlock;
@@ -590,9 +608,7 @@ struct PointWalk {
             j -= LK;
             ++qo;
         }
-        while (l > 0 && l * K > j) --l;
-        while ((l + 1) * K <= j) ++l;
-        pt = (tuple0 + (size_t)qo * M) * LK + j;
+        update();
     }
 };
 
@@ -622,10 +638,13 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
         __syncthreads();
         for (PointWalk it(p, tid, q_begin, b, m); it.i < npts; it.next()) {
             const float2 uv = *reinterpret_cast<const float2*>(p.loc + 2 * it.pt);
-            int tiles[4];
-            const int n = point_tiles<TS::TW>(uv.x, uv.y, lt[it.l], tiles);
-            for (int k = 0; k < n; ++k)
-                if (tiles[k] >= r0 && tiles[k] < r0 + rn) atomicAdd(&cnt[tiles[k] - r0], 1u);
+            int tile[4];
+            bool emit[4];
+            point_tiles<TS::TW>(uv.x, uv.y, lt[it.l], tile, emit);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (emit[c] && tile[c] >= r0 && tile[c] < r0 + rn) atomicAdd(&cnt[tile[c] - r0], 1u);
+            }
         }
         __syncthreads();
         const uint32_t total = block_exclusive_scan(cnt, off, rn, scratch);
@@ -635,20 +654,21 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
         __syncthreads();
         for (PointWalk it(p, tid, q_begin, b, m); it.i < npts; it.next()) {
             const float2 uv = *reinterpret_cast<const float2*>(p.loc + 2 * it.pt);
-            int tiles[4];
-            const int n = point_tiles<TS::TW>(uv.x, uv.y, lt[it.l], tiles);
-            if (n == 0) continue;
+            int tile[4];
+            bool emit[4];
+            const LevelTiles& L_ = lt[it.l];
+            point_tiles<TS::TW>(uv.x, uv.y, L_, tile, emit);
             // the entry carries all the tile kernel needs: the tuple (its
             // upstream-gradient row), the fp32 pixel coordinates (cell and
             // fractions follow from them exactly as here) and the weight
-            const LevelTiles& L_ = lt[it.l];
-            const float4 rec = make_float4(as_float((uint32_t)(it.pt / (size_t)p.LK)),
-                                           fmaf(uv.x, (float)L_.W, -0.5f),
+            const float4 rec = make_float4(as_float((uint32_t)it.t), fmaf(uv.x, (float)L_.W, -0.5f),
                                            fmaf(uv.y, (float)L_.H, -0.5f), p.attn[it.pt]);
-            for (int k = 0; k < n; ++k) {
-                if (tiles[k] < r0 || tiles[k] >= r0 + rn) continue;
-                const uint32_t slot = base + off[tiles[k] - r0] + atomicAdd(&cnt[tiles[k] - r0], 1u);
-                slab[slot] = rec;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (emit[c] && tile[c] >= r0 && tile[c] < r0 + rn) {
+                    const uint32_t slot = atomicAdd(&cnt[tile[c] - r0], 1u);
+                    slab[base + off[tile[c] - r0] + slot] = rec;
+                }
             }
         }
         base += total;
@@ -678,6 +698,9 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
     const int tid = threadIdx.x;
     const int BM = p.B * p.M;
     const int col = tid / G, r = tid % G;
+    // upstream-gradient rows through a buffer descriptor: 32-bit offsets
+    const __amdgpu_buffer_rsrc_t grsrc =
+        make_rsrc(p.grad_out, (uint32_t)((size_t)p.T * D * sizeof(float)));
 
     // XCD-affine schedule (the grid is a multiple of 8): with 8 or more
     // (b, m), XCD x takes the (b, m) = x (mod 8) one after the other, so its
@@ -730,8 +753,10 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
                     const uint32_t ge = c0 + min(e0 + u * kBlock, n - 1);
                     int lo = 0;   // last slab whose start <= ge (nW <= kMaxSlabs)
 #pragma unroll
-                    for (int step = kMaxSlabs / 2; step > 0; step >>= 1)
-                        if (lo + step < p.nW && wstart[lo + step] <= ge) lo += step;
+                    for (int step = kMaxSlabs / 2; step > 0; step >>= 1) {
+                        const int probe = min(lo + step, p.nW - 1);
+                        lo = wstart[probe] <= ge ? probe : lo;
+                    }
                     ent[u] = p.slab[((size_t)bm * p.nW + lo) * p.slab_per_block + woff[lo] +
                                     (ge - wstart[lo])];
                 }
@@ -779,7 +804,10 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
                     for (int u = 0; u < kUnroll; ++u) {
                         const uint32_t i = min(k + u, e - 1);
                         const float4 rv = rec[sorted[i]];
-                        gv[u] = *reinterpret_cast<const float4*>(p.grad_out + as_uint(rv.x) + r * 4);
+                        const u32x4 graw = __builtin_amdgcn_raw_buffer_load_b128(
+                            grsrc, (as_uint(rv.x) + (uint32_t)r * 4u) * 4u, 0, 0);
+                        gv[u] = make_float4(as_float(graw[0]), as_float(graw[1]), as_float(graw[2]),
+                                            as_float(graw[3]));
                         // the cell left of the column gives its right corners
                         // (fx), the cell at the column its left corners (1 - fx)
                         const float wx = i >= split ? 1.0f - rv.w : rv.w;
