@@ -13,8 +13,12 @@ events on the launch stream, and
 the CPU oracle's rate on the host (a bounded sample of the same workload).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --calibrate-copy MIB   (a plain copy-like kernel of known size,
+                                               run under the counter profiler to scale
+                                               its byte counters)
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -50,6 +54,60 @@ def algorithmic_bytes(w, value_bytes_per_elem=4):
             "step": fwd + bwd}
 
 
+KERNEL_SOURCE = os.path.join(ROOT, "scale_deformable_attention_amd", "csrc", "msda.hip")
+
+
+def source_digest():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """Per-dispatch HBM-side byte counters of each kernel, from the committed
+    counter summary for this workload (profiles/msda_kernels_<workload>_traffic.txt).
+
+    The summary holds FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged over
+    the dispatches of one run) for every kernel, the same two counters for the
+    calibration copy kernel with its known byte counts, and the digest of the
+    kernel source the counters were taken with. Returns {kernel: bytes per
+    dispatch}, or None if the file is missing or the kernels have changed since."""
+    path = os.path.join(ROOT, "profiles", f"msda_kernels_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kern, calib, digest = {}, None, None
+    with open(path) as f:
+        for line in f:
+            t = line.split()
+            if not t or t[0].startswith("#"):
+                continue
+            if t[0] == "source_sha256":
+                digest = t[1]
+            elif t[0] == "copy":       # copy <read bytes> <written bytes> <FETCH KiB> <WRITE KiB>
+                calib = tuple(float(v) for v in t[1:5])
+            elif t[0] == "kernel":     # kernel <name> <FETCH KiB> <WRITE KiB> <dispatches>
+                kern[t[1]] = (float(t[2]), float(t[3]))
+    if digest != source_digest() or calib is None:
+        return None
+    f_read = calib[0] / (calib[2] * 1024.0)
+    f_write = calib[1] / (calib[3] * 1024.0)
+    return {k: fk * 1024.0 * f_read + wk * 1024.0 * f_write for k, (fk, wk) in kern.items()}
+
+
+def calibrate_copy(mib):
+    """Launch a plain elementwise kernel (dst = -src, fp32) over mib MiB five
+    times: it reads and writes exactly mib MiB each, so its FETCH_SIZE and
+    WRITE_SIZE readings give the counters' scale."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "neg fp32", "bytes_read": n * 4, "bytes_written": n * 4,
+                      "launches": 5}), flush=True)
+
+
 def cpu_baseline(w, x, budget_s):
     """The oracle as it stands (single thread) on a bounded sample: whole batch
     entries of the workload, forward + backward, until the budget is used."""
@@ -83,12 +141,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the core runs on a single MI355X; sharding across "
-              "GPUs (batch or head split) is described in DESIGN.md but not run here.",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the core runs on a single MI355X. A layer is "
+              "sharded across GPUs by batch or by head, which needs no exchange, so the "
+              "per-GPU figure is the one-GPU run at the per-GPU shape.", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import torch
     import scale_deformable_attention_amd as msda
@@ -178,6 +240,10 @@ def main():
     dom_name = max(kernels, key=kernels.get)
     dom_ms, dom_bytes = kernels[dom_name], kernel_bytes[dom_name]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    measured = read_traffic(w.name)
+    traffic = None
+    if measured is not None and all(k in measured for k in dom_name.split("+")):
+        traffic = sum(measured[k] for k in dom_name.split("+"))
     step_bytes = ab["step"] if backward else ab["forward"]
     step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
 
@@ -200,10 +266,13 @@ def main():
                    "points_per_step": w.points, "global_batch": w.B, "parallelism": "none"},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes": dom_bytes, "avg_ms": dom_ms},
+                     "traffic": traffic, "algorithmic_bytes": dom_bytes, "avg_ms": dom_ms,
+                     "launches": len(dom_name.split("+"))},
         "step_roofline": {"algorithmic_bytes": step_bytes, "achieved": step_gbs,
                           "frac": step_gbs / HBM_PEAK_GBS},
         "kernels_ms": kernels,
+        "kernels_frac": {k: kernel_bytes[k] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS
+                         for k, v in kernels.items()},
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:
