@@ -57,6 +57,14 @@ struct bf16_t {
 __device__ inline float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ inline uint32_t as_uint(float f) { return __builtin_bit_cast(uint32_t, f); }
 
+// A 16-byte load marked non-temporal: for data read exactly once (the bin
+// entries), so that it does not push reused rows out of L2.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ inline float4 load_streaming(const float4* p) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
 template <typename T>
 struct Elem;
 template <>
@@ -466,9 +474,10 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
 
 // ---- grad_value tiles
 constexpr int kTileH = 4;           // pixel rows per tile
-constexpr int kBinRange = 4096;     // tile counters a bin block keeps in LDS at once
+constexpr int kBinRange = 1024;     // tile counters a bin block keeps in LDS at once
+constexpr int kBinUnroll = 4;       // points per thread in flight in the bin kernel
 constexpr int kChunk = 1024;        // entries a tile block sorts in LDS at once
-constexpr int kMaxSlabs = 32;       // bin blocks per (b, m) at most (a power of two)
+constexpr int kMaxSlabs = 64;       // bin blocks per (b, m) at most (a power of two)
 constexpr int kUnroll = 8;          // entries in flight per lane group in the sweep
 constexpr int kRecUnroll = 4;       // entries per thread in flight when building records
 
@@ -581,6 +590,7 @@ struct PointWalk {
     float invK;
     size_t t, pt;
     size_t tuple0;  // (b*Nq + q_begin)*M + m
+    size_t pt0;     // the walk's first point (valid whenever the walk is not empty)
     int M;
     __device__ PointWalk(const Params& p, int tid, int q_begin, int b, int m)
         : i(tid), LK(p.LK > 0 ? p.LK : 1), K(p.K > 0 ? p.K : 1), M(p.M) {
@@ -590,6 +600,7 @@ struct PointWalk {
         dq = kBlock / LK;
         dj = kBlock - dq * LK;
         tuple0 = ((size_t)b * p.Nq + q_begin) * p.M + m;
+        pt0 = tuple0 * LK;
         update();
     }
     __device__ void update() {
@@ -632,18 +643,33 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
     uint2* row = p.table + (size_t)blockIdx.x * p.t_stride;
     float4* slab = p.slab + (size_t)blockIdx.x * p.slab_per_block;
     uint32_t base = 0;
+    // a point index that is always valid (npts > 0 whenever a loop body runs)
+    // stands in for the lanes past the end, so that every load is unconditional
     for (int r0 = 0; r0 < T; r0 += kBinRange) {
         const int rn = min(kBinRange, T - r0);
         for (int i = tid; i < rn; i += kBlock) cnt[i] = 0;
         __syncthreads();
-        for (PointWalk it(p, tid, q_begin, b, m); it.i < npts; it.next()) {
-            const float2 uv = *reinterpret_cast<const float2*>(p.loc + 2 * it.pt);
-            int tile[4];
-            bool emit[4];
-            point_tiles<TS::TW>(uv.x, uv.y, lt[it.l], tile, emit);
+        for (PointWalk it(p, tid, q_begin, b, m); it.i < npts;) {
+            float2 uv[kBinUnroll];
+            int lvl[kBinUnroll];
+            bool ok[kBinUnroll];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if (emit[c] && tile[c] >= r0 && tile[c] < r0 + rn) atomicAdd(&cnt[tile[c] - r0], 1u);
+            for (int u = 0; u < kBinUnroll; ++u) {
+                ok[u] = it.i < npts;
+                lvl[u] = it.l;
+                uv[u] = *reinterpret_cast<const float2*>(p.loc + 2 * (ok[u] ? it.pt : it.pt0));
+                it.next();
+            }
+#pragma unroll
+            for (int u = 0; u < kBinUnroll; ++u) {
+                int tile[4];
+                bool emit[4];
+                point_tiles<TS::TW>(uv[u].x, uv[u].y, lt[lvl[u]], tile, emit);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (ok[u] && emit[c] && tile[c] >= r0 && tile[c] < r0 + rn)
+                        atomicAdd(&cnt[tile[c] - r0], 1u);
+                }
             }
         }
         __syncthreads();
@@ -652,22 +678,39 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
         __syncthreads();
         for (int i = tid; i < rn; i += kBlock) cnt[i] = 0;
         __syncthreads();
-        for (PointWalk it(p, tid, q_begin, b, m); it.i < npts; it.next()) {
-            const float2 uv = *reinterpret_cast<const float2*>(p.loc + 2 * it.pt);
-            int tile[4];
-            bool emit[4];
-            const LevelTiles& L_ = lt[it.l];
-            point_tiles<TS::TW>(uv.x, uv.y, L_, tile, emit);
-            // the entry carries all the tile kernel needs: the tuple (its
-            // upstream-gradient row), the fp32 pixel coordinates (cell and
-            // fractions follow from them exactly as here) and the weight
-            const float4 rec = make_float4(as_float((uint32_t)it.t), fmaf(uv.x, (float)L_.W, -0.5f),
-                                           fmaf(uv.y, (float)L_.H, -0.5f), p.attn[it.pt]);
+        for (PointWalk it(p, tid, q_begin, b, m); it.i < npts;) {
+            float2 uv[kBinUnroll];
+            float a[kBinUnroll];
+            int lvl[kBinUnroll];
+            bool ok[kBinUnroll];
+            uint32_t tup[kBinUnroll];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if (emit[c] && tile[c] >= r0 && tile[c] < r0 + rn) {
-                    const uint32_t slot = atomicAdd(&cnt[tile[c] - r0], 1u);
-                    slab[base + off[tile[c] - r0] + slot] = rec;
+            for (int u = 0; u < kBinUnroll; ++u) {
+                ok[u] = it.i < npts;
+                lvl[u] = it.l;
+                tup[u] = (uint32_t)it.t;
+                const size_t pt = ok[u] ? it.pt : it.pt0;
+                uv[u] = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
+                a[u] = p.attn[pt];
+                it.next();
+            }
+#pragma unroll
+            for (int u = 0; u < kBinUnroll; ++u) {
+                int tile[4];
+                bool emit[4];
+                const LevelTiles& L_ = lt[lvl[u]];
+                point_tiles<TS::TW>(uv[u].x, uv[u].y, L_, tile, emit);
+                // the entry carries all the tile kernel needs: the tuple (its
+                // upstream-gradient row), the fp32 pixel coordinates (cell and
+                // fractions follow from them exactly as here) and the weight
+                const float4 rec = make_float4(as_float(tup[u]), fmaf(uv[u].x, (float)L_.W, -0.5f),
+                                               fmaf(uv[u].y, (float)L_.H, -0.5f), a[u]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (ok[u] && emit[c] && tile[c] >= r0 && tile[c] < r0 + rn) {
+                        const uint32_t slot = atomicAdd(&cnt[tile[c] - r0], 1u);
+                        slab[base + off[tile[c] - r0] + slot] = rec;
+                    }
                 }
             }
         }
@@ -757,8 +800,8 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
                         const int probe = min(lo + step, p.nW - 1);
                         lo = wstart[probe] <= ge ? probe : lo;
                     }
-                    ent[u] = p.slab[((size_t)bm * p.nW + lo) * p.slab_per_block + woff[lo] +
-                                    (ge - wstart[lo])];
+                    ent[u] = load_streaming(p.slab + ((size_t)bm * p.nW + lo) * p.slab_per_block +
+                                            woff[lo] + (ge - wstart[lo]));
                 }
 #pragma unroll
                 for (int u = 0; u < kRecUnroll; ++u) {
@@ -904,8 +947,8 @@ BwdPlan plan_backward(const msda_dims_t* d) {
     BwdPlan pl;
     const int64_t BM = d->B * d->M;
     if (BM == 0) return pl;
-    // about 2048 bin blocks in total, at most kMaxSlabs per (b, m)
-    int64_t nW = (2048 + BM - 1) / BM;
+    // about 4096 bin blocks in total, at most kMaxSlabs per (b, m)
+    int64_t nW = (4096 + BM - 1) / BM;
     nW = nW < 1 ? 1 : (nW > kMaxSlabs ? kMaxSlabs : nW);
     if (d->Nq > 0 && nW > d->Nq) nW = d->Nq;
     const int64_t Qc = d->Nq > 0 ? (d->Nq + nW - 1) / nW : 0;
