@@ -31,6 +31,8 @@
 
 #include <stdint.h>
 
+#include <atomic>
+
 #include "msda.h"
 
 namespace {
@@ -119,6 +121,7 @@ struct Params {
     uint32_t slab_per_block;  // point-index capacity of one bin block's slab
     uint2* table;             // [B*M*nW][t_stride] (count, offset)
     float4* slab;             // [B*M*nW][slab_per_block] (tuple bits, x, y, A) entries
+    uint32_t* counters;       // [8] tile work counters, one per XCD group
 };
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -517,35 +520,55 @@ __device__ inline void setup_tiles(const Params& p, LevelTiles* lt, int* total) 
     __syncthreads();
 }
 
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ inline uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, BOUND_ZERO);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8
+// within each row of 16 lanes (lanes shifted in from outside the row read 0),
+// then the last lane of row 0 is added to row 1 and 3 (row broadcast 15) and
+// the last lane of row 1 to rows 2 and 3 (row broadcast 31).
+__device__ inline uint32_t wave_inclusive_scan(uint32_t x) {
+    x += dpp_u32<0x111, 0xF, true>(x);   // row_shr:1
+    x += dpp_u32<0x112, 0xF, true>(x);   // row_shr:2
+    x += dpp_u32<0x114, 0xF, true>(x);   // row_shr:4
+    x += dpp_u32<0x118, 0xF, true>(x);   // row_shr:8
+    x += dpp_u32<0x142, 0xA, false>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_u32<0x143, 0xC, false>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
 // Exclusive scan of a[0, n) into o[0, n) by the whole block; returns the total
-// to every thread. Wave 0 does the work (each lane a contiguous segment, then a
-// shuffle scan of the 64 segment sums); the rest wait at the barriers.
-// a and o may alias; scratch holds one word.
+// to every thread. Each thread takes a contiguous segment, the segment sums
+// are scanned per wave with DPP and the wave totals combined through LDS.
+// a and o may alias; scratch holds kWavesPerBlock words.
 __device__ inline uint32_t block_exclusive_scan(const uint32_t* a, uint32_t* o, int n,
                                                 uint32_t* scratch) {
     __syncthreads();
-    if (threadIdx.x < kWave) {
-        const int lane = threadIdx.x;
-        const int per = (n + kWave - 1) / kWave;
-        const int lo = min(lane * per, n), hi = min(lo + per, n);
-        uint32_t s = 0;
-        for (int i = lo; i < hi; ++i) s += a[i];
-        uint32_t incl = s;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int per = (n + kBlock - 1) / kBlock;
+    const int lo = min(tid * per, n), hi = min(lo + per, n);
+    uint32_t s = 0;
+    for (int i = lo; i < hi; ++i) s += a[i];
+    const uint32_t incl = wave_inclusive_scan(s);
+    if (lane == kWave - 1) scratch[wave] = incl;
+    __syncthreads();
+    uint32_t base = 0, total = 0;
 #pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const uint32_t up = __shfl_up(incl, d, kWave);
-            if (lane >= d) incl += up;
-        }
-        uint32_t run = incl - s;
-        for (int i = lo; i < hi; ++i) {
-            const uint32_t v = a[i];
-            o[i] = run;
-            run += v;
-        }
-        if (lane == kWave - 1) scratch[0] = incl;
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+        const uint32_t t = scratch[w];
+        base += w < wave ? t : 0u;
+        total += t;
+    }
+    uint32_t run = base + incl - s;
+    for (int i = lo; i < hi; ++i) {
+        const uint32_t v = a[i];
+        o[i] = run;
+        run += v;
     }
     __syncthreads();
-    return scratch[0];
+    return total;
 }
 
 // The distinct tiles (local indices in the (b, m)) that a point's
@@ -630,7 +653,7 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
     __shared__ int s_tiles;
     __shared__ uint32_t cnt[kBinRange];
     __shared__ uint32_t off[kBinRange];
-    __shared__ uint32_t scratch[kBlock];
+    __shared__ uint32_t scratch[kWavesPerBlock];
     setup_tiles<TS::TW>(p, lt, &s_tiles);
     // tables inconsistent with Nv could exceed the row: drop those tiles
     // rather than write past the workspace
@@ -642,6 +665,7 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
     const int npts = (q_end - q_begin) * p.LK;
     uint2* row = p.table + (size_t)blockIdx.x * p.t_stride;
     float4* slab = p.slab + (size_t)blockIdx.x * p.slab_per_block;
+    if (blockIdx.x == 0 && tid < 8) p.counters[tid] = 0;   // for the tile kernel that follows
     uint32_t base = 0;
     // a point index that is always valid (npts > 0 whenever a loop body runs)
     // stands in for the lanes past the end, so that every load is unconditional
@@ -719,23 +743,24 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
     }
 }
 
-// One work item = one tile of one (b, m). Work items run coarse levels first
-// (the most points per pixel, the longest lists), and consecutive items step
-// through (b, m) so that a block keeps one (b, m) residue mod 8 (one XCD, one
-// L2) when the grid and B*M are multiples of 8.
+// One work item = one tile of one (b, m). Work items are fetched dynamically
+// from a counter per XCD group (blocks i = x mod 8 run on XCD x and serve the
+// (b, m) = x mod 8, so an XCD's L2 sees only its own (b, m)), coarse levels
+// first: those tiles have the most points per pixel and the longest lists, and
+// start first.
 template <int D>
 __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
     using TS = TileShape<D>;
     constexpr int TW = TS::TW, G = TS::G, kCells = TS::kCells;
     __shared__ LevelTiles lt[MSDA_MAX_LEVELS];
-    __shared__ int s_tiles;
+    __shared__ int s_tiles, s_item;
     __shared__ uint32_t wcnt[kMaxSlabs], wstart[kMaxSlabs], woff[kMaxSlabs];
     __shared__ float4 rec[kChunk];        // (grad_out float index bits, A*(1-fy), A*fy, fx)
     __shared__ uint16_t cell_of[kChunk];
     __shared__ uint16_t sorted[kChunk];
     __shared__ uint32_t cstart[kCells + 1];
     __shared__ uint32_t ccount[kCells + 1];
-    __shared__ uint32_t scratch[kBlock];
+    __shared__ uint32_t scratch[kWavesPerBlock];
     setup_tiles<TW>(p, lt, &s_tiles);
     const int T = min(s_tiles, p.t_stride);
     const int tid = threadIdx.x;
@@ -745,19 +770,18 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
     const __amdgpu_buffer_rsrc_t grsrc =
         make_rsrc(p.grad_out, (uint32_t)((size_t)p.T * D * sizeof(float)));
 
-    // XCD-affine schedule (the grid is a multiple of 8): with 8 or more
-    // (b, m), XCD x takes the (b, m) = x (mod 8) one after the other, so its
-    // L2 holds one (b, m)'s upstream-gradient rows at a time; within one
-    // (b, m) the coarse levels (the most points per pixel) go first. With
-    // fewer (b, m) the items are dealt round-robin.
-    const int xcd = blockIdx.x % 8, jx = blockIdx.x / 8, nj = gridDim.x / 8;
+    const int xcd = blockIdx.x % 8;
     const int nbm_x = BM >= 8 ? (BM - xcd + 7) / 8 : 0;
     const int items = BM >= 8 ? nbm_x * T : (BM * T - xcd + 7) / 8;
-    for (int k = jx; k < items; k += nj) {
+    for (;;) {
+        if (tid == 0) s_item = (int)atomicAdd(p.counters + xcd, 1u);
+        __syncthreads();
+        const int k = s_item;
+        if (k >= items) break;
         int bm, tl;
         if (BM >= 8) {
-            bm = xcd + 8 * (k / T);
-            tl = T - 1 - k % T;
+            bm = xcd + 8 * (k % nbm_x);
+            tl = T - 1 - k / nbm_x;
         } else {
             const int it = xcd + 8 * k;
             bm = it % BM;
@@ -929,16 +953,17 @@ msda_status_t check_dims(const msda_dims_t* d, msda_dtype_t dt, bool backward) {
     return MSDA_SUCCESS;
 }
 
-// Workspace of the grad_value path (bin + tile kernels): per (b, m), nW bin
-// blocks each own Qc queries, a row of (count, offset) per tile and a slab of
-// 16-byte entries (at most 4 per point: one per corner tile). The
+// Workspace of the grad_value path (bin + tile kernels): 8 work counters of
+// the tile kernel, then per (b, m), nW bin blocks each own Qc queries, a row of
+// (count, offset) per tile and a slab of 16-byte entries (at most 4 per point:
+// one per corner tile). The
 // tile count of one (b, m) is bounded from Nv and L alone: a level of H x W
 // pixels has ceil(H/4) ceil(W/TW) tiles (TW >= 16), which is at most
 // H/4 + 3/4 when W <= TW and at most (H+3) W / (2 TW) <= H W / 8 otherwise,
 // so sum_l <= Nv/4 + L.
 struct BwdPlan {
     int64_t nW = 0, Qc = 0, t_stride = 0, slab_per_block = 0;
-    size_t table_off = 0, slab_off = 0, bytes = 0;
+    size_t counters_off = 0, table_off = 0, slab_off = 0, bytes = 0;
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -959,8 +984,9 @@ BwdPlan plan_backward(const msda_dims_t* d) {
     pl.slab_per_block = round_up((size_t)(4 * Qc * d->L * d->K), 64);
     const size_t table_bytes = (size_t)(BM * pl.nW * pl.t_stride) * sizeof(uint2);
     const size_t slab_bytes = (size_t)(BM * pl.nW * pl.slab_per_block) * sizeof(float4);
-    pl.table_off = 0;
-    pl.slab_off = round_up(table_bytes, kWorkspaceAlign);
+    pl.counters_off = 0;
+    pl.table_off = kWorkspaceAlign;   // after the 8 work counters
+    pl.slab_off = pl.table_off + round_up(table_bytes, kWorkspaceAlign);
     pl.bytes = pl.slab_off + round_up(slab_bytes, kWorkspaceAlign);
     return pl;
 }
@@ -996,6 +1022,18 @@ Sizes sizes_of(const msda_dims_t* d) {
     s.points = d->B * d->Nq * d->M * d->L * d->K;
     s.out = d->B * d->Nq * d->M * d->D;
     return s;
+}
+
+// Blocks of the tile kernel that fit on one CU, asked of the runtime once per
+// kernel and kept.
+int tile_blocks_per_cu(int64_t D, const void* kernel) {
+    static std::atomic<int> known[4];
+    std::atomic<int>& slot = known[D == 8 ? 0 : D == 16 ? 1 : D == 32 ? 2 : 3];
+    int n = slot.load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kBlock, 0) != hipSuccess || n < 1) n = 1;
+    slot.store(n, std::memory_order_relaxed);
+    return n;
 }
 
 msda_status_t launch(const void* kernel, int64_t blocks, Params& p, hipStream_t stream) {
@@ -1110,13 +1148,21 @@ msda_status_t msda_backward(const msda_dims_t* dims, msda_dtype_t value_dtype, c
         p.slab_per_block = (uint32_t)pl.slab_per_block;
         p.table = reinterpret_cast<uint2*>(static_cast<char*>(workspace) + pl.table_off);
         p.slab = reinterpret_cast<float4*>(static_cast<char*>(workspace) + pl.slab_off);
+        p.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + pl.counters_off);
         const int64_t BM = dims->B * dims->M;
         msda_status_t s = launch(k.bin, BM * pl.nW, p, stream);
         if (s != MSDA_SUCCESS) return s;
-        // persistent: blocks loop over the (b, m, tile) work items; the grid
-        // is a multiple of 8 for the XCD-affine schedule
+        // persistent: blocks fetch (b, m, tile) work items, as many blocks as
+        // fit on the GPU at once; the grid is a multiple of 8 for the
+        // XCD-affine schedule
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return MSDA_ERROR_LAUNCH;
+        const int per_cu = tile_blocks_per_cu(dims->D, k.tile);
         const int64_t items = BM * pl.t_stride;
-        const int64_t grid = items < 2048 ? ((items + 7) / 8) * 8 : 2048;
+        const int64_t resident = ((int64_t)per_cu * (cus > 0 ? cus : 1) + 7) / 8 * 8;
+        const int64_t grid = items < resident ? ((items + 7) / 8) * 8 : resident;
         s = launch(k.tile, grid, p, stream);
         if (s != MSDA_SUCCESS) return s;
     }
