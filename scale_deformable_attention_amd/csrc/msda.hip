@@ -478,8 +478,8 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
 // ---- grad_value tiles
 constexpr int kTileH = 4;           // pixel rows per tile
 constexpr int kBinRange = 1024;     // tile counters a bin block keeps in LDS at once
-constexpr int kBinUnroll = 4;       // points per thread in flight in the bin kernel
-constexpr int kChunk = 1024;        // entries a tile block sorts in LDS at once
+constexpr int kBinUnroll = 8;       // points per thread in flight in the bin kernel
+constexpr int kChunk = 2048;        // entries a tile block sorts in LDS at once
 constexpr int kMaxSlabs = 64;       // bin blocks per (b, m) at most (a power of two)
 constexpr int kUnroll = 8;          // entries in flight per lane group in the sweep
 constexpr int kRecUnroll = 4;       // entries per thread in flight when building records
