@@ -344,18 +344,15 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
 //     sums live in registers. Every grad_value element is then written exactly
 //     once with a plain store (zeros where nothing lands), so no fill pass.
 
-struct alignas(16) PointRecord {
-    uint32_t off[4];
-    float dot[4];  // sum_d g[d] * v_c[d], filled by the gathering group
-};
-
 template <typename T, int D>
 __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
     using S = Shape<T, D>;
     constexpr int G = S::G, TPW = S::TPW, PL = S::kPerLane;
     constexpr int kRowBytesPerHead = D * Elem<T>::kBytes;
     __shared__ int4 levels[MSDA_MAX_LEVELS];
-    __shared__ PointRecord records[kWavesPerBlock][kWave];
+    // corner offsets of the points of a chunk: group g's at row g (padded by
+    // one slot so that the groups' broadcast reads fall in different banks)
+    __shared__ uint4 offs[kWavesPerBlock][TPW][G + 1];
     load_levels(p, levels);
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -365,19 +362,18 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
     const uint32_t row_bytes = (uint32_t)p.M * kRowBytesPerHead;
     const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(p.value, p.value_bytes);
 
-    const int t1w = tuple0 + lane % TPW;
-    const int t1 = t1w < p.T ? tuple_of(p, t1w) : 0;
-    const int jrow = lane / TPW;
-    const bool t1_ok = t1w < p.T;
-    const uint32_t base1 = t1_ok ? tuple_base_bytes(p, t1, row_bytes, kRowBytesPerHead) : 0;
+    // lane r of group g: channels [r*PL, r*PL + PL) of tuple g's rows, and
+    // point jc + r of tuple g in chunk jc (built, then finished, by this lane)
     const int g = lane / G, r = lane % G;
-    const int t2w = tuple0 + g;
-    const int t2 = t2w < p.T ? tuple_of(p, t2w) : p.T;
+    const int tw = tuple0 + g;
+    const bool t_ok = tw < p.T;
+    const int t = t_ok ? tuple_of(p, tw) : 0;
+    const uint32_t base = t_ok ? tuple_base_bytes(p, t, row_bytes, kRowBytesPerHead) : 0;
 
     // upstream gradient of the group's tuple, this lane's channels
     float go[PL];
-    if (t2 < p.T) {
-        const float4* src = reinterpret_cast<const float4*>(p.grad_out + (size_t)t2 * D + r * PL);
+    if (t_ok) {
+        const float4* src = reinterpret_cast<const float4*>(p.grad_out + (size_t)t * D + r * PL);
 #pragma unroll
         for (int e = 0; e < PL; e += 4) {
             const float4 v4 = src[e / 4];
@@ -393,21 +389,20 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
 
     for (int jc = 0; jc < p.LK; jc += G) {
         // phase 1: this lane's point -> corner offsets in LDS; keep the rest
-        const int j = jc + jrow;
-        const bool mine = t1_ok && j < p.LK;
+        const int j = jc + r;
+        const bool mine = t_ok && j < p.LK;
         size_t pt = 0;
         float a = 0.0f, Hf = 0.0f, Wf = 0.0f;
         Geometry geo;
-        PointRecord rec;
         if (mine) {
             const int l = (unsigned)j / (unsigned)p.K;
             const int4 lv = levels[l];
-            pt = (size_t)t1 * p.LK + j;
+            pt = (size_t)t * p.LK + j;
             const float2 uv = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
             a = p.attn[pt];
             Hf = (float)lv.x;
             Wf = (float)lv.y;
-            geo = point_geometry(uv.x, uv.y, lv, base1, row_bytes);
+            geo = point_geometry(uv.x, uv.y, lv, base, row_bytes);
         } else {
             geo.fx = geo.fy = 0.0f;
 #pragma unroll
@@ -416,19 +411,15 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
                 geo.off[c] = kOutside;
             }
         }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            rec.off[c] = geo.off[c];
-            rec.dot[c] = 0.0f;
-        }
-        records[wave][lane] = rec;
+        offs[wave][g][r] = make_uint4(geo.off[0], geo.off[1], geo.off[2], geo.off[3]);
         wave_sync();
-        // phase 2: gather and per-corner dot products, reduced over the group
+        // phase 2: the group gathers its G points and forms the per-corner dot
+        // products, reduced over the group; lane i keeps those of point i
+        float mine_dot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            const int slot = i * TPW + g;
-            const uint4 offs = *reinterpret_cast<const uint4*>(records[wave][slot].off);
-            const uint32_t off[4] = {offs.x, offs.y, offs.z, offs.w};
+            const uint4 o4 = offs[wave][g][i];
+            const uint32_t off[4] = {o4.x, o4.y, o4.z, o4.w};
             float dot[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -442,36 +433,32 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
                 dot[c] = s;
             }
 #pragma unroll
-            for (int c = 0; c < 4; ++c) dot[c] = group_sum<G>(dot[c]);
-            if (r == 0)
-                *reinterpret_cast<float4*>(records[wave][slot].dot) =
-                    make_float4(dot[0], dot[1], dot[2], dot[3]);
+            for (int c = 0; c < 4; ++c) {
+                dot[c] = group_sum<G>(dot[c]);
+                mine_dot[c] = r == i ? dot[c] : mine_dot[c];
+            }
         }
-        wave_sync();
-        // phase 3: the record's owner turns the dot products into the weight
-        // and location gradients of its point
+        wave_sync();   // the next chunk rewrites offs
+        // phase 3: this lane turns the dot products into the weight and
+        // location gradients of its point
         if (mine) {
-            const float4 d4 = *reinterpret_cast<const float4*>(records[wave][lane].dot);
-            const float dot[4] = {d4.x, d4.y, d4.z, d4.w};
             const float fx = geo.fx, fy = geo.fy;
-            const float w[4] = {(1.0f - fx) * (1.0f - fy), fx * (1.0f - fy), (1.0f - fx) * fy,
-                                fx * fy};
+            const float w[4] = {(1.0f - fx) * (1.0f - fy), fx * (1.0f - fy), (1.0f - fx) * fy, fx * fy};
             const float dwdx[4] = {-(1.0f - fy), (1.0f - fy), -fy, fy};
             const float dwdy[4] = {-(1.0f - fx), -fx, (1.0f - fx), fx};
             float ga = 0.0f, gx = 0.0f, gy = 0.0f;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 if (geo.valid[c]) {
-                    ga = fmaf(w[c], dot[c], ga);
-                    gx = fmaf(dwdx[c], dot[c], gx);
-                    gy = fmaf(dwdy[c], dot[c], gy);
+                    ga = fmaf(w[c], mine_dot[c], ga);
+                    gx = fmaf(dwdx[c], mine_dot[c], gx);
+                    gy = fmaf(dwdy[c], mine_dot[c], gy);
                 }
             }
             if (p.grad_attn) p.grad_attn[pt] = ga;
             if (p.grad_loc)
                 *reinterpret_cast<float2*>(p.grad_loc + 2 * pt) = make_float2(a * Wf * gx, a * Hf * gy);
         }
-        wave_sync();
     }
 }
 
