@@ -270,16 +270,27 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
 #pragma unroll
     for (int e = 0; e < PL; ++e) acc[e] = 0.0f;
 
+    // this lane's point of the next chunk: its location and weight are loaded
+    // one chunk ahead, while the current chunk's rows are gathered
+    auto fetch = [&](int jc, float2& uv, float& a) {
+        const int j = jc + jrow;
+        const size_t pt = (size_t)t1 * p.LK + min(j, p.LK - 1);
+        uv = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
+        a = p.attn[pt];
+    };
+    float2 uv_next = make_float2(0.f, 0.f);
+    float a_next = 0.0f;
+    if (t1_ok && p.LK > 0) fetch(0, uv_next, a_next);
     for (int jc = 0; jc < p.LK; jc += G) {
+        const float2 uv = uv_next;
+        const float a = a_next;
+        if (t1_ok && jc + G < p.LK) fetch(jc + G, uv_next, a_next);
         // phase 1: one point per lane -> record in LDS
         FwdRecord rec;
         const int j = jc + jrow;
         if (t1_ok && j < p.LK) {
             const int l = (unsigned)j / (unsigned)p.K;
             const int4 lv = levels[l];
-            const size_t pt = (size_t)t1 * p.LK + j;
-            const float2 uv = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
-            const float a = p.attn[pt];
             const Geometry geo = point_geometry(uv.x, uv.y, lv, base1, row_bytes);
             const float ay0 = a * (1.0f - geo.fy), ay1 = a * geo.fy;
             const float w[4] = {ay0 * (1.0f - geo.fx), ay0 * geo.fx, ay1 * (1.0f - geo.fx),
@@ -387,19 +398,30 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
         for (int e = 0; e < PL; ++e) go[e] = 0.0f;
     }
 
+    // this lane's point of the next chunk: its location and weight are loaded
+    // one chunk ahead, while the current chunk's rows are gathered
+    auto fetch = [&](int jc, float2& uv, float& a) {
+        const size_t pt = (size_t)t * p.LK + min(jc + r, p.LK - 1);
+        uv = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
+        a = p.attn[pt];
+    };
+    float2 uv_next = make_float2(0.f, 0.f);
+    float a_next = 0.0f;
+    if (t_ok && p.LK > 0) fetch(0, uv_next, a_next);
     for (int jc = 0; jc < p.LK; jc += G) {
+        const float2 uv = uv_next;
+        float a = a_next;
+        if (t_ok && jc + G < p.LK) fetch(jc + G, uv_next, a_next);
         // phase 1: this lane's point -> corner offsets in LDS; keep the rest
         const int j = jc + r;
         const bool mine = t_ok && j < p.LK;
         size_t pt = 0;
-        float a = 0.0f, Hf = 0.0f, Wf = 0.0f;
+        float Hf = 0.0f, Wf = 0.0f;
         Geometry geo;
         if (mine) {
             const int l = (unsigned)j / (unsigned)p.K;
             const int4 lv = levels[l];
             pt = (size_t)t * p.LK + j;
-            const float2 uv = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
-            a = p.attn[pt];
             Hf = (float)lv.x;
             Wf = (float)lv.y;
             geo = point_geometry(uv.x, uv.y, lv, base, row_bytes);
