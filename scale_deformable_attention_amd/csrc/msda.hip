@@ -119,7 +119,7 @@ struct Params {
     int Qc;                   // queries per bin block
     int t_stride;             // row stride of the per-block tile table
     uint32_t slab_per_block;  // point-index capacity of one bin block's slab
-    uint2* table;             // [B*M*nW][t_stride] (count, offset)
+    uint2* table;             // [B*M][t_stride][nW] (count, offset)
     float4* slab;             // [B*M*nW][slab_per_block] (tuple bits, x, y, A) entries
     uint32_t* counters;       // [8] tile work counters, one per XCD group
 };
@@ -489,6 +489,7 @@ constexpr int kTileH = 4;           // pixel rows per tile
 constexpr int kBinRange = 1024;     // tile counters a bin block keeps in LDS at once
 constexpr int kBinUnroll = 8;       // points per thread in flight in the bin kernel
 constexpr int kChunk = 2048;        // entries a tile block sorts in LDS at once
+constexpr int kMinQueries = 64;     // queries per bin block at least (when there are enough)
 constexpr int kMaxSlabs = 64;       // bin blocks per (b, m) at most (a power of two)
 constexpr int kUnroll = 8;          // entries in flight per lane group in the sweep
 constexpr int kRecUnroll = 4;       // entries per thread in flight when building records
@@ -672,7 +673,8 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
     const int b = bm / p.M, m = bm - b * p.M;
     const int q_begin = min(w * p.Qc, p.Nq), q_end = min(q_begin + p.Qc, p.Nq);
     const int npts = (q_end - q_begin) * p.LK;
-    uint2* row = p.table + (size_t)blockIdx.x * p.t_stride;
+    // this block's column of the (tile, bin block) table of its (b, m)
+    uint2* row = p.table + (size_t)bm * p.t_stride * p.nW + w;
     float4* slab = p.slab + (size_t)blockIdx.x * p.slab_per_block;
     if (blockIdx.x == 0 && tid < 8) p.counters[tid] = 0;   // for the tile kernel that follows
     uint32_t base = 0;
@@ -707,7 +709,7 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
         }
         __syncthreads();
         const uint32_t total = block_exclusive_scan(cnt, off, rn, scratch);
-        for (int i = tid; i < rn; i += kBlock) row[r0 + i] = make_uint2(cnt[i], base + off[i]);
+        for (int i = tid; i < rn; i += kBlock) row[(size_t)(r0 + i) * p.nW] = make_uint2(cnt[i], base + off[i]);
         __syncthreads();
         for (int i = tid; i < rn; i += kBlock) cnt[i] = 0;
         __syncthreads();
@@ -805,7 +807,7 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
 
         // this tile's entries in every slab of (b, m)
         for (int w = tid; w < p.nW; w += kBlock) {
-            const uint2 e = p.table[((size_t)bm * p.nW + w) * p.t_stride + tl];
+            const uint2 e = p.table[((size_t)bm * p.t_stride + tl) * p.nW + w];
             wcnt[w] = e.x;
             woff[w] = e.y;
         }
@@ -981,10 +983,13 @@ BwdPlan plan_backward(const msda_dims_t* d) {
     BwdPlan pl;
     const int64_t BM = d->B * d->M;
     if (BM == 0) return pl;
-    // about 4096 bin blocks in total, at most kMaxSlabs per (b, m)
+    // about 4096 bin blocks in total, at most kMaxSlabs per (b, m) and at
+    // least kMinQueries queries per block (fewer, fuller slabs when there are
+    // few queries: every tile reads one table entry per slab)
     int64_t nW = (4096 + BM - 1) / BM;
     nW = nW < 1 ? 1 : (nW > kMaxSlabs ? kMaxSlabs : nW);
-    if (d->Nq > 0 && nW > d->Nq) nW = d->Nq;
+    const int64_t nW_q = (d->Nq + kMinQueries - 1) / kMinQueries;
+    if (nW > nW_q) nW = nW_q < 1 ? 1 : nW_q;
     const int64_t Qc = d->Nq > 0 ? (d->Nq + nW - 1) / nW : 0;
     pl.nW = Qc > 0 ? (d->Nq + Qc - 1) / Qc : 1;
     pl.Qc = Qc;
