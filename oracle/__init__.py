@@ -116,3 +116,78 @@ def backward(value, spatial_shapes, level_start_index, sampling_locations, atten
     if with_abs:
         return gv, gl, ga, gva, gla, gaa
     return gv, gl, ga
+
+
+def _bind_fused(lib):
+    if getattr(lib, "_fused_bound", False):
+        return lib
+    lib.msda_oracle_forward_fused.restype = ctypes.c_int
+    lib.msda_oracle_forward_fused.argtypes = [_i64] * 7 + [_pd, _pi, _pi, _pf, _pf, _pf, _pd, _pd]
+    lib.msda_oracle_backward_fused.restype = ctypes.c_int
+    lib.msda_oracle_backward_fused.argtypes = [_i64] * 7 + [_pd, _pi, _pi, _pf, _pf, _pf, _pd] + \
+        [_pd] * 8
+    lib._fused_bound = True
+    return lib
+
+
+def _prep_fused(value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
+                attention_logits):
+    value = np.ascontiguousarray(value, dtype=np.float64)
+    shapes = np.ascontiguousarray(spatial_shapes, dtype=np.int64).reshape(-1, 2)
+    lsi = np.ascontiguousarray(level_start_index, dtype=np.int64).reshape(-1)
+    ref = np.ascontiguousarray(reference_points, dtype=np.float32)
+    off = np.ascontiguousarray(sampling_offsets, dtype=np.float32)
+    B, Nv, M, D = value.shape
+    if off.ndim != 6 or off.shape[0] != B or off.shape[2] != M or off.shape[5] != 2:
+        raise ValueError("offsets must be [B,Nq,M,L,K,2]")
+    _, Nq, _, L, K, _ = off.shape
+    logits = np.ascontiguousarray(attention_logits, dtype=np.float32).reshape(B, Nq, M, L * K)
+    if ref.shape != (B, Nq, L, 2):
+        raise ValueError("reference points must be [B,Nq,L,2]")
+    if shapes.shape[0] != L or lsi.shape[0] != L:
+        raise ValueError("spatial_shapes / level_start_index do not have L rows")
+    return (B, Nv, M, D, L, Nq, K), value, shapes, lsi, ref, off, logits
+
+
+def forward_fused(value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
+                  attention_logits, with_abs=False, lib=None):
+    """Fused front-end + core forward in double: locations from reference
+    points [B,Nq,L,2] and offsets [B,Nq,M,L,K,2] (level pixels), weights as the
+    softmax of logits [B,Nq,M,L*K]. Returns out [B,Nq,M,D] (and the absolute
+    term sums when ``with_abs``)."""
+    dims, value, shapes, lsi, ref, off, logits = _prep_fused(
+        value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
+        attention_logits)
+    B, Nv, M, D, L, Nq, K = dims
+    out = np.empty((B, Nq, M, D), np.float64)
+    out_abs = np.empty_like(out) if with_abs else None
+    rc = _bind_fused(lib or library()).msda_oracle_forward_fused(
+        *dims, _ptr(value, ctypes.c_double), _ptr(shapes, ctypes.c_int64),
+        _ptr(lsi, ctypes.c_int64), _ptr(ref, ctypes.c_float), _ptr(off, ctypes.c_float),
+        _ptr(logits, ctypes.c_float), _ptr(out, ctypes.c_double), _ptr(out_abs, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return (out, out_abs) if with_abs else out
+
+
+def backward_fused(value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
+                   attention_logits, grad_output, with_abs=False, lib=None):
+    """Fused backward in double. Returns (grad_value, grad_reference_points,
+    grad_offsets, grad_logits), followed by their absolute term sums when
+    ``with_abs``."""
+    dims, value, shapes, lsi, ref, off, logits = _prep_fused(
+        value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
+        attention_logits)
+    B, Nv, M, D, L, Nq, K = dims
+    g = np.ascontiguousarray(grad_output, dtype=np.float64).reshape(B, Nq, M, D)
+    outs = [np.empty((B, Nv, M, D)), np.empty((B, Nq, L, 2)), np.empty((B, Nq, M, L, K, 2)),
+            np.empty((B, Nq, M, L * K))]
+    abss = [np.empty_like(o) for o in outs] if with_abs else [None] * 4
+    rc = _bind_fused(lib or library()).msda_oracle_backward_fused(
+        *dims, _ptr(value, ctypes.c_double), _ptr(shapes, ctypes.c_int64),
+        _ptr(lsi, ctypes.c_int64), _ptr(ref, ctypes.c_float), _ptr(off, ctypes.c_float),
+        _ptr(logits, ctypes.c_float), _ptr(g, ctypes.c_double),
+        *[_ptr(o, ctypes.c_double) for o in outs], *[_ptr(a, ctypes.c_double) for a in abss])
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return tuple(outs) + (tuple(abss) if with_abs else ())

@@ -66,6 +66,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORACLE_OK 0
@@ -242,5 +243,155 @@ int msda_oracle_backward(int64_t B, int64_t Nv, int64_t M, int64_t D, int64_t L,
     return ORACLE_OK;
 }
 
+/*
+ * Fused front-end: the two model steps the pages put right before the core
+ * (DETR-to-Deformable-DETR article, cf-1.com section 3.2):
+ *
+ *   loc[b,q,m,l,k] = ref[b,q,l] + off[b,q,m,l,k] / (W_l, H_l)
+ *       offsets in level-l pixels, the normalizer stacked as (W, H);
+ *   A[b,q,m,:]     = softmax of logits[b,q,m,:] over the L*K samples of one
+ *       (query, head) (cf-1.com 3.2; CSDN MSDA explainer section 3, note 3).
+ *
+ * Reference points come per level, [B, Nq, L, 2] (x, y) normalized; a caller
+ * with one point per query repeats it over the levels (the encoder's own
+ * position on every level, discosf.com section 2.2).
+ *
+ * The location decides the cell, so it is formed in single precision, as the
+ * GPU forms it: the quotient off / W rounded to float, then the sum rounded to
+ * float. The softmax and everything after are double.
+ *
+ * Backward: with gLoc and gA the core's location and weight gradients,
+ *   grad_off[...,0] = gLoc[...,0] / W_l,  grad_off[...,1] = gLoc[...,1] / H_l
+ *   grad_ref[b,q,l] = sum over heads m and points k of gLoc[b,q,m,l,k]
+ *   grad_logits[b,q,m,j] = A_j * (gA_j - sum_i A_i gA_i)   (softmax Jacobian)
+ */
+static float fused_coord(float ref, float off, int64_t size) {
+    const float quotient = off / (float)size;
+    return ref + quotient;
+}
+
+/* Locations and softmax weights of every point; NULL when out of memory. */
+static int fused_front(int64_t B, int64_t M, int64_t L, int64_t Nq, int64_t K,
+                       const int64_t *shapes, const float *ref, const float *off,
+                       const float *logits, float **loc_out, double **attn_out) {
+    const int64_t LK = L * K, T = B * Nq * M;
+    float *loc = (float *)malloc((size_t)(T * LK * 2 + 1) * sizeof(float));
+    double *attn = (double *)malloc((size_t)(T * LK + 1) * sizeof(double));
+    if (!loc || !attn) {
+        free(loc);
+        free(attn);
+        return ORACLE_BAD_ARGS;
+    }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t q = 0; q < Nq; ++q)
+            for (int64_t m = 0; m < M; ++m) {
+                const int64_t t = (b * Nq + q) * M + m;
+                for (int64_t l = 0; l < L; ++l) {
+                    const int64_t H = shapes[2 * l], W = shapes[2 * l + 1];
+                    const float *r = ref + ((b * Nq + q) * L + l) * 2;
+                    for (int64_t k = 0; k < K; ++k) {
+                        const int64_t p = t * LK + l * K + k;
+                        loc[2 * p] = fused_coord(r[0], off[2 * p], W);
+                        loc[2 * p + 1] = fused_coord(r[1], off[2 * p + 1], H);
+                    }
+                }
+                const float *z = logits + t * LK;
+                double zmax = -INFINITY, sum = 0.0;
+                for (int64_t j = 0; j < LK; ++j) zmax = (double)z[j] > zmax ? (double)z[j] : zmax;
+                for (int64_t j = 0; j < LK; ++j) sum += exp((double)z[j] - zmax);
+                for (int64_t j = 0; j < LK; ++j) attn[t * LK + j] = exp((double)z[j] - zmax) / sum;
+            }
+    *loc_out = loc;
+    *attn_out = attn;
+    return ORACLE_OK;
+}
+
+int msda_oracle_forward_fused(int64_t B, int64_t Nv, int64_t M, int64_t D, int64_t L,
+                              int64_t Nq, int64_t K, const double *value, const int64_t *shapes,
+                              const int64_t *lsi, const float *ref, const float *off,
+                              const float *logits, double *out, double *out_abs) {
+    if (check_args(B, Nv, M, D, L, Nq, K, shapes, lsi) != ORACLE_OK) return ORACLE_BAD_ARGS;
+    float *loc;
+    double *attn;
+    if (fused_front(B, M, L, Nq, K, shapes, ref, off, logits, &loc, &attn) != ORACLE_OK)
+        return ORACLE_BAD_ARGS;
+    const int rc = msda_oracle_forward(B, Nv, M, D, L, Nq, K, value, shapes, lsi, loc, attn, out,
+                                       out_abs);
+    free(loc);
+    free(attn);
+    return rc;
+}
+
+/* Any gradient pointer may be NULL; each abs pointer may be NULL. */
+int msda_oracle_backward_fused(int64_t B, int64_t Nv, int64_t M, int64_t D, int64_t L,
+                               int64_t Nq, int64_t K, const double *value, const int64_t *shapes,
+                               const int64_t *lsi, const float *ref, const float *off,
+                               const float *logits, const double *grad_out, double *grad_value,
+                               double *grad_ref, double *grad_off, double *grad_logits,
+                               double *grad_value_abs, double *grad_ref_abs,
+                               double *grad_off_abs, double *grad_logits_abs) {
+    if (check_args(B, Nv, M, D, L, Nq, K, shapes, lsi) != ORACLE_OK) return ORACLE_BAD_ARGS;
+    const int64_t LK = L * K, T = B * Nq * M, P = T * LK;
+    float *loc;
+    double *attn;
+    if (fused_front(B, M, L, Nq, K, shapes, ref, off, logits, &loc, &attn) != ORACLE_OK)
+        return ORACLE_BAD_ARGS;
+    double *gloc = (double *)malloc((size_t)(2 * P + 1) * sizeof(double));
+    double *gloc_abs = (double *)malloc((size_t)(2 * P + 1) * sizeof(double));
+    double *ga = (double *)malloc((size_t)(P + 1) * sizeof(double));
+    double *ga_abs = (double *)malloc((size_t)(P + 1) * sizeof(double));
+    int rc = (gloc && gloc_abs && ga && ga_abs) ? ORACLE_OK : ORACLE_BAD_ARGS;
+    if (rc == ORACLE_OK)
+        rc = msda_oracle_backward(B, Nv, M, D, L, Nq, K, value, shapes, lsi, loc, attn, grad_out,
+                                  grad_value, gloc, ga, grad_value_abs, gloc_abs, ga_abs);
+    if (rc == ORACLE_OK) {
+        if (grad_ref) memset(grad_ref, 0, (size_t)(B * Nq * L * 2) * sizeof(double));
+        if (grad_ref_abs) memset(grad_ref_abs, 0, (size_t)(B * Nq * L * 2) * sizeof(double));
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t q = 0; q < Nq; ++q)
+                for (int64_t m = 0; m < M; ++m) {
+                    const int64_t t = (b * Nq + q) * M + m;
+                    double s = 0.0, s_abs = 0.0;   /* sum_i A_i gA_i */
+                    for (int64_t j = 0; j < LK; ++j) {
+                        s += attn[t * LK + j] * ga[t * LK + j];
+                        s_abs += attn[t * LK + j] * ga_abs[t * LK + j];
+                    }
+                    for (int64_t l = 0; l < L; ++l) {
+                        const int64_t H = shapes[2 * l], W = shapes[2 * l + 1];
+                        const int64_t r = ((b * Nq + q) * L + l) * 2;
+                        for (int64_t k = 0; k < K; ++k) {
+                            const int64_t p = t * LK + l * K + k;
+                            if (grad_off) {
+                                grad_off[2 * p] = gloc[2 * p] / (double)W;
+                                grad_off[2 * p + 1] = gloc[2 * p + 1] / (double)H;
+                            }
+                            if (grad_off_abs) {
+                                grad_off_abs[2 * p] = gloc_abs[2 * p] / (double)W;
+                                grad_off_abs[2 * p + 1] = gloc_abs[2 * p + 1] / (double)H;
+                            }
+                            if (grad_ref) {
+                                grad_ref[r] += gloc[2 * p];
+                                grad_ref[r + 1] += gloc[2 * p + 1];
+                            }
+                            if (grad_ref_abs) {
+                                grad_ref_abs[r] += gloc_abs[2 * p];
+                                grad_ref_abs[r + 1] += gloc_abs[2 * p + 1];
+                            }
+                            const double a = attn[p];
+                            if (grad_logits) grad_logits[p] = a * (ga[p] - s);
+                            if (grad_logits_abs) grad_logits_abs[p] = a * (ga_abs[p] + s_abs);
+                        }
+                    }
+                }
+    }
+    free(loc);
+    free(attn);
+    free(gloc);
+    free(gloc_abs);
+    free(ga);
+    free(ga_abs);
+    return rc;
+}
+
 /* Version tag so a test can tell a stale build from the current source. */
-int msda_oracle_version(void) { return 1; }
+int msda_oracle_version(void) { return 2; }

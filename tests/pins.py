@@ -439,7 +439,162 @@ def pin_permutation(lib=None):
     assert np.array_equal(fwd(lib, value[pb], shapes, lsi, loc[pb], attn[pb]), o[pb])
 
 
+# ----------------------------------------------------------------------------- fused front-end
+# Pinned conventions (cf-1.com section 3.2): location = reference point +
+# offset / (W_l, H_l) with offsets in level pixels and the normalizer stacked
+# (W, H); weights = softmax of the logits over the L*K samples of one (query,
+# head) (also CSDN explainer section 3 note 3).
+
+def random_fused_case(rng, B=2, M=3, D=4, shapes=((4, 6), (3, 5), (2, 2)), Nq=5, K=2):
+    shapes, lsi = level_tables(shapes)
+    L = shapes.shape[0]
+    Nv = int((shapes[:, 0] * shapes[:, 1]).sum())
+    value = rng.standard_normal((B, Nv, M, D))
+    ref = rng.uniform(0.0, 1.0, size=(B, Nq, L, 2)).astype(np.float32)
+    off = (rng.standard_normal((B, Nq, M, L, K, 2)) * 1.5).astype(np.float32)
+    logits = (rng.standard_normal((B, Nq, M, L * K)) * 2.0).astype(np.float32)
+    g = rng.standard_normal((B, Nq, M, D))
+    return value, shapes, lsi, ref, off, logits, g
+
+
+def _fused_torch_reference(value, shapes, lsi, ref, off, logits, g):
+    """The fused front-end and the core as torch float64 autograd: torch's
+    softmax for the weights, per-level grid_sample (bilinear, zeros padding,
+    align_corners=False) for the samples. The normalized location carries the
+    single-precision value the core samples at (the quotient and the sum
+    rounded to float) while its gradient flows through the exact float64
+    expression."""
+    import torch
+    import torch.nn.functional as F
+    B, Nv, M, D = value.shape
+    _, Nq, _, L, K, _ = off.shape
+    V = torch.tensor(value, dtype=torch.float64, requires_grad=True)
+    R = torch.tensor(ref.astype(np.float64), requires_grad=True)
+    O = torch.tensor(off.astype(np.float64), requires_grad=True)
+    Z = torch.tensor(logits.astype(np.float64), requires_grad=True)
+    A = torch.softmax(Z, dim=-1).reshape(B, Nq, M, L, K)
+    out = torch.zeros(B, Nq, M, D, dtype=torch.float64)
+    for l in range(L):
+        H, W = int(shapes[l][0]), int(shapes[l][1])
+        norm = torch.tensor([W, H], dtype=torch.float64)
+        u = R[:, :, None, l, None, :] + O[:, :, :, l] / norm          # [B, Nq, M, K, 2]
+        q32 = (off[:, :, :, l] / np.array([W, H], np.float32)).astype(np.float32)
+        u32 = (ref[:, :, None, l, None, :] + q32).astype(np.float32)
+        x32 = np.stack([coord32(u32[..., 0], W), coord32(u32[..., 1], H)], -1)
+        u_at = torch.tensor((x32.astype(np.float64) + 0.5) / np.array([W, H], np.float64))
+        u_used = u + (u_at - u).detach()
+        v_l = V[:, lsi[l]:lsi[l] + H * W].permute(0, 2, 3, 1).reshape(B * M, D, H, W)
+        grid = (2.0 * u_used - 1.0).permute(0, 2, 1, 3, 4).reshape(B * M, Nq, K, 2)
+        s = F.grid_sample(v_l, grid, mode="bilinear", padding_mode="zeros",
+                          align_corners=False)                            # [B*M, D, Nq, K]
+        s = s.reshape(B, M, D, Nq, K).permute(0, 3, 1, 4, 2)              # [B, Nq, M, K, D]
+        out = out + (A[:, :, :, l, :, None] * s).sum(3)
+    (out * torch.tensor(g, dtype=torch.float64)).sum().backward()
+    return (out.detach().numpy(), V.grad.numpy(), R.grad.numpy(), O.grad.numpy(),
+            Z.grad.numpy())
+
+
+def pin_fused_torch(lib=None):
+    """Fused forward and all four gradients equal torch's softmax + per-level
+    grid_sample with autograd (library routines, independent code)."""
+    for seed in (31, 32):
+        rng = np.random.default_rng(seed)
+        value, shapes, lsi, ref, off, logits, g = random_fused_case(rng)
+        ro, rgv, rgr, rgo, rgz = _fused_torch_reference(value, shapes, lsi, ref, off, logits, g)
+        o = oracle.forward_fused(value, shapes, lsi, ref, off, logits, lib=lib)
+        gv, gr, go, gz = oracle.backward_fused(value, shapes, lsi, ref, off, logits, g, lib=lib)
+        _close(o, ro, 1e-12, "fused forward vs torch")
+        _close(gv, rgv, 1e-12, "fused value gradient vs torch")
+        _close(gz, rgz, 1e-12, "logit gradient vs torch")
+        _close(go, rgo, 1e-10, "offset gradient vs torch")
+        _close(gr, rgr, 1e-10, "reference-point gradient vs torch")
+
+
+def pin_fused_pixel_shift(lib=None):
+    """Closed form: reference points at pixel centres of power-of-two levels and
+    whole-pixel offsets (all exact in float) land on pixel centres; with one
+    logit far above the others the output is the value at the shifted pixel."""
+    shapes, lsi = level_tables([(4, 8), (2, 4)])
+    L, K, M, D, Nq = 2, 2, 2, 3, 4
+    rng = np.random.default_rng(33)
+    Nv = int((shapes[:, 0] * shapes[:, 1]).sum())
+    value = rng.standard_normal((1, Nv, M, D))
+    ref = np.zeros((1, Nq, L, 2), np.float32)
+    off = np.zeros((1, Nq, M, L, K, 2), np.float32)
+    logits = np.full((1, Nq, M, L * K), -200.0, np.float32)
+    want = np.zeros((1, Nq, M, D))
+    for q in range(Nq):
+        for l in range(L):
+            H, W = shapes[l]
+            i, j = rng.integers(0, W), rng.integers(0, H)
+            ref[0, q, l] = ((i + 0.5) / W, (j + 0.5) / H)
+        for m in range(M):
+            l, k = rng.integers(0, L), rng.integers(0, K)
+            H, W = shapes[l]
+            i = int(round(ref[0, q, l, 0] * W - 0.5))
+            j = int(round(ref[0, q, l, 1] * H - 0.5))
+            di, dj = rng.integers(-i, W - i), rng.integers(-j, H - j)
+            off[0, q, m, l, k] = (di, dj)
+            logits[0, q, m, l * K + k] = 0.0
+            want[0, q, m] = value[0, lsi[l] + (j + dj) * W + (i + di), m]
+    o = oracle.forward_fused(value, shapes, lsi, ref, off, logits, lib=lib)
+    _close(o, want, 1e-12, "fused pixel shift")
+
+
+def pin_fused_finite_differences(lib=None):
+    """Gradients of L = sum(g * out) with respect to logits, offsets and
+    reference points equal difference quotients of the fused oracle (smooth in
+    the logits; linear in the pixel coordinate inside a cell)."""
+    rng = np.random.default_rng(34)
+    value, shapes, lsi, ref, off, logits, g = random_fused_case(rng, B=1, M=2, D=3, Nq=2, K=2,
+                                                                shapes=((3, 4), (2, 3)))
+    loss = lambda r, o, z: float((oracle.forward_fused(value, shapes, lsi, r, o, z, lib=lib)  # noqa: E731
+                                  * g).sum())
+    _, gr, go, gz = oracle.backward_fused(value, shapes, lsi, ref, off, logits, g, lib=lib)
+    for idx in np.ndindex(*logits.shape):
+        zp, zm = logits.copy(), logits.copy()
+        h = 2.0 ** -8
+        zp[idx] += h
+        zm[idx] -= h
+        fd = (loss(ref, off, zp) - loss(ref, off, zm)) / (2 * h)
+        assert abs(fd - gz[idx]) <= 1e-4 * max(1.0, abs(fd)), f"d/dlogit{idx}: {fd} vs {gz[idx]}"
+    h = np.float32(2.0 ** -10)
+    checked = 0
+    for idx in np.ndindex(*off.shape):
+        l, axis = idx[3], idx[5]
+        n = shapes[l][1] if axis == 0 else shapes[l][0]
+        op, om = off.copy(), off.copy()
+        op[idx] = np.float32(off[idx] + h)
+        om[idx] = np.float32(off[idx] - h)
+        base = ref[idx[0], idx[1], l, axis]
+        xs = [coord32(np.float32(base + np.float32(o_ / np.float32(n))), n)
+              for o_ in (op[idx], om[idx], off[idx])]
+        if len({float(np.floor(x)) for x in xs}) != 1:
+            continue
+        fd = (loss(ref, op, logits) - loss(ref, om, logits)) / (float(xs[0]) - float(xs[1]))
+        assert abs(fd - go[idx]) <= 1e-6 * max(1.0, abs(fd)), f"d/doffset{idx}: {fd} vs {go[idx]}"
+        checked += 1
+    assert checked > off.size // 2, "too few offsets checked"
+    # a reference point moves every head's and point's location on its level
+    h = np.float32(2.0 ** -12)
+    checked = 0
+    for idx in np.ndindex(*ref.shape):
+        l, axis = idx[2], idx[3]
+        n = shapes[l][1] if axis == 0 else shapes[l][0]
+        rp, rm = ref.copy(), ref.copy()
+        rp[idx] = np.float32(ref[idx] + h)
+        rm[idx] = np.float32(ref[idx] - h)
+        q = (off[idx[0], idx[1], :, l, :, axis] / np.float32(n)).astype(np.float32)
+        cells = [np.floor(coord32((r_[idx] + q).astype(np.float32), n)) for r_ in (rp, rm, ref)]
+        if not (np.array_equal(cells[0], cells[2]) and np.array_equal(cells[1], cells[2])):
+            continue
+        fd = (loss(rp, off, logits) - loss(rm, off, logits)) / (float(rp[idx]) - float(rm[idx]))
+        assert abs(fd - gr[idx]) <= 1e-4 * max(1.0, abs(fd)), f"d/dref{idx}: {fd} vs {gr[idx]}"
+        checked += 1
+    assert checked > 0, "no reference point checked"
+
+
 ALL_PINS = [pin_golden_hand_worked, pin_pixel_centres, pin_constant_field, pin_bilinear_field,
             pin_out_of_bounds, pin_linearity, pin_grid_sample, pin_brute_force,
             pin_finite_differences, pin_single_scale_resampling, pin_scatter_conservation,
-            pin_permutation]
+            pin_permutation, pin_fused_torch, pin_fused_pixel_shift, pin_fused_finite_differences]

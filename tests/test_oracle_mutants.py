@@ -36,6 +36,16 @@ MUTANTS = {
     "attn_grad_drops_g": ("ga += g[d] * s;", "ga += s;"),
     "value_grad_drops_A": ("const double t = a * c[i].w * g[d];", "const double t = c[i].w * g[d];"),
     "value_grad_wrong_corner_weight": ("const double t = a * c[i].w * g[d];", "const double t = a * c[3 - i].w * g[d];"),
+    # fused front-end
+    "fused_offset_x_over_H": ("loc[2 * p] = fused_coord(r[0], off[2 * p], W);",
+                              "loc[2 * p] = fused_coord(r[0], off[2 * p], H);"),
+    "fused_no_normalizer": ("const float quotient = off / (float)size;", "const float quotient = off + 0.0f * (float)size;"),
+    "fused_softmax_per_level": ("for (int64_t j = 0; j < LK; ++j) sum += exp((double)z[j] - zmax);",
+                                "for (int64_t j = 0; j < K; ++j) sum += exp((double)z[j] - zmax);"),
+    "fused_logit_grad_no_jacobian": ("if (grad_logits) grad_logits[p] = a * (ga[p] - s);",
+                                     "if (grad_logits) grad_logits[p] = a * ga[p];"),
+    "fused_ref_grad_one_head": ("grad_ref[r] += gloc[2 * p];", "grad_ref[r] += m == 0 ? gloc[2 * p] : 0.0;"),
+    "fused_offset_grad_times_W": ("grad_off[2 * p] = gloc[2 * p] / (double)W;", "grad_off[2 * p] = gloc[2 * p] * (double)W;"),
 }
 
 CHILD = r"""
