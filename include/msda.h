@@ -67,7 +67,7 @@ extern "C" {
 #endif
 
 #define MSDA_VERSION_MAJOR 0
-#define MSDA_VERSION_MINOR 2
+#define MSDA_VERSION_MINOR 3
 #define MSDA_VERSION_PATCH 0
 
 /* Largest number of feature levels the kernels accept. */
@@ -153,6 +153,63 @@ msda_status_t msda_backward(const msda_dims_t *dims, msda_dtype_t value_dtype,
  * backward's size checks would. No HIP call. */
 msda_status_t msda_backward_workspace_size(const msda_dims_t *dims, msda_dtype_t value_dtype,
                                            size_t *bytes);
+
+/*
+ * Fused front-end: the same core with its two preceding model steps done
+ * inside the kernels (DETR-to-Deformable-DETR article, cf-1.com section 3.2):
+ *   sampling location = reference point + offset / (W_l, H_l)
+ *       offsets in level-l pixels, the normalizer stacked as (W, H);
+ *   attention weights = softmax of the logits over the L*K samples of one
+ *       (query, head) (also the CSDN MSDA explainer, section 3, note 3).
+ * Neither the locations nor the weights are materialized in memory.
+ *
+ *   reference_points  [B, Nq, L, 2]        (x, y) normalized to [0, 1]; a
+ *                                          point shared by the levels is
+ *                                          repeated over L
+ *   sampling_offsets  [B, Nq, M, L, K, 2]  (x, y) in level-l pixels, fp32
+ *   attention_logits  [B, Nq, M, L*K]      fp32
+ *
+ * The location is formed in fp32 as ref + (off / W): the quotient and the sum
+ * each correctly rounded; the core then proceeds as msda_forward does. The
+ * softmax is fp32 (max-shifted exponentials).
+ *
+ * Alignment: value and output 16-byte; reference_points and
+ * sampling_offsets 8-byte; the rest 4-byte. Sizes and errors as msda_forward.
+ */
+msda_status_t msda_forward_fused(const msda_dims_t *dims, msda_dtype_t value_dtype,
+                                 const void *value, const int64_t *spatial_shapes,
+                                 const int64_t *level_start_index, const float *reference_points,
+                                 const float *sampling_offsets, const float *attention_logits,
+                                 float *output, hipStream_t stream);
+
+/*
+ * Backward of msda_forward_fused for grad_output. With gLoc and gA the core's
+ * location and weight gradients (see msda_backward):
+ *   grad_sampling_offsets[...,0]  = gLoc[...,0] / W_l   (= A * sum_d g ds/dx)
+ *   grad_sampling_offsets[...,1]  = gLoc[...,1] / H_l
+ *   grad_reference_points[b,q,l]  = sum over heads m and points k of gLoc
+ *   grad_attention_logits[b,q,m,j] = A_j * (gA_j - sum_i A_i gA_i)
+ *   grad_value                    as msda_backward
+ * Any gradient pointer may be NULL to skip it.
+ *
+ * workspace: at least msda_backward_fused_workspace_size() bytes, 256-byte
+ * aligned, owned by the caller, clobbered; needed whenever a gradient is
+ * requested and there is work (B*Nq*M > 0, or grad_value with B > 0).
+ * Alignment: value, grad_output and grad_value 16-byte; reference points,
+ * offsets and their gradients 8-byte; others 4-byte.
+ */
+msda_status_t msda_backward_fused(const msda_dims_t *dims, msda_dtype_t value_dtype,
+                                  const void *value, const int64_t *spatial_shapes,
+                                  const int64_t *level_start_index, const float *reference_points,
+                                  const float *sampling_offsets, const float *attention_logits,
+                                  const float *grad_output, float *grad_value,
+                                  float *grad_reference_points, float *grad_sampling_offsets,
+                                  float *grad_attention_logits, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace msda_backward_fused needs for these sizes. No HIP call. */
+msda_status_t msda_backward_fused_workspace_size(const msda_dims_t *dims,
+                                                 msda_dtype_t value_dtype, size_t *bytes);
 
 /* Host-side check of a HOST copy of the level tables against Nv: every
  * H_l, W_l >= 1, level_start_index the prefix sums, sum H_l*W_l == Nv.

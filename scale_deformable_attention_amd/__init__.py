@@ -5,10 +5,13 @@ package is its Python binding. Importing the package does not load the
 library; the first call does, and raises if it has not been built.
 """
 from ._binding import (MSDA_DTYPE_BF16, MSDA_DTYPE_F32, MsdaError, MSDeformAttnFunction,
-                       library, ms_deform_attn, msda_backward, msda_backward_workspace_size,
-                       msda_check_tables, msda_forward,
-                       msda_version)
+                       MSDeformAttnFusedFunction, library, ms_deform_attn, ms_deform_attn_fused,
+                       msda_backward, msda_backward_fused, msda_backward_fused_workspace_size,
+                       msda_backward_workspace_size, msda_check_tables, msda_forward,
+                       msda_forward_fused, msda_version)
 
-__all__ = ["msda_forward", "msda_backward", "msda_backward_workspace_size", "msda_check_tables", "msda_version", "library",
-           "ms_deform_attn", "MSDeformAttnFunction", "MsdaError", "MSDA_DTYPE_F32",
-           "MSDA_DTYPE_BF16"]
+__all__ = ["msda_forward", "msda_backward", "msda_backward_workspace_size",
+           "msda_forward_fused", "msda_backward_fused", "msda_backward_fused_workspace_size",
+           "msda_check_tables", "msda_version", "library", "ms_deform_attn",
+           "MSDeformAttnFunction", "ms_deform_attn_fused", "MSDeformAttnFusedFunction",
+           "MsdaError", "MSDA_DTYPE_F32", "MSDA_DTYPE_BF16"]

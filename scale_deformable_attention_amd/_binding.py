@@ -57,6 +57,16 @@ def library():
         lib.msda_status_string.argtypes = [ctypes.c_int]
         lib.msda_version.restype = ctypes.c_int
         lib.msda_version.argtypes = []
+        lib.msda_forward_fused.restype = ctypes.c_int
+        lib.msda_forward_fused.argtypes = [ctypes.POINTER(MsdaDims), ctypes.c_int, vp, i64p, i64p,
+                                           fp, fp, fp, fp, vp]
+        lib.msda_backward_fused.restype = ctypes.c_int
+        lib.msda_backward_fused.argtypes = [ctypes.POINTER(MsdaDims), ctypes.c_int, vp, i64p,
+                                            i64p, fp, fp, fp, fp, fp, fp, fp, fp, vp,
+                                            ctypes.c_size_t, vp]
+        lib.msda_backward_fused_workspace_size.restype = ctypes.c_int
+        lib.msda_backward_fused_workspace_size.argtypes = [ctypes.POINTER(MsdaDims), ctypes.c_int,
+                                                           ctypes.POINTER(ctypes.c_size_t)]
         _LIB = lib
     return _LIB
 
@@ -247,3 +257,145 @@ def ms_deform_attn(value, spatial_shapes, level_start_index, sampling_locations,
     """Differentiable core: output [B, Nq, M*D]."""
     return MSDeformAttnFunction.apply(value, spatial_shapes, level_start_index,
                                       sampling_locations, attention_weights)
+
+
+# ----------------------------------------------------------------------------- fused front-end
+def _common_fused(value, spatial_shapes, level_start_index, reference_points, sampling_offsets,
+                  attention_logits):
+    dev = value.device
+    if dev.type != "cuda":
+        raise ValueError("value must be a GPU tensor")
+    _check(value, "value", (torch.float32, torch.bfloat16), dev)
+    _check(spatial_shapes, "spatial_shapes", (torch.int64,), dev)
+    _check(level_start_index, "level_start_index", (torch.int64,), dev)
+    _check(reference_points, "reference_points", (torch.float32,), dev)
+    _check(sampling_offsets, "sampling_offsets", (torch.float32,), dev)
+    _check(attention_logits, "attention_logits", (torch.float32,), dev)
+    if value.dim() != 4:
+        raise ValueError("value must be [B, Nv, M, D]")
+    if sampling_offsets.dim() != 6 or sampling_offsets.shape[-1] != 2:
+        raise ValueError("sampling_offsets must be [B, Nq, M, L, K, 2]")
+    B, Nv, M, D = value.shape
+    Bq, Nq, Mq, L, K, _ = sampling_offsets.shape
+    if (Bq, Mq) != (B, M):
+        raise ValueError("sampling_offsets batch/head sizes differ from value's")
+    if tuple(reference_points.shape) != (B, Nq, L, 2):
+        raise ValueError("reference_points must be [B, Nq, L, 2]")
+    if tuple(attention_logits.shape) not in ((B, Nq, M, L * K), (B, Nq, M, L, K)):
+        raise ValueError("attention_logits must be [B, Nq, M, L*K]")
+    if tuple(spatial_shapes.shape) != (L, 2) or tuple(level_start_index.shape) != (L,):
+        raise ValueError("spatial_shapes must be [L, 2] and level_start_index [L]")
+    return dev, MsdaDims(B, Nv, M, D, L, Nq, K)
+
+
+def msda_forward_fused(value, spatial_shapes, level_start_index, reference_points,
+                       sampling_offsets, attention_logits, output=None, stream=None):
+    """Fused forward (include/msda.h msda_forward_fused): locations from the
+    reference points [B,Nq,L,2] and offsets [B,Nq,M,L,K,2] (level pixels),
+    weights as the softmax of the logits [B,Nq,M,L*K], both formed in the
+    kernel. Returns output [B, Nq, M*D] (fp32)."""
+    dev, dims = _common_fused(value, spatial_shapes, level_start_index, reference_points,
+                              sampling_offsets, attention_logits)
+    if output is None:
+        output = torch.empty((dims.B, dims.Nq, dims.M * dims.D), dtype=torch.float32, device=dev)
+    else:
+        _check(output, "output", (torch.float32,), dev)
+        if output.numel() != dims.B * dims.Nq * dims.M * dims.D:
+            raise ValueError("output has the wrong number of elements")
+    st = library().msda_forward_fused(ctypes.byref(dims), _value_dtype(value), _ptr(value),
+                                      _ptr(spatial_shapes), _ptr(level_start_index),
+                                      _ptr(reference_points), _ptr(sampling_offsets),
+                                      _ptr(attention_logits), _ptr(output), _stream(dev, stream))
+    if st != 0:
+        raise MsdaError(st, "msda_forward_fused")
+    return output
+
+
+def msda_backward_fused_workspace_size(value, sampling_offsets):
+    """Workspace bytes msda_backward_fused needs for these tensors' sizes."""
+    B, Nv, M, D = value.shape
+    _, Nq, _, L, K, _ = sampling_offsets.shape
+    dims = MsdaDims(B, Nv, M, D, L, Nq, K)
+    n = ctypes.c_size_t(0)
+    st = library().msda_backward_fused_workspace_size(ctypes.byref(dims), _value_dtype(value),
+                                                      ctypes.byref(n))
+    if st != 0:
+        raise MsdaError(st, "msda_backward_fused_workspace_size")
+    return n.value
+
+
+def msda_backward_fused(value, spatial_shapes, level_start_index, reference_points,
+                        sampling_offsets, attention_logits, grad_output, grad_value=None,
+                        grad_reference_points=None, grad_sampling_offsets=None,
+                        grad_attention_logits=None, needs=(True, True, True, True),
+                        workspace=None, stream=None):
+    """Fused backward (include/msda.h msda_backward_fused). Returns
+    (grad_value, grad_reference_points, grad_sampling_offsets,
+    grad_attention_logits), fp32, None where ``needs`` is False; given output
+    tensors are written in place."""
+    dev, dims = _common_fused(value, spatial_shapes, level_start_index, reference_points,
+                              sampling_offsets, attention_logits)
+    _check(grad_output, "grad_output", (torch.float32,), dev)
+    if grad_output.numel() != dims.B * dims.Nq * dims.M * dims.D:
+        raise ValueError("grad_output has the wrong number of elements")
+    outs = []
+    for need, given, shape, name in (
+            (needs[0], grad_value, (dims.B, dims.Nv, dims.M, dims.D), "grad_value"),
+            (needs[1], grad_reference_points, tuple(reference_points.shape),
+             "grad_reference_points"),
+            (needs[2], grad_sampling_offsets, tuple(sampling_offsets.shape),
+             "grad_sampling_offsets"),
+            (needs[3], grad_attention_logits, tuple(attention_logits.shape),
+             "grad_attention_logits")):
+        if not need:
+            outs.append(None)
+        elif given is None:
+            outs.append(torch.empty(shape, dtype=torch.float32, device=dev))
+        else:
+            _check(given, name, (torch.float32,), dev)
+            if tuple(given.shape) != shape:
+                raise ValueError(f"{name} must have shape {shape}")
+            outs.append(given)
+    n = msda_backward_fused_workspace_size(value, sampling_offsets)
+    if workspace is None:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.numel() * workspace.element_size() < n:
+        raise ValueError(f"workspace must be a {n}-byte tensor on {dev}")
+    st = library().msda_backward_fused(
+        ctypes.byref(dims), _value_dtype(value), _ptr(value), _ptr(spatial_shapes),
+        _ptr(level_start_index), _ptr(reference_points), _ptr(sampling_offsets),
+        _ptr(attention_logits), _ptr(grad_output), *[_ptr(o) for o in outs], _ptr(workspace),
+        ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(dev, stream))
+    if st != 0:
+        raise MsdaError(st, "msda_backward_fused")
+    return tuple(outs)
+
+
+class MSDeformAttnFusedFunction(torch.autograd.Function):
+    """Autograd wrapper of the fused front-end + core, both passes in HIP."""
+
+    @staticmethod
+    def forward(ctx, value, spatial_shapes, level_start_index, reference_points,
+                sampling_offsets, attention_logits):
+        ctx.save_for_backward(value, spatial_shapes, level_start_index, reference_points,
+                              sampling_offsets, attention_logits)
+        return msda_forward_fused(value, spatial_shapes, level_start_index, reference_points,
+                                  sampling_offsets, attention_logits)
+
+    @staticmethod
+    def backward(ctx, grad_output):
+        value, shapes, lsi, ref, off, logits = ctx.saved_tensors
+        needs = (ctx.needs_input_grad[0], ctx.needs_input_grad[3], ctx.needs_input_grad[4],
+                 ctx.needs_input_grad[5])
+        gv, gr, go, gz = msda_backward_fused(value, shapes, lsi, ref, off, logits,
+                                             grad_output.contiguous(), needs=needs)
+        if gv is not None and value.dtype != torch.float32:
+            gv = gv.to(value.dtype)
+        return gv, None, None, gr, go, gz
+
+
+def ms_deform_attn_fused(value, spatial_shapes, level_start_index, reference_points,
+                         sampling_offsets, attention_logits):
+    """Differentiable fused front-end + core: output [B, Nq, M*D]."""
+    return MSDeformAttnFusedFunction.apply(value, spatial_shapes, level_start_index,
+                                           reference_points, sampling_offsets, attention_logits)

@@ -122,7 +122,32 @@ struct Params {
     uint2* table;             // [B*M][t_stride][nW] (count, offset)
     float4* slab;             // [B*M*nW][slab_per_block] (tuple bits, x, y, A) entries
     uint32_t* counters;       // [8] tile work counters, one per XCD group
+    // fused front-end: locations and weights formed from the model's raw
+    // outputs inside the kernels
+    const float* ref;         // [B, Nq, L, 2] reference points (x, y), normalized
+    const float* off;         // [B, Nq, M, L, K, 2] offsets (x, y) in level pixels
+    const float* logits;      // [B, Nq, M, L*K]
+    float2* smax;             // [T] max and 1/sum of each tuple's exp(logit - max)
+    float* grad_off;          // [B, Nq, M, L, K, 2]
+    float* grad_logits;       // [B, Nq, M, L*K]
 };
+
+// Fused front-end of point j (level l) of tuple t: the location is the
+// reference point plus the offset over the level's size (W for x, H for y),
+// the quotient and the sum each rounded to float; the weight is
+// exp(z - max) / sum over the tuple's L*K logits.
+__device__ inline void fused_point(const Params& p, int t, int j, int l, int4 lv, float zmax,
+                                   float inv_sum, float2& uv, float& a) {
+    const size_t pt = (size_t)t * p.LK + j;
+    const size_t bq = (size_t)(t / p.M);
+    const float2 r = *reinterpret_cast<const float2*>(p.ref + 2 * (bq * p.L + l));
+    const float2 o = *reinterpret_cast<const float2*>(p.off + 2 * pt);
+    const float qx = o.x / (float)lv.y;
+    const float qy = o.y / (float)lv.x;
+    uv.x = r.x + qx;
+    uv.y = r.y + qy;
+    a = expf(p.logits[pt] - zmax) * inv_sum;
+}
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -239,13 +264,14 @@ struct alignas(16) FwdRecord {
     float w[4];   // A * bilinear weight, 0 for corners outside
 };
 
-template <typename T, int D>
+template <typename T, int D, bool kFused>
 __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
     using S = Shape<T, D>;
     constexpr int G = S::G, TPW = S::TPW, PL = S::kPerLane;
     constexpr int kRowBytesPerHead = D * Elem<T>::kBytes;
     __shared__ int4 levels[MSDA_MAX_LEVELS];
     __shared__ FwdRecord records[kWavesPerBlock][kWave];
+    __shared__ float stat[kFused ? kWavesPerBlock : 1][kWave];
     load_levels(p, levels);
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -270,13 +296,43 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
 #pragma unroll
     for (int e = 0; e < PL; ++e) acc[e] = 0.0f;
 
+    // fused: the softmax statistics of tuple t1. Its G builder lanes (lane
+    // t1 % TPW + i * TPW) each scan every G-th logit and combine through LDS.
+    float zmax = 0.0f, inv_sum = 0.0f;
+    if constexpr (kFused) {
+        const float* z = p.logits + (size_t)t1 * p.LK;
+        float mx = -INFINITY;
+        if (t1_ok)
+            for (int j = jrow; j < p.LK; j += G) mx = fmaxf(mx, z[j]);
+        stat[wave][lane] = mx;
+        wave_sync();
+        mx = -INFINITY;
+        for (int i = 0; i < G; ++i) mx = fmaxf(mx, stat[wave][i * TPW + lane % TPW]);
+        wave_sync();
+        float se = 0.0f;
+        if (t1_ok)
+            for (int j = jrow; j < p.LK; j += G) se += expf(z[j] - mx);
+        stat[wave][lane] = se;
+        wave_sync();
+        se = 0.0f;
+        for (int i = 0; i < G; ++i) se += stat[wave][i * TPW + lane % TPW];
+        wave_sync();
+        zmax = mx;
+        inv_sum = 1.0f / se;
+    }
+
     // this lane's point of the next chunk: its location and weight are loaded
     // one chunk ahead, while the current chunk's rows are gathered
     auto fetch = [&](int jc, float2& uv, float& a) {
-        const int j = jc + jrow;
-        const size_t pt = (size_t)t1 * p.LK + min(j, p.LK - 1);
-        uv = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
-        a = p.attn[pt];
+        const int j = min(jc + jrow, p.LK - 1);
+        if constexpr (kFused) {
+            const int l = (unsigned)j / (unsigned)p.K;
+            fused_point(p, t1, j, l, levels[l], zmax, inv_sum, uv, a);
+        } else {
+            const size_t pt = (size_t)t1 * p.LK + j;
+            uv = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
+            a = p.attn[pt];
+        }
     };
     float2 uv_next = make_float2(0.f, 0.f);
     float a_next = 0.0f;
@@ -355,7 +411,7 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
 //     sums live in registers. Every grad_value element is then written exactly
 //     once with a plain store (zeros where nothing lands), so no fill pass.
 
-template <typename T, int D>
+template <typename T, int D, bool kFused>
 __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
     using S = Shape<T, D>;
     constexpr int G = S::G, TPW = S::TPW, PL = S::kPerLane;
@@ -398,12 +454,29 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
         for (int e = 0; e < PL; ++e) go[e] = 0.0f;
     }
 
+    // fused: the tuple's softmax statistics (computed beforehand)
+    float zmax = 0.0f, inv_sum = 0.0f;
+    if constexpr (kFused) {
+        if (t_ok) {
+            const float2 st = p.smax[t];
+            zmax = st.x;
+            inv_sum = st.y;
+        }
+    }
+    float s_ag = 0.0f;   // fused: this lane's part of sum_j A_j gA_j over the tuple
+
     // this lane's point of the next chunk: its location and weight are loaded
     // one chunk ahead, while the current chunk's rows are gathered
     auto fetch = [&](int jc, float2& uv, float& a) {
-        const size_t pt = (size_t)t * p.LK + min(jc + r, p.LK - 1);
-        uv = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
-        a = p.attn[pt];
+        const int j = min(jc + r, p.LK - 1);
+        if constexpr (kFused) {
+            const int l = (unsigned)j / (unsigned)p.K;
+            fused_point(p, t, j, l, levels[l], zmax, inv_sum, uv, a);
+        } else {
+            const size_t pt = (size_t)t * p.LK + j;
+            uv = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
+            a = p.attn[pt];
+        }
     };
     float2 uv_next = make_float2(0.f, 0.f);
     float a_next = 0.0f;
@@ -477,9 +550,30 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
                     gy = fmaf(dwdy[c], mine_dot[c], gy);
                 }
             }
-            if (p.grad_attn) p.grad_attn[pt] = ga;
-            if (p.grad_loc)
-                *reinterpret_cast<float2*>(p.grad_loc + 2 * pt) = make_float2(a * Wf * gx, a * Hf * gy);
+            if constexpr (kFused) {
+                // offsets: d loc / d off = 1 / (W, H) cancels the pixel scale;
+                // the logits' gradient is finished below, once the tuple's
+                // sum is known (gA parked in the output meanwhile)
+                if (p.grad_off)
+                    *reinterpret_cast<float2*>(p.grad_off + 2 * pt) = make_float2(a * gx, a * gy);
+                if (p.grad_logits) p.grad_logits[pt] = ga;
+                s_ag = fmaf(a, ga, s_ag);
+            } else {
+                if (p.grad_attn) p.grad_attn[pt] = ga;
+                if (p.grad_loc)
+                    *reinterpret_cast<float2*>(p.grad_loc + 2 * pt) = make_float2(a * Wf * gx, a * Hf * gy);
+            }
+        }
+    }
+    if constexpr (kFused) {
+        // softmax Jacobian: dL/dz_j = A_j (gA_j - sum_i A_i gA_i)
+        const float s_all = group_sum<G>(s_ag);
+        if (p.grad_logits && t_ok) {
+            for (int j = r; j < p.LK; j += G) {
+                const size_t pt = (size_t)t * p.LK + j;
+                const float a = expf(p.logits[pt] - zmax) * inv_sum;
+                p.grad_logits[pt] = a * (p.grad_logits[pt] - s_all);
+            }
         }
     }
 }
@@ -656,7 +750,7 @@ struct PointWalk {
     }
 };
 
-template <int D>
+template <int D, bool kFused>
 __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
     using TS = TileShape<D>;
     __shared__ LevelTiles lt[MSDA_MAX_LEVELS];
@@ -677,6 +771,21 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
     uint2* row = p.table + (size_t)bm * p.t_stride * p.nW + w;
     float4* slab = p.slab + (size_t)blockIdx.x * p.slab_per_block;
     if (blockIdx.x == 0 && tid < 8) p.counters[tid] = 0;   // for the tile kernel that follows
+    // location (and weight) of the walk's current point, or of its first point
+    // for lanes past the end, so that every load is unconditional
+    auto point_of = [&](const PointWalk& it, bool ok, float2& uv, float& a, bool want_a) {
+        if constexpr (kFused) {
+            const int t = ok ? (int)it.t : (int)it.tuple0;
+            const int j = ok ? it.j : 0;
+            const int l = ok ? it.l : 0;
+            const float2 st = want_a ? p.smax[t] : make_float2(0.f, 0.f);
+            fused_point(p, t, j, l, make_int4(lt[l].H, lt[l].W, lt[l].start, 0), st.x, st.y, uv, a);
+        } else {
+            const size_t pt = ok ? it.pt : it.pt0;
+            uv = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
+            a = want_a ? p.attn[pt] : 0.0f;
+        }
+    };
     uint32_t base = 0;
     // a point index that is always valid (npts > 0 whenever a loop body runs)
     // stands in for the lanes past the end, so that every load is unconditional
@@ -692,7 +801,8 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
             for (int u = 0; u < kBinUnroll; ++u) {
                 ok[u] = it.i < npts;
                 lvl[u] = it.l;
-                uv[u] = *reinterpret_cast<const float2*>(p.loc + 2 * (ok[u] ? it.pt : it.pt0));
+                float a_unused;
+                point_of(it, ok[u], uv[u], a_unused, false);
                 it.next();
             }
 #pragma unroll
@@ -724,9 +834,7 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
                 ok[u] = it.i < npts;
                 lvl[u] = it.l;
                 tup[u] = (uint32_t)it.t;
-                const size_t pt = ok[u] ? it.pt : it.pt0;
-                uv[u] = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
-                a[u] = p.attn[pt];
+                point_of(it, ok[u], uv[u], a[u], true);
                 it.next();
             }
 #pragma unroll
@@ -930,6 +1038,42 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
     }
 }
 
+// ------------------------------------------------------------------ fused front-end
+// Softmax statistics of every tuple's L*K logits: (max, 1 / sum exp(z - max)),
+// one thread per tuple.
+__global__ __launch_bounds__(kBlock) void msda_softmax_stats_kernel(Params p) {
+    const int t = blockIdx.x * kBlock + threadIdx.x;
+    if (t >= p.T) return;
+    const float* z = p.logits + (size_t)t * p.LK;
+    float mx = -INFINITY;
+    for (int j = 0; j < p.LK; ++j) mx = fmaxf(mx, z[j]);
+    float se = 0.0f;
+    for (int j = 0; j < p.LK; ++j) se += expf(z[j] - mx);
+    p.smax[t] = make_float2(mx, 1.0f / se);
+}
+
+// Gradient of a reference point: every head's and point's location on its
+// level moves with it, so dL/dref[b,q,l] = sum over m, k of dL/dloc, where
+// dL/dloc = dL/doff * (W, H). One thread per (b, q, l).
+__global__ __launch_bounds__(kBlock) void msda_ref_grad_kernel(Params p, float* grad_ref) {
+    const size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;   // (b*Nq + q)*L + l
+    if (i >= (size_t)p.B * p.Nq * p.L) return;
+    const size_t bq = i / p.L;
+    const int l = (int)(i - bq * p.L);
+    const float Hf = (float)p.shapes[2 * l], Wf = (float)p.shapes[2 * l + 1];
+    float gx = 0.0f, gy = 0.0f;
+    for (int m = 0; m < p.M; ++m) {
+        const float2* g = reinterpret_cast<const float2*>(p.grad_off) +
+                          ((bq * p.M + m) * p.L + l) * p.K;
+        for (int k = 0; k < p.K; ++k) {
+            const float2 v = g[k];
+            gx += v.x;
+            gy += v.y;
+        }
+    }
+    reinterpret_cast<float2*>(grad_ref)[i] = make_float2(gx * Wf, gy * Hf);
+}
+
 // ------------------------------------------------------------------ host side
 constexpr int64_t k2GiB = int64_t(1) << 31;
 constexpr size_t kWorkspaceAlign = 256;
@@ -1063,15 +1207,21 @@ struct Kernels {
     const void* point = nullptr;
     const void* bin = nullptr;
     const void* tile = nullptr;
+    const void* fwd_fused = nullptr;
+    const void* point_fused = nullptr;
+    const void* bin_fused = nullptr;
     int tuples_per_block = 0;
 };
 
 template <typename T, int D>
 Kernels kernels_for() {
     Kernels k;
-    k.fwd = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D>);
-    k.point = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D>);
-    k.bin = reinterpret_cast<const void*>(&msda_bin_kernel<D>);
+    k.fwd = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D, false>);
+    k.point = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D, false>);
+    k.bin = reinterpret_cast<const void*>(&msda_bin_kernel<D, false>);
+    k.fwd_fused = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D, true>);
+    k.point_fused = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D, true>);
+    k.bin_fused = reinterpret_cast<const void*>(&msda_bin_kernel<D, true>);
     k.tile = reinterpret_cast<const void*>(&msda_tile_kernel<D>);
     k.tuples_per_block = Shape<T, D>::TPW * kWavesPerBlock;
     return k;
@@ -1087,6 +1237,53 @@ Kernels pick(msda_dtype_t dt, int64_t D) {
     }
 #undef MSDA_PICK
     return Kernels();
+}
+
+// grad_value: the bin kernel, then the tile kernel, on the workspace of `pl`.
+msda_status_t launch_grad_value(Params& p, const BwdPlan& pl, const msda_dims_t* dims,
+                                const void* bin, const void* tile, void* workspace,
+                                hipStream_t stream) {
+    p.nW = (int)pl.nW;
+    p.Qc = (int)pl.Qc;
+    p.t_stride = (int)pl.t_stride;
+    p.slab_per_block = (uint32_t)pl.slab_per_block;
+    p.table = reinterpret_cast<uint2*>(static_cast<char*>(workspace) + pl.table_off);
+    p.slab = reinterpret_cast<float4*>(static_cast<char*>(workspace) + pl.slab_off);
+    p.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + pl.counters_off);
+    const int64_t BM = dims->B * dims->M;
+    msda_status_t s = launch(bin, BM * pl.nW, p, stream);
+    if (s != MSDA_SUCCESS) return s;
+    // persistent: blocks fetch (b, m, tile) work items, as many blocks as fit
+    // on the GPU at once; the grid is a multiple of 8 for the XCD-affine
+    // schedule
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return MSDA_ERROR_LAUNCH;
+    const int per_cu = tile_blocks_per_cu(dims->D, tile);
+    const int64_t items = BM * pl.t_stride;
+    const int64_t resident = ((int64_t)per_cu * (cus > 0 ? cus : 1) + 7) / 8 * 8;
+    const int64_t grid = items < resident ? ((items + 7) / 8) * 8 : resident;
+    return launch(tile, grid, p, stream);
+}
+
+// Workspace of the fused backward: the core's (grad_value path), then the
+// tuples' softmax statistics, then room for the offsets' gradient when the
+// caller asks for the reference points' gradient only.
+struct FusedPlan {
+    BwdPlan core;
+    size_t smax_off = 0, goff_off = 0, bytes = 0;
+};
+
+FusedPlan plan_backward_fused(const msda_dims_t* d) {
+    FusedPlan f;
+    f.core = plan_backward(d);
+    const Sizes n = sizes_of(d);
+    const int64_t T = d->B * d->Nq * d->M;
+    f.smax_off = round_up(f.core.bytes, kWorkspaceAlign);
+    f.goff_off = f.smax_off + round_up((size_t)T * sizeof(float2), kWorkspaceAlign);
+    f.bytes = f.goff_off + round_up((size_t)n.points * 2 * sizeof(float), kWorkspaceAlign);
+    return f;
 }
 
 }  // namespace
@@ -1156,32 +1353,114 @@ msda_status_t msda_backward(const msda_dims_t* dims, msda_dtype_t value_dtype, c
     const Kernels k = pick(value_dtype, dims->D);
     if (!k.point) return MSDA_ERROR_NOT_SUPPORTED;
     if (grad_value && n.value) {
-        p.nW = (int)pl.nW;
-        p.Qc = (int)pl.Qc;
-        p.t_stride = (int)pl.t_stride;
-        p.slab_per_block = (uint32_t)pl.slab_per_block;
-        p.table = reinterpret_cast<uint2*>(static_cast<char*>(workspace) + pl.table_off);
-        p.slab = reinterpret_cast<float4*>(static_cast<char*>(workspace) + pl.slab_off);
-        p.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + pl.counters_off);
-        const int64_t BM = dims->B * dims->M;
-        msda_status_t s = launch(k.bin, BM * pl.nW, p, stream);
-        if (s != MSDA_SUCCESS) return s;
-        // persistent: blocks fetch (b, m, tile) work items, as many blocks as
-        // fit on the GPU at once; the grid is a multiple of 8 for the
-        // XCD-affine schedule
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return MSDA_ERROR_LAUNCH;
-        const int per_cu = tile_blocks_per_cu(dims->D, k.tile);
-        const int64_t items = BM * pl.t_stride;
-        const int64_t resident = ((int64_t)per_cu * (cus > 0 ? cus : 1) + 7) / 8 * 8;
-        const int64_t grid = items < resident ? ((items + 7) / 8) * 8 : resident;
-        s = launch(k.tile, grid, p, stream);
+        const msda_status_t s = launch_grad_value(p, pl, dims, k.bin, k.tile, workspace, stream);
         if (s != MSDA_SUCCESS) return s;
     }
     if (p.T == 0 || (!grad_sampling_locations && !grad_attention_weights)) return MSDA_SUCCESS;
     return launch(k.point, ((int64_t)p.T + k.tuples_per_block - 1) / k.tuples_per_block, p, stream);
+}
+
+msda_status_t msda_forward_fused(const msda_dims_t* dims, msda_dtype_t value_dtype,
+                                 const void* value, const int64_t* spatial_shapes,
+                                 const int64_t* level_start_index, const float* reference_points,
+                                 const float* sampling_offsets, const float* attention_logits,
+                                 float* output, hipStream_t stream) {
+    const msda_status_t st = check_dims(dims, value_dtype, false);
+    if (st != MSDA_SUCCESS) return st;
+    const Sizes n = sizes_of(dims);
+    const int64_t n_ref = dims->B * dims->Nq * dims->L * 2;
+    if ((n.value && !value) || !spatial_shapes || !level_start_index ||
+        (n.points && (!sampling_offsets || !attention_logits)) || (n_ref && !reference_points) ||
+        (n.out && !output))
+        return MSDA_ERROR_INVALID_VALUE;
+    if (!aligned(value, 16) || !aligned(output, 16) || !aligned(sampling_offsets, 8) ||
+        !aligned(reference_points, 8) || !aligned(attention_logits, 4) ||
+        !aligned(spatial_shapes, 8) || !aligned(level_start_index, 8))
+        return MSDA_ERROR_INVALID_VALUE;
+    Params p = make_params(dims, value_dtype, value, spatial_shapes, level_start_index, nullptr,
+                           nullptr);
+    p.ref = reference_points;
+    p.off = sampling_offsets;
+    p.logits = attention_logits;
+    p.out = output;
+    if (p.T == 0) return MSDA_SUCCESS;
+    const Kernels k = pick(value_dtype, dims->D);
+    if (!k.fwd_fused) return MSDA_ERROR_NOT_SUPPORTED;
+    return launch(k.fwd_fused, ((int64_t)p.T + k.tuples_per_block - 1) / k.tuples_per_block, p,
+                  stream);
+}
+
+msda_status_t msda_backward_fused_workspace_size(const msda_dims_t* dims,
+                                                 msda_dtype_t value_dtype, size_t* bytes) {
+    if (!bytes) return MSDA_ERROR_INVALID_VALUE;
+    const msda_status_t st = check_dims(dims, value_dtype, true);
+    if (st != MSDA_SUCCESS) return st;
+    *bytes = plan_backward_fused(dims).bytes;
+    return MSDA_SUCCESS;
+}
+
+msda_status_t msda_backward_fused(const msda_dims_t* dims, msda_dtype_t value_dtype,
+                                  const void* value, const int64_t* spatial_shapes,
+                                  const int64_t* level_start_index, const float* reference_points,
+                                  const float* sampling_offsets, const float* attention_logits,
+                                  const float* grad_output, float* grad_value,
+                                  float* grad_reference_points, float* grad_sampling_offsets,
+                                  float* grad_attention_logits, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    const msda_status_t st = check_dims(dims, value_dtype, true);
+    if (st != MSDA_SUCCESS) return st;
+    const Sizes n = sizes_of(dims);
+    const int64_t n_ref = dims->B * dims->Nq * dims->L * 2;
+    if ((n.value && !value) || !spatial_shapes || !level_start_index ||
+        (n.points && (!sampling_offsets || !attention_logits)) || (n_ref && !reference_points) ||
+        (n.out && !grad_output))
+        return MSDA_ERROR_INVALID_VALUE;
+    if (!aligned(value, 16) || !aligned(grad_output, 16) || !aligned(grad_value, 16) ||
+        !aligned(sampling_offsets, 8) || !aligned(grad_sampling_offsets, 8) ||
+        !aligned(reference_points, 8) || !aligned(grad_reference_points, 8) ||
+        !aligned(attention_logits, 4) || !aligned(grad_attention_logits, 4) ||
+        !aligned(spatial_shapes, 8) || !aligned(level_start_index, 8) ||
+        !aligned(workspace, kWorkspaceAlign))
+        return MSDA_ERROR_INVALID_VALUE;
+    Params p = make_params(dims, value_dtype, value, spatial_shapes, level_start_index, nullptr,
+                           nullptr);
+    const bool want_value = grad_value && n.value;
+    const bool want_point =
+        p.T > 0 && (grad_reference_points || grad_sampling_offsets || grad_attention_logits);
+    if (!want_value && !want_point) return MSDA_SUCCESS;
+    const FusedPlan pl = plan_backward_fused(dims);
+    if (!workspace || workspace_bytes < pl.bytes) return MSDA_ERROR_INVALID_VALUE;
+    p.ref = reference_points;
+    p.off = sampling_offsets;
+    p.logits = attention_logits;
+    p.grad_out = grad_output;
+    p.grad_value = grad_value;
+    p.smax = reinterpret_cast<float2*>(static_cast<char*>(workspace) + pl.smax_off);
+    const Kernels k = pick(value_dtype, dims->D);
+    if (!k.point_fused) return MSDA_ERROR_NOT_SUPPORTED;
+    msda_status_t s = launch(reinterpret_cast<const void*>(&msda_softmax_stats_kernel),
+                             ((int64_t)p.T + kBlock - 1) / kBlock, p, stream);   // none if T = 0
+    if (s != MSDA_SUCCESS) return s;
+    if (want_value) {
+        s = launch_grad_value(p, pl.core, dims, k.bin_fused, k.tile, workspace, stream);
+        if (s != MSDA_SUCCESS) return s;
+    }
+    if (!want_point) return MSDA_SUCCESS;
+    p.grad_off = grad_sampling_offsets
+                     ? grad_sampling_offsets
+                     : (grad_reference_points
+                            ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.goff_off)
+                            : nullptr);
+    p.grad_logits = grad_attention_logits;
+    s = launch(k.point_fused, ((int64_t)p.T + k.tuples_per_block - 1) / k.tuples_per_block, p,
+               stream);
+    if (s != MSDA_SUCCESS || !grad_reference_points) return s;
+    const int64_t nref = dims->B * dims->Nq * dims->L;
+    void* args[] = {&p, &grad_reference_points};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&msda_ref_grad_kernel),
+                                         dim3((unsigned)((nref + kBlock - 1) / kBlock)), dim3(kBlock),
+                                         args, 0, stream);
+    return e == hipSuccess ? MSDA_SUCCESS : MSDA_ERROR_LAUNCH;
 }
 
 msda_status_t msda_check_tables(const int64_t* host_spatial_shapes,

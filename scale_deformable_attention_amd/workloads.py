@@ -149,6 +149,11 @@ def generate(w: Workload, batch_slice=None):
       attention_weights  [B,Nq,M,L,K] float32
       grad_output      [B,Nq,M*D] float32
       reference_points [Nq,2] float64 (x, y) normalized
+    and the raw draws, as the fused front-end takes them:
+      reference_points_levels [B,Nq,L,2] float32 (the query's point, the same
+                       on every level)
+      sampling_offsets   [B,Nq,M,L,K,2] float32, level pixels
+      attention_logits   [B,Nq,M,L*K] float32
     ``batch_slice`` (a slice over B) keeps only those batch entries; the draws
     are made for the full batch first so a slice is a true sub-sample.
     """
@@ -172,6 +177,10 @@ def generate(w: Workload, batch_slice=None):
         "attention_weights": attn.astype(np.float32),
         "grad_output": grad_output,
         "reference_points": ref,
+        "reference_points_levels": np.ascontiguousarray(np.broadcast_to(
+            ref.astype(np.float32)[None, :, None, :], (B, Nq, L, 2))),
+        "sampling_offsets": offsets.astype(np.float32),
+        "attention_logits": logits.astype(np.float32),
     }
     if w.value_dtype == "bf16":
         bits = bf16_round(value)
@@ -182,7 +191,8 @@ def generate(w: Workload, batch_slice=None):
         out["value"] = value
     if batch_slice is not None:
         for key in ("value", "value_bf16", "value_f32_orig", "sampling_locations",
-                    "attention_weights", "grad_output"):
+                    "attention_weights", "grad_output", "reference_points_levels",
+                    "sampling_offsets", "attention_logits"):
             if key in out:
                 out[key] = np.ascontiguousarray(out[key][batch_slice])
     return out

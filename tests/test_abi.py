@@ -22,8 +22,10 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["msda_backward", "msda_backward_workspace_size",
-                                    "msda_check_tables", "msda_forward", "msda_status_string",
+    assert declared_functions() == ["msda_backward", "msda_backward_fused",
+                                    "msda_backward_fused_workspace_size",
+                                    "msda_backward_workspace_size", "msda_check_tables",
+                                    "msda_forward", "msda_forward_fused", "msda_status_string",
                                     "msda_version"]
 
 
@@ -35,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = msda.library()
-    assert lib.msda_version() == 200
+    assert lib.msda_version() == 300
     for s in range(4):
         assert len(lib.msda_status_string(s)) > 0
     assert lib.msda_status_string(99) == b"unknown status"
@@ -62,6 +64,27 @@ def bwd_status(dims, dtype=0, ws_bytes=1 << 40, **ptrs):
         ctypes.c_size_t(ws_bytes), None)
 
 
+def fused_fwd_status(dims, dtype=0, **ptrs):
+    p = dict(value=FAKE, shapes=FAKE, lsi=FAKE, ref=FAKE, off=FAKE, logits=FAKE, out=FAKE)
+    p.update(ptrs)
+    return msda.library().msda_forward_fused(
+        None if dims is None else ctypes.byref(dims), dtype, p["value"], p["shapes"], p["lsi"],
+        p["ref"], p["off"], p["logits"], p["out"], None)
+
+
+def fused_bwd_status(dims, dtype=0, ws_bytes=1 << 40, **ptrs):
+    p = dict(value=FAKE, shapes=FAKE, lsi=FAKE, ref=FAKE, off=FAKE, logits=FAKE, gout=FAKE,
+             gv=FAKE, gref=FAKE, goff=FAKE, glog=FAKE, ws=FAKE)
+    p.update(ptrs)
+    return msda.library().msda_backward_fused(
+        None if dims is None else ctypes.byref(dims), dtype, p["value"], p["shapes"], p["lsi"],
+        p["ref"], p["off"], p["logits"], p["gout"], p["gv"], p["gref"], p["goff"], p["glog"],
+        p["ws"], ctypes.c_size_t(ws_bytes), None)
+
+
+ALL_STATUS_FNS = [fwd_status, bwd_status, fused_fwd_status, fused_bwd_status]
+
+
 def dims(**kw):
     d = dict(B=1, Nv=80, M=2, D=8, L=2, Nq=16, K=2)
     d.update(kw)
@@ -71,7 +94,7 @@ def dims(**kw):
 INVALID, UNSUPPORTED = 1, 2
 
 
-@pytest.mark.parametrize("status_fn", [fwd_status, bwd_status])
+@pytest.mark.parametrize("status_fn", ALL_STATUS_FNS)
 def test_invalid_sizes(status_fn):
     assert status_fn(None) == INVALID
     for bad in (dict(B=-1), dict(Nq=-3), dict(K=-1), dict(M=0), dict(Nv=0), dict(L=0),
@@ -80,7 +103,7 @@ def test_invalid_sizes(status_fn):
     assert status_fn(dims(), dtype=7) == INVALID
 
 
-@pytest.mark.parametrize("status_fn", [fwd_status, bwd_status])
+@pytest.mark.parametrize("status_fn", ALL_STATUS_FNS)
 def test_unsupported_sizes(status_fn):
     for d in (4, 12, 24, 128):
         assert status_fn(dims(D=d)) == UNSUPPORTED, d
@@ -102,6 +125,20 @@ def test_null_and_misaligned_pointers():
     for key in ("value", "gout", "gv", "loc", "gl"):
         assert bwd_status(dims(), **{key: odd}) == INVALID, key
     assert fwd_status(dims(), attn=ctypes.c_void_p(0x10002)) == INVALID
+
+
+def test_fused_null_and_misaligned_pointers():
+    for key in ("value", "shapes", "lsi", "ref", "off", "logits", "out"):
+        assert fused_fwd_status(dims(), **{key: None}) == INVALID, key
+    for key in ("value", "shapes", "lsi", "ref", "off", "logits", "gout"):
+        assert fused_bwd_status(dims(), **{key: None}) == INVALID, key
+    odd = ctypes.c_void_p(0x10004)
+    for key in ("value", "out", "ref", "off", "shapes", "lsi"):
+        assert fused_fwd_status(dims(), **{key: odd}) == INVALID, key
+    for key in ("value", "gout", "gv", "ref", "off", "gref", "goff"):
+        assert fused_bwd_status(dims(), **{key: odd}) == INVALID, key
+    assert fused_fwd_status(dims(), logits=ctypes.c_void_p(0x10002)) == INVALID
+    assert fused_bwd_status(dims(), glog=ctypes.c_void_p(0x10002)) == INVALID
 
 
 def workspace_size(d, dtype=0):
@@ -127,6 +164,22 @@ def test_workspace_size_and_checks():
     assert bwd_status(dims(D=12), gv=None, ws=None, ws_bytes=0) == UNSUPPORTED
 
 
+def test_fused_workspace_size_and_checks():
+    n = ctypes.c_size_t(0)
+    lib = msda.library()
+    assert lib.msda_backward_fused_workspace_size(ctypes.byref(dims()), 0, ctypes.byref(n)) == 0
+    core = workspace_size(dims())[1]
+    # the fused plan adds the softmax statistics and an offset-gradient buffer
+    assert n.value > core and n.value % 256 == 0
+    assert lib.msda_backward_fused_workspace_size(ctypes.byref(dims(D=12)), 0,
+                                                  ctypes.byref(n)) == UNSUPPORTED
+    assert lib.msda_backward_fused_workspace_size(ctypes.byref(dims()), 0, None) == INVALID
+    lib.msda_backward_fused_workspace_size(ctypes.byref(dims()), 0, ctypes.byref(n))
+    assert fused_bwd_status(dims(), ws_bytes=n.value - 1) == INVALID
+    assert fused_bwd_status(dims(), ws=None) == INVALID
+    assert fused_bwd_status(dims(), ws=ctypes.c_void_p(0x10010)) == INVALID
+
+
 def test_check_tables():
     assert msda.msda_check_tables([[8, 8], [4, 4]], [0, 64], 80) == 0
     assert msda.msda_check_tables([[8, 8], [4, 4]], [0, 63], 80) == INVALID
@@ -141,3 +194,7 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         msda.msda_forward(v, torch.zeros(2, 2, dtype=torch.int64), torch.zeros(2, dtype=torch.int64),
                           torch.zeros(1, 16, 2, 2, 2, 2), torch.zeros(1, 16, 2, 2, 2))
+    with pytest.raises(ValueError):
+        msda.msda_forward_fused(v, torch.zeros(2, 2, dtype=torch.int64),
+                                torch.zeros(2, dtype=torch.int64), torch.zeros(1, 16, 2, 2),
+                                torch.zeros(1, 16, 2, 2, 2, 2), torch.zeros(1, 16, 2, 4))
