@@ -12,7 +12,13 @@ B*Nq*M*L*K per step), the roofline of the dominant kernel measured live with HIP
 events on the launch stream, and
 the CPU oracle's rate on the host (a bounded sample of the same workload).
 
+With --frontend fused the step is msda_forward_fused + msda_backward_fused on
+the same workload: the kernels take the raw reference points, pixel offsets
+and attention logits and form the locations and softmax weights themselves,
+and the backward returns the offset, reference-point and logit gradients.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--workload NAME] [--frontend core|fused]
        python bench.py --calibrate-copy MIB   (a plain copy-like kernel of known size,
                                                run under the counter profiler to scale
                                                its byte counters)
@@ -33,26 +39,36 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 METRIC = "sampled points/sec (B·Nq·M·L·K) fwd+bwd; achieved HBM GB/s vs peak"
 
 
-def algorithmic_bytes(w, value_bytes_per_elem=4):
+def algorithmic_bytes(w, value_bytes_per_elem=4, fused=False):
     """Compulsory bytes of each launch (each input read once, each output
     written once). Per sampled point: location 8 B + weight 4 B (+ their
-    gradients 8 B + 4 B in the backward). Per (b,q,m): D*4 B of output (or
+    gradients 8 B + 4 B in the backward); fused: offset 8 B + logit 4 B (+
+    their gradients), the same count. Per (b,q,m): D*4 B of output (or
     upstream gradient). Per value element: read once (+ grad_value written
-    once in the backward)."""
+    once in the backward). Fused also reads a reference point of 8 B per
+    (b,q,l) (and writes its gradient in the backward)."""
     P = w.points
     T = w.B * w.num_queries * w.M
     V = w.B * w.Nv * w.M * w.D
-    fwd = V * value_bytes_per_elem + P * 12 + T * w.D * 4
+    R = w.B * w.num_queries * w.L * 8 if fused else 0
+    fwd = V * value_bytes_per_elem + P * 12 + T * w.D * 4 + R
     # location/weight gradients: value, locations, weights, upstream gradient
     # in; their gradients (12 B per point) out
-    bwd_point = V * value_bytes_per_elem + P * 12 + T * w.D * 4 + P * 12
+    bwd_point = V * value_bytes_per_elem + P * 12 + T * w.D * 4 + P * 12 + 2 * R
     # grad_value: locations, weights, upstream gradient in; grad_value out
-    bwd_value = P * 12 + T * w.D * 4 + V * 4
+    bwd_value = P * 12 + T * w.D * 4 + V * 4 + R
     # the whole backward reads each input once and writes each gradient once
-    bwd = V * value_bytes_per_elem + P * 12 + T * w.D * 4 + V * 4 + P * 12
+    bwd = V * value_bytes_per_elem + P * 12 + T * w.D * 4 + V * 4 + P * 12 + 2 * R
     return {"forward": fwd, "bwd_point": bwd_point, "bwd_value": bwd_value, "backward": bwd,
             "step": fwd + bwd}
 
+
+KERNEL_NAMES = {
+    "core": ("msda_fwd_kernel", "msda_bwd_point_kernel", "msda_bin_kernel+msda_tile_kernel"),
+    "fused": ("msda_fwd_kernel<fused>",
+              "msda_softmax_stats_kernel+msda_bwd_point_kernel<fused>+msda_ref_grad_kernel",
+              "msda_softmax_stats_kernel+msda_bin_kernel<fused>+msda_tile_kernel"),
+}
 
 KERNEL_SOURCE = os.path.join(ROOT, "scale_deformable_attention_amd", "csrc", "msda.hip")
 
@@ -64,7 +80,8 @@ def source_digest():
 
 def read_traffic(workload):
     """Per-dispatch HBM-side byte counters of each kernel, from the committed
-    counter summary for this workload (profiles/msda_kernels_<workload>_traffic.txt).
+    counter summary for this workload (profiles/msda_kernels_<workload>_traffic.txt,
+    with <workload> followed by _fused for the fused front-end).
 
     The summary holds FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged over
     the dispatches of one run) for every kernel, the same two counters for the
@@ -108,19 +125,23 @@ def calibrate_copy(mib):
                       "launches": 5}), flush=True)
 
 
-def cpu_baseline(w, x, budget_s):
+def cpu_baseline(w, x, budget_s, fused=False):
     """The oracle as it stands (single thread) on a bounded sample: whole batch
     entries of the workload, forward + backward, until the budget is used."""
     import oracle
     done_points, t_total, batches = 0, 0.0, 0
     per_batch = w.points // w.B
+    fwd, bwd = (oracle.forward_fused, oracle.backward_fused) if fused else \
+        (oracle.forward, oracle.backward)
+    keys = ("reference_points_levels", "sampling_offsets", "attention_logits") if fused else \
+        ("sampling_locations", "attention_weights")
     for b in range(w.B):
         sl = slice(b, b + 1)
-        args = (x["value"][sl], x["spatial_shapes"], x["level_start_index"],
-                x["sampling_locations"][sl], x["attention_weights"][sl])
+        args = (x["value"][sl], x["spatial_shapes"], x["level_start_index"]) + \
+            tuple(x[k][sl] for k in keys)
         t0 = time.perf_counter()
-        oracle.forward(*args)
-        oracle.backward(*args, x["grad_output"][sl])
+        fwd(*args)
+        bwd(*args, x["grad_output"][sl])
         t_total += time.perf_counter() - t0
         done_points += per_batch
         batches += 1
@@ -138,6 +159,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="encoder_train")
+    ap.add_argument("--frontend", choices=("core", "fused"), default="core",
+                    help="core: locations and weights given; fused: formed in the kernels "
+                         "from reference points, offsets and logits")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline sample")
@@ -176,14 +200,35 @@ def main():
     ws = torch.empty(max(msda.msda_backward_workspace_size(value, loc), 1), dtype=torch.uint8,
                      device=dev)
     backward = w.backward
+    fused = args.frontend == "fused"
+    if fused:
+        ref = torch.from_numpy(x["reference_points_levels"]).to(dev)
+        off = torch.from_numpy(x["sampling_offsets"]).to(dev)
+        logits = torch.from_numpy(x["attention_logits"]).to(dev)
+        del loc, attn, gl, ga
+        gref = torch.empty_like(ref)
+        goff = torch.empty_like(off)
+        glog = torch.empty_like(logits)
+        ws = torch.empty(max(msda.msda_backward_fused_workspace_size(value, off), 1),
+                         dtype=torch.uint8, device=dev)
 
-    def fwd():
-        msda.msda_forward(value, shapes, lsi, loc, attn, output=out)
+        def fwd():
+            msda.msda_forward_fused(value, shapes, lsi, ref, off, logits, output=out)
 
-    def bwd(needs=(True, True, True)):
-        msda.msda_backward(value, shapes, lsi, loc, attn, gout, grad_value=gv,
-                           grad_sampling_locations=gl, grad_attention_weights=ga, needs=needs,
-                           workspace=ws)
+        def bwd(needs=(True, True, True)):
+            msda.msda_backward_fused(value, shapes, lsi, ref, off, logits, gout, grad_value=gv,
+                                     grad_reference_points=gref, grad_sampling_offsets=goff,
+                                     grad_attention_logits=glog,
+                                     needs=(needs[0], needs[1], needs[1], needs[2]),
+                                     workspace=ws)
+    else:
+        def fwd():
+            msda.msda_forward(value, shapes, lsi, loc, attn, output=out)
+
+        def bwd(needs=(True, True, True)):
+            msda.msda_backward(value, shapes, lsi, loc, attn, gout, grad_value=gv,
+                               grad_sampling_locations=gl, grad_attention_weights=ga,
+                               needs=needs, workspace=ws)
 
     def step():
         fwd()
@@ -223,24 +268,24 @@ def main():
     # each kernel on its own (same inputs, same stream): the forward kernel;
     # the backward with only the location/weight gradients (the point kernel);
     # the backward with only grad_value (bin + tile kernels)
-    kernels = {"msda_fwd_kernel": timed(fwd, args.steps)}
+    # (fused: the backward's softmax-statistics kernel runs in both halves, the
+    # reference-point reduction after the point kernel)
+    names = KERNEL_NAMES["fused" if fused else "core"]
+    kernels = {names[0]: timed(fwd, args.steps)}
     if backward:
-        kernels["msda_bwd_point_kernel"] = timed(lambda: bwd((False, True, True)), args.steps)
-        kernels["msda_bin_kernel+msda_tile_kernel"] = timed(lambda: bwd((True, False, False)),
-                                                            args.steps)
+        kernels[names[1]] = timed(lambda: bwd((False, True, True)), args.steps)
+        kernels[names[2]] = timed(lambda: bwd((True, False, False)), args.steps)
         step()   # leave a full set of gradients in place
         torch.cuda.synchronize()
 
     ms_per_step = total_ms / args.steps
     pts_per_s = w.points / (ms_per_step * 1e-3)
-    ab = algorithmic_bytes(w, 2 if w.value_dtype == "bf16" else 4)
-    kernel_bytes = {"msda_fwd_kernel": ab["forward"],
-                    "msda_bwd_point_kernel": ab["bwd_point"],
-                    "msda_bin_kernel+msda_tile_kernel": ab["bwd_value"]}
+    ab = algorithmic_bytes(w, 2 if w.value_dtype == "bf16" else 4, fused)
+    kernel_bytes = dict(zip(names, (ab["forward"], ab["bwd_point"], ab["bwd_value"])))
     dom_name = max(kernels, key=kernels.get)
     dom_ms, dom_bytes = kernels[dom_name], kernel_bytes[dom_name]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    measured = read_traffic(w.name)
+    measured = read_traffic(w.name + ("_fused" if fused else ""))
     traffic = None
     if measured is not None and all(k in measured for k in dom_name.split("+")):
         traffic = sum(measured[k] for k in dom_name.split("+"))
@@ -262,7 +307,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.note}; B={w.B} M={w.M} D={w.D} L={w.L} K={w.K} "
                                f"Nq={w.num_queries} Nv={w.Nv} shapes={list(w.shapes)} "
-                               f"offsets N(0,{w.sigma_px} px)",
+                               f"offsets N(0,{w.sigma_px} px)"
+                               + ("; fused front-end (reference points + offsets, softmax "
+                                  "of logits, in the kernels)" if fused else ""),
+                   "frontend": args.frontend,
                    "points_per_step": w.points, "global_batch": w.B, "parallelism": "none"},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
@@ -276,7 +324,7 @@ def main():
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget, fused)
     print(json.dumps(result), flush=True)
 
 

@@ -132,21 +132,50 @@ struct Params {
     float* grad_logits;       // [B, Nq, M, L*K]
 };
 
-// Fused front-end of point j (level l) of tuple t: the location is the
-// reference point plus the offset over the level's size (W for x, H for y),
-// the quotient and the sum each rounded to float; the weight is
-// exp(z - max) / sum over the tuple's L*K logits.
-__device__ inline void fused_point(const Params& p, int t, int j, int l, int4 lv, float zmax,
-                                   float inv_sum, float2& uv, float& a) {
+// The inputs of point j (level l) of tuple t as loaded: its location and
+// weight, or (fused front-end) the reference point, the offset in level pixels
+// and the logit. Loading is kept apart from finish_point's arithmetic so that
+// a chunk's loads can stay in flight while the previous chunk is gathered.
+struct PointIn {
+    float2 uv;    // location, or the reference point
+    float2 off;   // fused: offset
+    float z;      // weight, or the logit
+};
+
+template <bool kFused>
+__device__ inline PointIn load_point(const Params& p, int t, int j, int l) {
+    PointIn in;
     const size_t pt = (size_t)t * p.LK + j;
-    const size_t bq = (size_t)(t / p.M);
-    const float2 r = *reinterpret_cast<const float2*>(p.ref + 2 * (bq * p.L + l));
-    const float2 o = *reinterpret_cast<const float2*>(p.off + 2 * pt);
-    const float qx = o.x / (float)lv.y;
-    const float qy = o.y / (float)lv.x;
-    uv.x = r.x + qx;
-    uv.y = r.y + qy;
-    a = expf(p.logits[pt] - zmax) * inv_sum;
+    if constexpr (kFused) {
+        const size_t bq = (size_t)(t / p.M);
+        in.uv = *reinterpret_cast<const float2*>(p.ref + 2 * (bq * p.L + l));
+        in.off = *reinterpret_cast<const float2*>(p.off + 2 * pt);
+        in.z = p.logits[pt];
+    } else {
+        in.uv = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
+        in.off = make_float2(0.0f, 0.0f);
+        in.z = p.attn[pt];
+    }
+    return in;
+}
+
+// Fused front-end: the location is the reference point plus the offset over
+// the level's size (W for x, H for y), the quotient and the sum each rounded
+// to float; the weight is exp(z - max) / sum over the tuple's L*K logits
+// (zmax and inv_sum are that max and 1 / sum).
+template <bool kFused>
+__device__ inline void finish_point(const PointIn& in, int4 lv, float zmax, float inv_sum,
+                                    float2& uv, float& a) {
+    if constexpr (kFused) {
+        const float qx = in.off.x / (float)lv.y;
+        const float qy = in.off.y / (float)lv.x;
+        uv.x = in.uv.x + qx;
+        uv.y = in.uv.y + qy;
+        a = expf(in.z - zmax) * inv_sum;
+    } else {
+        uv = in.uv;
+        a = in.z;
+    }
 }
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -296,22 +325,44 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
 #pragma unroll
     for (int e = 0; e < PL; ++e) acc[e] = 0.0f;
 
-    // fused: the softmax statistics of tuple t1. Its G builder lanes (lane
-    // t1 % TPW + i * TPW) each scan every G-th logit and combine through LDS.
+    // this lane's point of the next chunk is loaded one chunk ahead, while
+    // the current chunk's rows are gathered
+    auto fetch = [&](int jc) {
+        const int j = min(jc + jrow, p.LK - 1);
+        return load_point<kFused>(p, t1, j, (unsigned)j / (unsigned)p.K);
+    };
+    PointIn in_next{};
+    if (t1_ok && p.LK > 0) in_next = fetch(0);
+
+    // fused: the softmax statistics of tuple t1 (while the first chunk's loads
+    // are in flight). Its G builder lanes (lane t1 % TPW + i * TPW) each scan
+    // every G-th logit, the first kZ of them kept in registers, and combine
+    // through LDS.
     float zmax = 0.0f, inv_sum = 0.0f;
     if constexpr (kFused) {
+        constexpr int kZ = 4;
         const float* z = p.logits + (size_t)t1 * p.LK;
+        float zr[kZ];
         float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kZ; ++i) {
+            const int j = jrow + i * G;
+            zr[i] = (t1_ok && j < p.LK) ? z[j] : -INFINITY;
+            mx = fmaxf(mx, zr[i]);
+        }
         if (t1_ok)
-            for (int j = jrow; j < p.LK; j += G) mx = fmaxf(mx, z[j]);
+            for (int j = jrow + kZ * G; j < p.LK; j += G) mx = fmaxf(mx, z[j]);
         stat[wave][lane] = mx;
         wave_sync();
         mx = -INFINITY;
         for (int i = 0; i < G; ++i) mx = fmaxf(mx, stat[wave][i * TPW + lane % TPW]);
         wave_sync();
         float se = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kZ; ++i)
+            if (t1_ok && jrow + i * G < p.LK) se += expf(zr[i] - mx);
         if (t1_ok)
-            for (int j = jrow; j < p.LK; j += G) se += expf(z[j] - mx);
+            for (int j = jrow + kZ * G; j < p.LK; j += G) se += expf(z[j] - mx);
         stat[wave][lane] = se;
         wave_sync();
         se = 0.0f;
@@ -321,32 +372,18 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
         inv_sum = 1.0f / se;
     }
 
-    // this lane's point of the next chunk: its location and weight are loaded
-    // one chunk ahead, while the current chunk's rows are gathered
-    auto fetch = [&](int jc, float2& uv, float& a) {
-        const int j = min(jc + jrow, p.LK - 1);
-        if constexpr (kFused) {
-            const int l = (unsigned)j / (unsigned)p.K;
-            fused_point(p, t1, j, l, levels[l], zmax, inv_sum, uv, a);
-        } else {
-            const size_t pt = (size_t)t1 * p.LK + j;
-            uv = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
-            a = p.attn[pt];
-        }
-    };
-    float2 uv_next = make_float2(0.f, 0.f);
-    float a_next = 0.0f;
-    if (t1_ok && p.LK > 0) fetch(0, uv_next, a_next);
     for (int jc = 0; jc < p.LK; jc += G) {
-        const float2 uv = uv_next;
-        const float a = a_next;
-        if (t1_ok && jc + G < p.LK) fetch(jc + G, uv_next, a_next);
+        const PointIn in = in_next;
+        if (t1_ok && jc + G < p.LK) in_next = fetch(jc + G);
         // phase 1: one point per lane -> record in LDS
         FwdRecord rec;
         const int j = jc + jrow;
         if (t1_ok && j < p.LK) {
             const int l = (unsigned)j / (unsigned)p.K;
             const int4 lv = levels[l];
+            float2 uv;
+            float a;
+            finish_point<kFused>(in, lv, zmax, inv_sum, uv, a);
             const Geometry geo = point_geometry(uv.x, uv.y, lv, base1, row_bytes);
             const float ay0 = a * (1.0f - geo.fy), ay1 = a * geo.fy;
             const float w[4] = {ay0 * (1.0f - geo.fx), ay0 * geo.fx, ay1 * (1.0f - geo.fx),
@@ -465,31 +502,23 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
     }
     float s_ag = 0.0f;   // fused: this lane's part of sum_j A_j gA_j over the tuple
 
-    // this lane's point of the next chunk: its location and weight are loaded
-    // one chunk ahead, while the current chunk's rows are gathered
-    auto fetch = [&](int jc, float2& uv, float& a) {
+    // this lane's point of the next chunk is loaded one chunk ahead, while
+    // the current chunk's rows are gathered
+    auto fetch = [&](int jc) {
         const int j = min(jc + r, p.LK - 1);
-        if constexpr (kFused) {
-            const int l = (unsigned)j / (unsigned)p.K;
-            fused_point(p, t, j, l, levels[l], zmax, inv_sum, uv, a);
-        } else {
-            const size_t pt = (size_t)t * p.LK + j;
-            uv = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
-            a = p.attn[pt];
-        }
+        return load_point<kFused>(p, t, j, (unsigned)j / (unsigned)p.K);
     };
-    float2 uv_next = make_float2(0.f, 0.f);
-    float a_next = 0.0f;
-    if (t_ok && p.LK > 0) fetch(0, uv_next, a_next);
+    PointIn in_next{};
+    if (t_ok && p.LK > 0) in_next = fetch(0);
     for (int jc = 0; jc < p.LK; jc += G) {
-        const float2 uv = uv_next;
-        float a = a_next;
-        if (t_ok && jc + G < p.LK) fetch(jc + G, uv_next, a_next);
+        const PointIn in = in_next;
+        if (t_ok && jc + G < p.LK) in_next = fetch(jc + G);
         // phase 1: this lane's point -> corner offsets in LDS; keep the rest
         const int j = jc + r;
         const bool mine = t_ok && j < p.LK;
         size_t pt = 0;
         float Hf = 0.0f, Wf = 0.0f;
+        float a = 0.0f;
         Geometry geo;
         if (mine) {
             const int l = (unsigned)j / (unsigned)p.K;
@@ -497,6 +526,8 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
             pt = (size_t)t * p.LK + j;
             Hf = (float)lv.x;
             Wf = (float)lv.y;
+            float2 uv;
+            finish_point<kFused>(in, lv, zmax, inv_sum, uv, a);
             geo = point_geometry(uv.x, uv.y, lv, base, row_bytes);
         } else {
             geo.fx = geo.fy = 0.0f;
@@ -779,7 +810,8 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
             const int j = ok ? it.j : 0;
             const int l = ok ? it.l : 0;
             const float2 st = want_a ? p.smax[t] : make_float2(0.f, 0.f);
-            fused_point(p, t, j, l, make_int4(lt[l].H, lt[l].W, lt[l].start, 0), st.x, st.y, uv, a);
+            finish_point<true>(load_point<true>(p, t, j, l),
+                               make_int4(lt[l].H, lt[l].W, lt[l].start, 0), st.x, st.y, uv, a);
         } else {
             const size_t pt = ok ? it.pt : it.pt0;
             uv = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
@@ -1042,14 +1074,40 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
 // Softmax statistics of every tuple's L*K logits: (max, 1 / sum exp(z - max)),
 // one thread per tuple.
 __global__ __launch_bounds__(kBlock) void msda_softmax_stats_kernel(Params p) {
-    const int t = blockIdx.x * kBlock + threadIdx.x;
-    if (t >= p.T) return;
-    const float* z = p.logits + (size_t)t * p.LK;
-    float mx = -INFINITY;
-    for (int j = 0; j < p.LK; ++j) mx = fmaxf(mx, z[j]);
-    float se = 0.0f;
-    for (int j = 0; j < p.LK; ++j) se += expf(z[j] - mx);
-    p.smax[t] = make_float2(mx, 1.0f / se);
+    // a quad of lanes per tuple: with L*K a multiple of 4 (and 16-byte aligned
+    // logits) each lane reads whole float4s, so the quads of a wave read one
+    // contiguous run of logits. Grid-stride over tuples; a quad's lanes always
+    // share their tuple, so all four take part in the quad reductions.
+    const int i = threadIdx.x & 3;
+    const bool vec = (p.LK & 3) == 0 && (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0;
+    const int n4 = p.LK >> 2;
+    const int64_t stride = (int64_t)gridDim.x * (kBlock / 4);
+    for (int64_t t = ((int64_t)blockIdx.x * kBlock + threadIdx.x) >> 2; t < p.T; t += stride) {
+        const float* z = p.logits + t * p.LK;
+        const float4* z4 = reinterpret_cast<const float4*>(z);
+        float mx = -INFINITY;
+        if (vec) {
+            for (int f = i; f < n4; f += 4) {
+                const float4 v = z4[f];
+                mx = fmaxf(mx, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+            }
+        } else {
+            for (int j = i; j < p.LK; j += 4) mx = fmaxf(mx, z[j]);
+        }
+        mx = fmaxf(mx, dpp<0xB1>(mx));   // quad_perm [1,0,3,2]
+        mx = fmaxf(mx, dpp<0x4E>(mx));   // quad_perm [2,3,0,1]
+        float se = 0.0f;
+        if (vec) {
+            for (int f = i; f < n4; f += 4) {
+                const float4 v = z4[f];
+                se += (expf(v.x - mx) + expf(v.y - mx)) + (expf(v.z - mx) + expf(v.w - mx));
+            }
+        } else {
+            for (int j = i; j < p.LK; j += 4) se += expf(z[j] - mx);
+        }
+        se = group_sum<4>(se);
+        if (i == 0) p.smax[t] = make_float2(mx, 1.0f / se);
+    }
 }
 
 // Gradient of a reference point: every head's and point's location on its
@@ -1438,8 +1496,10 @@ msda_status_t msda_backward_fused(const msda_dims_t* dims, msda_dtype_t value_dt
     p.smax = reinterpret_cast<float2*>(static_cast<char*>(workspace) + pl.smax_off);
     const Kernels k = pick(value_dtype, dims->D);
     if (!k.point_fused) return MSDA_ERROR_NOT_SUPPORTED;
+    // (none if T = 0; at most 2^20 blocks, which stride over the tuples)
     msda_status_t s = launch(reinterpret_cast<const void*>(&msda_softmax_stats_kernel),
-                             ((int64_t)p.T + kBlock - 1) / kBlock, p, stream);   // none if T = 0
+                             std::min<int64_t>((4 * (int64_t)p.T + kBlock - 1) / kBlock, 1 << 20),
+                             p, stream);
     if (s != MSDA_SUCCESS) return s;
     if (want_value) {
         s = launch_grad_value(p, pl.core, dims, k.bin_fused, k.tile, workspace, stream);
