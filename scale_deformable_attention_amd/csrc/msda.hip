@@ -432,21 +432,27 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
 // request at the memory side, and LDS fp32 atomics are slower still).
 //
 //  1. msda_bwd_point_kernel: the weight and location gradients. Same tuple
-//     mapping as the forward; per point the group gathers the four corner rows,
-//     forms the four dot products g . v_c, reduces them across the group with
-//     DPP, and the record's owner lane finishes the point.
+//     mapping as the forward; lane r of group g builds and finishes point
+//     jc + r of its tuple. Per point the group gathers the four corner rows,
+//     forms the four partial dot products g . v_c, reduces them across the
+//     group with DPP, and the point's lane keeps them and finishes the point.
 //  2. msda_bin_kernel: sorts the points into buckets by the grad_value tiles
 //     (TH x TW pixels of one (b, m, level)) their inside-the-level corners land
 //     in. A block owns a range of queries of one (b, m); it counts per tile with
 //     LDS integer atomics (fast), scans, writes its per-tile (count, offset)
-//     row to the workspace and the point indices to its own slab. No global
-//     atomics: every block writes only its own rows.
-//  3. msda_tile_kernel: one block owns one tile. It collects the tile's points
-//     from every slab of its (b, m), sorts them by cell (counting sort in LDS),
-//     and lane group c sweeps pixel column c top to bottom: the cells left of
-//     and at the column feed it, two rows at a time, and the column's pixel
-//     sums live in registers. Every grad_value element is then written exactly
-//     once with a plain store (zeros where nothing lands), so no fill pass.
+//     row to the workspace and one 16-byte entry per (point, tile) -- tuple,
+//     pixel coordinates, weight -- to its own slab. No global atomics: every
+//     block writes only its own rows.
+//  3. msda_tile_kernel: persistent blocks fetch tiles from a counter per XCD
+//     group. A block collects its tile's entries from every slab of the tile's
+//     (b, m), sorts them by cell (counting sort in LDS), and lane group c
+//     sweeps pixel column c top to bottom: the cells left of and at the column
+//     feed it, and the column's pixel sums live in registers. Every grad_value
+//     element is then written exactly once with a plain store (zeros where
+//     nothing lands), so no fill pass.
+// The fused front-end adds msda_softmax_stats_kernel before these (the
+// softmax max and 1/sum per tuple) and msda_ref_grad_kernel after the point
+// kernel (the reference-point gradient, a sum over heads and points).
 
 template <typename T, int D, bool kFused>
 __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
