@@ -67,7 +67,7 @@ extern "C" {
 #endif
 
 #define MSDA_VERSION_MAJOR 0
-#define MSDA_VERSION_MINOR 3
+#define MSDA_VERSION_MINOR 4
 #define MSDA_VERSION_PATCH 0
 
 /* Largest number of feature levels the kernels accept. */
@@ -210,6 +210,116 @@ msda_status_t msda_backward_fused(const msda_dims_t *dims, msda_dtype_t value_dt
 /* Bytes of workspace msda_backward_fused needs for these sizes. No HIP call. */
 msda_status_t msda_backward_fused_workspace_size(const msda_dims_t *dims,
                                                  msda_dtype_t value_dtype, size_t *bytes);
+
+/*
+ * Fully connected layer y = x W^T + b (torch nn.Linear semantics), fp32 on the
+ * matrix cores (fp32 products, fp32 accumulation). MSDeformAttn wraps the
+ * core in four of them: the value projection on the flattened input, the
+ * sampling-offset and attention-weight heads on the query, and the output
+ * projection (deformable-attention practice guide, section 3.1;
+ * DETR-to-Deformable-DETR article, section 3.2).
+ *
+ *   x       [rows, in_features]
+ *   weight  [out_features, in_features]
+ *   bias    [out_features], or NULL for none
+ *   y       [rows, out_features], overwritten
+ *
+ * rows may be 0; in_features, out_features >= 1. Sizes of 2^30 rows or 2^20
+ * features and more return MSDA_ERROR_NOT_SUPPORTED. Pointers 4-byte aligned
+ * (16-byte aligned tensors with feature counts that are multiples of 4 take
+ * vector loads).
+ */
+msda_status_t msda_linear_forward(int64_t rows, int64_t in_features, int64_t out_features,
+                                  const float *x, const float *weight, const float *bias,
+                                  float *y, hipStream_t stream);
+
+/*
+ * Backward of msda_linear_forward for grad_y [rows, out_features]:
+ *   grad_x      [rows, in_features]          = grad_y W
+ *   grad_weight [out_features, in_features]  = grad_y^T x
+ *   grad_bias   [out_features]               = sum of grad_y over the rows
+ * each overwritten, each may be NULL to skip it. The weight and bias
+ * gradients sum over the rows in a fixed order (split over blocks, then the
+ * splits in order): repeatable bit for bit. workspace: at least
+ * msda_linear_backward_workspace_size() bytes, 16-byte aligned, clobbered;
+ * needed when grad_weight or grad_bias is requested.
+ */
+msda_status_t msda_linear_backward(int64_t rows, int64_t in_features, int64_t out_features,
+                                   const float *x, const float *weight, const float *grad_y,
+                                   float *grad_x, float *grad_weight, float *grad_bias,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace msda_linear_backward needs. No HIP call. */
+msda_status_t msda_linear_backward_workspace_size(int64_t rows, int64_t in_features,
+                                                  int64_t out_features, size_t *bytes);
+
+/*
+ * The whole MSDeformAttn layer around the fused core (deformable-attention
+ * practice guide, section 3.1: value_proj, sampling_offsets,
+ * attention_weights and output_proj; DETR-to-Deformable-DETR article,
+ * section 3.2), fp32 throughout, C = M * D channels:
+ *
+ *   value   = input_flatten W_v^T + b_v     [B, Nv, C], read as [B, Nv, M, D]
+ *   offsets = query W_o^T + b_o             [B, Nq, M*L*K*2] = [B, Nq, M, L, K, 2]
+ *   logits  = query W_a^T + b_a             [B, Nq, M*L*K]   = [B, Nq, M, L*K]
+ *   core    = msda_forward_fused(value, reference_points, offsets, logits)
+ *   output  = core W_out^T + b_out          [B, Nq, C]
+ *
+ * Weights are torch nn.Linear layouts: W_v, W_out [C, C]; W_o [M*L*K*2, C];
+ * W_a [M*L*K, C]; biases [out features] or NULL for none. No padding mask
+ * (every value row is a real pixel).
+ */
+typedef struct {
+    const float *value_weight, *value_bias;    /* [C, C], [C]                   */
+    const float *offset_weight, *offset_bias;  /* [M*L*K*2, C], [M*L*K*2]       */
+    const float *attn_weight, *attn_bias;      /* [M*L*K, C], [M*L*K]           */
+    const float *output_weight, *output_bias;  /* [C, C], [C]                   */
+} msda_layer_params_t;
+
+/* Gradients of the layer's parameters, same layouts; NULL skips one. */
+typedef struct {
+    float *value_weight, *value_bias;
+    float *offset_weight, *offset_bias;
+    float *attn_weight, *attn_bias;
+    float *output_weight, *output_bias;
+} msda_layer_grads_t;
+
+/*
+ * Forward of the layer. query [B, Nq, C], input_flatten [B, Nv, C],
+ * reference_points [B, Nq, L, 2], output [B, Nq, C] (overwritten).
+ * saved: caller-owned device buffer of msda_layer_saved_size() bytes,
+ * 256-byte aligned; the forward writes value, offsets, logits and core into
+ * it, and msda_layer_backward reads them. dims->D in {8, 16, 32, 64},
+ * M*L*K >= 1. Alignment: query, input_flatten, output 16-byte;
+ * reference_points 8-byte; weights 4-byte.
+ */
+msda_status_t msda_layer_forward(const msda_dims_t *dims, const float *query,
+                                 const float *input_flatten, const float *reference_points,
+                                 const int64_t *spatial_shapes, const int64_t *level_start_index,
+                                 const msda_layer_params_t *params, float *output, void *saved,
+                                 size_t saved_bytes, hipStream_t stream);
+
+/*
+ * Backward of the layer for grad_output [B, Nq, C], from the buffer `saved`
+ * that msda_layer_forward filled with the same inputs and parameters.
+ * Writes (each may be NULL): grad_query [B, Nq, C], grad_input_flatten
+ * [B, Nv, C], grad_reference_points [B, Nq, L, 2] and the parameter
+ * gradients in *grads (grads may be NULL). workspace: device scratch of
+ * msda_layer_workspace_size() bytes, 256-byte aligned, clobbered.
+ */
+msda_status_t msda_layer_backward(const msda_dims_t *dims, const float *query,
+                                  const float *input_flatten, const float *reference_points,
+                                  const int64_t *spatial_shapes, const int64_t *level_start_index,
+                                  const msda_layer_params_t *params, const void *saved,
+                                  size_t saved_bytes, const float *grad_output, float *grad_query,
+                                  float *grad_input_flatten, float *grad_reference_points,
+                                  const msda_layer_grads_t *grads, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of the forward's saved activations and of the backward's workspace.
+ * No HIP call. */
+msda_status_t msda_layer_saved_size(const msda_dims_t *dims, size_t *bytes);
+msda_status_t msda_layer_workspace_size(const msda_dims_t *dims, size_t *bytes);
 
 /* Host-side check of a HOST copy of the level tables against Nv: every
  * H_l, W_l >= 1, level_start_index the prefix sums, sum H_l*W_l == Nv.

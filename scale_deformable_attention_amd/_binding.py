@@ -23,6 +23,18 @@ class MsdaDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("B", "Nv", "M", "D", "L", "Nq", "K")]
 
 
+LAYER_PARAMS = ("value_weight", "value_bias", "offset_weight", "offset_bias", "attn_weight",
+                "attn_bias", "output_weight", "output_bias")
+
+
+class MsdaLayerParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_PARAMS]
+
+
+class MsdaLayerGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_PARAMS]
+
+
 class MsdaError(RuntimeError):
     def __init__(self, status, where):
         super().__init__(f"{where}: {STATUS.get(status, status)} "
@@ -64,6 +76,27 @@ def library():
         lib.msda_backward_fused.argtypes = [ctypes.POINTER(MsdaDims), ctypes.c_int, vp, i64p,
                                             i64p, fp, fp, fp, fp, fp, fp, fp, fp, vp,
                                             ctypes.c_size_t, vp]
+        i64 = ctypes.c_int64
+        lib.msda_linear_forward.restype = ctypes.c_int
+        lib.msda_linear_forward.argtypes = [i64, i64, i64, fp, fp, fp, fp, vp]
+        lib.msda_linear_backward.restype = ctypes.c_int
+        lib.msda_linear_backward.argtypes = [i64, i64, i64, fp, fp, fp, fp, fp, fp, vp,
+                                             ctypes.c_size_t, vp]
+        lib.msda_linear_backward_workspace_size.restype = ctypes.c_int
+        lib.msda_linear_backward_workspace_size.argtypes = [i64, i64, i64,
+                                                            ctypes.POINTER(ctypes.c_size_t)]
+        lp, lg = ctypes.POINTER(MsdaLayerParams), ctypes.POINTER(MsdaLayerGrads)
+        lib.msda_layer_forward.restype = ctypes.c_int
+        lib.msda_layer_forward.argtypes = [ctypes.POINTER(MsdaDims), fp, fp, fp, i64p, i64p, lp,
+                                           fp, vp, ctypes.c_size_t, vp]
+        lib.msda_layer_backward.restype = ctypes.c_int
+        lib.msda_layer_backward.argtypes = [ctypes.POINTER(MsdaDims), fp, fp, fp, i64p, i64p, lp,
+                                            vp, ctypes.c_size_t, fp, fp, fp, fp, lg, vp,
+                                            ctypes.c_size_t, vp]
+        for name in ("msda_layer_saved_size", "msda_layer_workspace_size"):
+            getattr(lib, name).restype = ctypes.c_int
+            getattr(lib, name).argtypes = [ctypes.POINTER(MsdaDims),
+                                           ctypes.POINTER(ctypes.c_size_t)]
         lib.msda_backward_fused_workspace_size.restype = ctypes.c_int
         lib.msda_backward_fused_workspace_size.argtypes = [ctypes.POINTER(MsdaDims), ctypes.c_int,
                                                            ctypes.POINTER(ctypes.c_size_t)]
@@ -399,3 +432,183 @@ def ms_deform_attn_fused(value, spatial_shapes, level_start_index, reference_poi
     """Differentiable fused front-end + core: output [B, Nq, M*D]."""
     return MSDeformAttnFusedFunction.apply(value, spatial_shapes, level_start_index,
                                            reference_points, sampling_offsets, attention_logits)
+
+
+# ----------------------------------------------------------------------------- linear layers
+def _linear_sizes(x, weight):
+    if weight.dim() != 2:
+        raise ValueError("weight must be [out_features, in_features]")
+    O, I = weight.shape
+    if x.shape[-1] != I:
+        raise ValueError("x's last dimension must equal in_features")
+    return x.numel() // I if I else 0, I, O
+
+
+def msda_linear_forward(x, weight, bias=None, output=None, stream=None):
+    """y = x W^T + b on the matrix cores (include/msda.h msda_linear_forward).
+    x [..., in], weight [out, in], bias [out] or None -> y [..., out], fp32."""
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    _check(x, "x", (torch.float32,), dev)
+    _check(weight, "weight", (torch.float32,), dev)
+    if bias is not None:
+        _check(bias, "bias", (torch.float32,), dev)
+    R, I, O = _linear_sizes(x, weight)
+    if bias is not None and tuple(bias.shape) != (O,):
+        raise ValueError("bias must be [out_features]")
+    if output is None:
+        output = torch.empty(tuple(x.shape[:-1]) + (O,), dtype=torch.float32, device=dev)
+    else:
+        _check(output, "output", (torch.float32,), dev)
+        if output.numel() != R * O:
+            raise ValueError("output has the wrong number of elements")
+    st = library().msda_linear_forward(R, I, O, _ptr(x), _ptr(weight), _ptr(bias), _ptr(output),
+                                       _stream(dev, stream))
+    if st != 0:
+        raise MsdaError(st, "msda_linear_forward")
+    return output
+
+
+def msda_linear_backward_workspace_size(rows, in_features, out_features):
+    n = ctypes.c_size_t(0)
+    st = library().msda_linear_backward_workspace_size(rows, in_features, out_features,
+                                                       ctypes.byref(n))
+    if st != 0:
+        raise MsdaError(st, "msda_linear_backward_workspace_size")
+    return n.value
+
+
+def msda_linear_backward(x, weight, grad_y, needs=(True, True, True), workspace=None,
+                         stream=None):
+    """Gradients of msda_linear_forward (include/msda.h msda_linear_backward):
+    (grad_x, grad_weight, grad_bias), None where ``needs`` is False."""
+    dev = x.device
+    _check(x, "x", (torch.float32,), dev)
+    _check(weight, "weight", (torch.float32,), dev)
+    _check(grad_y, "grad_y", (torch.float32,), dev)
+    R, I, O = _linear_sizes(x, weight)
+    if grad_y.numel() != R * O:
+        raise ValueError("grad_y has the wrong number of elements")
+    gx = torch.empty_like(x) if needs[0] else None
+    gw = torch.empty_like(weight) if needs[1] else None
+    gb = torch.empty(O, dtype=torch.float32, device=dev) if needs[2] else None
+    n = msda_linear_backward_workspace_size(R, I, O)
+    if workspace is None and (needs[1] or needs[2]):
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = library().msda_linear_backward(R, I, O, _ptr(x), _ptr(weight), _ptr(grad_y), _ptr(gx),
+                                        _ptr(gw), _ptr(gb), _ptr(workspace),
+                                        ctypes.c_size_t(ws_bytes), _stream(dev, stream))
+    if st != 0:
+        raise MsdaError(st, "msda_linear_backward")
+    return gx, gw, gb
+
+
+# ----------------------------------------------------------------------------- the layer
+def _layer_dims(query, input_flatten, spatial_shapes, n_heads, n_points):
+    B, Nq, C = query.shape
+    Bv, Nv, Cv = input_flatten.shape
+    if (Bv, Cv) != (B, C):
+        raise ValueError("query and input_flatten must share batch and channels")
+    if C % n_heads:
+        raise ValueError("channels must be a multiple of the head count")
+    L = spatial_shapes.shape[0]
+    return MsdaDims(B, Nv, n_heads, C // n_heads, L, Nq, n_points)
+
+
+def _layer_params(params, dev):
+    st = MsdaLayerParams()
+    for n in LAYER_PARAMS:
+        t = params.get(n)
+        if t is not None:
+            _check(t, n, (torch.float32,), dev)
+        setattr(st, n, None if t is None else t.data_ptr())
+    return st
+
+
+def msda_layer_sizes(query, input_flatten, spatial_shapes, n_heads, n_points):
+    """(saved bytes, workspace bytes) of the layer entry points."""
+    dims = _layer_dims(query, input_flatten, spatial_shapes, n_heads, n_points)
+    a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    for name, out in (("msda_layer_saved_size", a), ("msda_layer_workspace_size", b)):
+        st = getattr(library(), name)(ctypes.byref(dims), ctypes.byref(out))
+        if st != 0:
+            raise MsdaError(st, name)
+    return a.value, b.value
+
+
+def msda_layer_forward(query, input_flatten, reference_points, spatial_shapes,
+                       level_start_index, params, n_heads, n_points, output=None, saved=None,
+                       stream=None):
+    """MSDeformAttn layer forward (include/msda.h msda_layer_forward).
+    params: dict of the eight tensors named in LAYER_PARAMS (biases may be
+    None). Returns (output [B, Nq, C], saved), saved being the uint8 buffer
+    the backward needs."""
+    dev = query.device
+    if dev.type != "cuda":
+        raise ValueError("query must be a GPU tensor")
+    for t, n in ((query, "query"), (input_flatten, "input_flatten"),
+                 (reference_points, "reference_points")):
+        _check(t, n, (torch.float32,), dev)
+    _check(spatial_shapes, "spatial_shapes", (torch.int64,), dev)
+    _check(level_start_index, "level_start_index", (torch.int64,), dev)
+    dims = _layer_dims(query, input_flatten, spatial_shapes, n_heads, n_points)
+    if tuple(reference_points.shape) != (dims.B, dims.Nq, dims.L, 2):
+        raise ValueError("reference_points must be [B, Nq, L, 2]")
+    nsaved, _ = msda_layer_sizes(query, input_flatten, spatial_shapes, n_heads, n_points)
+    if saved is None:
+        saved = torch.empty(max(nsaved, 1), dtype=torch.uint8, device=dev)
+    if output is None:
+        output = torch.empty_like(query)
+    pst = _layer_params(params, dev)
+    st = library().msda_layer_forward(ctypes.byref(dims), _ptr(query), _ptr(input_flatten),
+                                      _ptr(reference_points), _ptr(spatial_shapes),
+                                      _ptr(level_start_index), ctypes.byref(pst), _ptr(output),
+                                      _ptr(saved), ctypes.c_size_t(saved.numel()),
+                                      _stream(dev, stream))
+    if st != 0:
+        raise MsdaError(st, "msda_layer_forward")
+    return output, saved
+
+
+def msda_layer_backward(query, input_flatten, reference_points, spatial_shapes,
+                        level_start_index, params, n_heads, n_points, saved, grad_output,
+                        needs_inputs=(True, True, True), needs_params=True, grads=None,
+                        workspace=None, stream=None):
+    """Gradients of the layer (include/msda.h msda_layer_backward). Returns a
+    dict: query, input_flatten, reference_points and the parameter names of
+    LAYER_PARAMS (parameters that are None, or not needed, are absent).
+    ``grads`` may hold preallocated output tensors under those names."""
+    dev = query.device
+    _check(grad_output, "grad_output", (torch.float32,), dev)
+    dims = _layer_dims(query, input_flatten, spatial_shapes, n_heads, n_points)
+    _, nws = msda_layer_sizes(query, input_flatten, spatial_shapes, n_heads, n_points)
+    if workspace is None:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    out = dict(grads or {})
+    for need, name, like in zip(needs_inputs, ("query", "input_flatten", "reference_points"),
+                                (query, input_flatten, reference_points)):
+        if need and name not in out:
+            out[name] = torch.empty_like(like)
+        elif not need:
+            out.pop(name, None)
+    gst = MsdaLayerGrads()
+    for n in LAYER_PARAMS:
+        if needs_params and params.get(n) is not None:
+            if n not in out:
+                out[n] = torch.empty_like(params[n])
+            setattr(gst, n, out[n].data_ptr())
+        else:
+            out.pop(n, None)
+            setattr(gst, n, None)
+    pst = _layer_params(params, dev)
+    st = library().msda_layer_backward(
+        ctypes.byref(dims), _ptr(query), _ptr(input_flatten), _ptr(reference_points),
+        _ptr(spatial_shapes), _ptr(level_start_index), ctypes.byref(pst), _ptr(saved),
+        ctypes.c_size_t(saved.numel()), _ptr(grad_output), _ptr(out.get("query")),
+        _ptr(out.get("input_flatten")), _ptr(out.get("reference_points")), ctypes.byref(gst),
+        _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(dev, stream))
+    if st != 0:
+        raise MsdaError(st, "msda_layer_backward")
+    return out

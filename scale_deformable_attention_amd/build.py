@@ -5,7 +5,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "msda.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "msda.hip"), os.path.join(HERE, "csrc", "linear.hip"),
+           os.path.join(HERE, "csrc", "layer.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libmsda.so")
 ARCH = "gfx950"

@@ -1,0 +1,26 @@
+// gemm.h -- internal interface of the matrix-core GEMM in linear.hip, used by
+// the layer entry points. Not part of the C ABI.
+#pragma once
+#include <stdint.h>
+
+#include "msda.h"
+
+// C[m, n] = sum_k A(m, k) B(k, n) (+ bias[n]) (+ C[m, n] if accumulate), fp32.
+//   a_kmajor: A(m, k) = A[m * lda + k], else A[k * lda + m]
+//   b_kmajor: B(k, n) = B[n * ldb + k], else B[k * ldb + n]
+// splits > 1 splits the reduction over blocks into `partials` (splits * M * N
+// floats, device) and sums them with a second kernel.
+msda_status_t msda_gemm(bool a_kmajor, bool b_kmajor, int M, int N, int K, const float* A,
+                        int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
+                        const float* bias, bool accumulate, int splits, float* partials,
+                        hipStream_t stream);
+
+// out[n] (+)= sum over the R rows of g[r * ldg + n], through `partials`
+// (splits * N floats, device).
+msda_status_t msda_colsum(int R, int N, const float* g, int64_t ldg, float* out, int splits,
+                          float* partials, bool accumulate, hipStream_t stream);
+
+// Reduction splits used for a weight gradient over `rows` rows, and the
+// workspace floats a linear backward needs.
+int msda_linear_splits(int64_t rows);
+size_t msda_linear_workspace_floats(int64_t rows, int64_t in_features, int64_t out_features);

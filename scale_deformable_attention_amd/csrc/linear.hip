@@ -1,0 +1,430 @@
+// linear.hip -- the fully connected projections around the deformable
+// attention core on the gfx950 matrix cores: y = x W^T + b and its gradients
+// (torch nn.Linear semantics). In MSDeformAttn four of them surround the core:
+// the value projection, the sampling-offset and attention-weight heads on the
+// query, and the output projection (deformable-attention practice guide,
+// section 3.1; DETR-to-Deformable-DETR article, section 3.2).
+//
+// One kernel serves the three products a linear layer needs:
+//   forward      y[r, o]  = sum_i x[r, i] W[o, i]       (both operands i-contiguous)
+//   input grad   dx[r, i] = sum_o dy[r, o] W[o, i]      (W walked along its rows)
+//   weight grad  dW[o, i] = sum_r dy[r, o] x[r, i]      (reduction over the rows,
+//                                                         split over blocks)
+// Block tile 128 x 128, four waves of 64 x 64, each a 2 x 2 grid of
+// v_mfma_f32_32x32x2_f32 (fp32 in, fp32 accumulate). A 16-deep slice of both
+// operands is staged in LDS, k-major, double buffered; the next slice's
+// global loads are in flight while the current one feeds the matrix cores.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "gemm.h"
+#include "msda.h"
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;          // 4 waves
+constexpr int kTile = 128;             // block tile, rows and columns
+constexpr int kBK = 16;                // reduction slice per iteration
+constexpr int kLdsRow = kTile + 4;     // padded LDS row (floats)
+constexpr int kSplitMax = 256;         // reduction splits of a weight gradient at most
+
+// C = A B (+ bias) (+ C) with A(m, k), B(k, n) read through strides:
+//   kAK: A(m, k) = A[m * lda + k]   else A[k * lda + m]
+//   kBK_: B(k, n) = B[n * ldb + k]  else B[k * ldb + n]
+struct GemmArgs {
+    const float* A;
+    const float* B;
+    float* C;
+    const float* bias;     // [N], or null
+    int64_t lda, ldb, ldc;
+    int M, N, K;
+    int k_split;           // reduction length per split (a multiple of kBK)
+    int splits;
+    int accumulate;        // C += result (splits == 1 only)
+    int64_t split_stride;  // elements between consecutive splits' partial outputs
+};
+
+// Blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous
+// range of work items so that the column tiles of one row tile (which share
+// the rows of A) meet in one L2.
+__device__ inline int xcd_work_item() {
+    const int blk = blockIdx.x, nblk = gridDim.x;
+    const int x = blk % 8, i = blk / 8, per = nblk / 8, rem = nblk % 8;
+    return x * per + (x < rem ? x : rem) + i;
+}
+
+template <bool kAK, bool kBKm, bool kVec>
+__global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmArgs g) {
+    __shared__ float As[2][kBK * kLdsRow];
+    __shared__ float Bs[2][kBK * kLdsRow];
+    const int tid = threadIdx.x;
+    const int mt = (g.M + kTile - 1) / kTile, nt = (g.N + kTile - 1) / kTile;
+    const int work = xcd_work_item();
+    const int z = work / (mt * nt);
+    const int t = work - z * (mt * nt);
+    const int m0 = (t / nt) * kTile, n0 = (t % nt) * kTile;
+    const int kbeg = z * g.k_split;
+    const int kend = min(g.K, kbeg + g.k_split);
+
+    // ---- staging: 2048 elements of each operand per slice, 8 per thread
+    float ra[8], rb[8];
+    auto load = [&](const float* P, int64_t ld, bool kmajor, int lim_mn, int base_mn, int k0,
+                    float* r) {
+        if constexpr (kVec) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int idx = tid + kThreads * i;
+                int mn, k;
+                if (kmajor) {
+                    mn = idx >> 2;
+                    k = (idx & 3) * 4;
+                } else {
+                    k = idx >> 5;
+                    mn = (idx & 31) * 4;
+                }
+                const bool ok = base_mn + mn < lim_mn && k0 + k < kend;
+                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (ok) {
+                    const float* src = kmajor ? P + (int64_t)(base_mn + mn) * ld + (k0 + k)
+                                              : P + (int64_t)(k0 + k) * ld + (base_mn + mn);
+                    v = *reinterpret_cast<const float4*>(src);
+                }
+                r[4 * i] = v.x;
+                r[4 * i + 1] = v.y;
+                r[4 * i + 2] = v.z;
+                r[4 * i + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int idx = tid + kThreads * i;
+                const int mn = kmajor ? idx >> 4 : idx & (kTile - 1);
+                const int k = kmajor ? idx & (kBK - 1) : idx >> 7;
+                const bool ok = base_mn + mn < lim_mn && k0 + k < kend;
+                r[i] = ok ? (kmajor ? P[(int64_t)(base_mn + mn) * ld + (k0 + k)]
+                                    : P[(int64_t)(k0 + k) * ld + (base_mn + mn)])
+                          : 0.0f;
+            }
+        }
+    };
+    auto store = [&](float* S, bool kmajor, const float* r) {
+        if constexpr (kVec) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int idx = tid + kThreads * i;
+                if (kmajor) {
+                    const int mn = idx >> 2, k = (idx & 3) * 4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) S[(k + e) * kLdsRow + mn] = r[4 * i + e];
+                } else {
+                    const int k = idx >> 5, mn = (idx & 31) * 4;
+                    *reinterpret_cast<float4*>(&S[k * kLdsRow + mn]) =
+                        make_float4(r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int idx = tid + kThreads * i;
+                const int mn = kmajor ? idx >> 4 : idx & (kTile - 1);
+                const int k = kmajor ? idx & (kBK - 1) : idx >> 7;
+                S[k * kLdsRow + mn] = r[i];
+            }
+        }
+    };
+
+    // ---- wave tile 64 x 64 at (wm, wn); lane (li, lk) feeds row/column li, k-offset lk
+    const int lane = tid & 63, w = tid >> 6;
+    const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+    const int li = lane & 31, lk = lane >> 5;
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+    int buf = 0;
+    if (kbeg < kend) {
+        load(g.A, g.lda, kAK, g.M, m0, kbeg, ra);
+        load(g.B, g.ldb, kBKm, g.N, n0, kbeg, rb);
+        store(As[0], kAK, ra);
+        store(Bs[0], kBKm, rb);
+    }
+    __syncthreads();
+    for (int k0 = kbeg; k0 < kend; k0 += kBK) {
+        const bool more = k0 + kBK < kend;
+        if (more) {
+            load(g.A, g.lda, kAK, g.M, m0, k0 + kBK, ra);
+            load(g.B, g.ldb, kBKm, g.N, n0, k0 + kBK, rb);
+        }
+        const float* Ab = As[buf];
+        const float* Bb = Bs[buf];
+#pragma unroll
+        for (int s = 0; s < kBK; s += 2) {
+            const float* Ar = Ab + (s + lk) * kLdsRow + wm + li;
+            const float* Br = Bb + (s + lk) * kLdsRow + wn + li;
+            const float a0 = Ar[0], a1 = Ar[32], b0 = Br[0], b1 = Br[32];
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+        }
+        if (more) {
+            store(As[buf ^ 1], kAK, ra);
+            store(Bs[buf ^ 1], kBKm, rb);
+        }
+        __syncthreads();
+        buf ^= 1;
+    }
+
+    // ---- epilogue: 32x32 accumulator register r of lane (li, lk) holds
+    // row 8 * (r / 4) + 4 * lk + r % 4, column li
+    float* C = g.C + (int64_t)z * g.split_stride;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int col = n0 + wn + 32 * b + li;
+            if (col >= g.N) continue;
+            const float bv = g.bias ? g.bias[col] : 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm + 32 * a + 8 * (r >> 2) + 4 * lk + (r & 3);
+                if (row < g.M) {
+                    float* dst = C + (int64_t)row * g.ldc + col;
+                    float v = acc[a][b][r] + bv;
+                    if (g.accumulate) v += *dst;
+                    *dst = v;
+                }
+            }
+        }
+    }
+}
+
+// out[m, n] (row stride ldo) = sum over s < splits of part[s * M * N + m * N + n]
+// (+ bias[n]) (+ out[m, n] if accumulate). One thread per element.
+__global__ __launch_bounds__(kThreads) void msda_split_reduce_kernel(const float* part, int splits,
+                                                                     int M, int N, float* out,
+                                                                     int64_t ldo, const float* bias,
+                                                                     int accumulate) {
+    const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t MN = (int64_t)M * N;
+    if (e >= MN) return;
+    float s = 0.0f;
+    for (int i = 0; i < splits; ++i) s += part[(int64_t)i * MN + e];
+    const int m = (int)(e / N), n = (int)(e - (int64_t)m * N);
+    if (bias) s += bias[n];
+    float* dst = out + (int64_t)m * ldo + n;
+    if (accumulate) s += *dst;
+    *dst = s;
+}
+
+// part[s * N + n] = sum of g[r * ldg + n] over rows r of split s
+// (rows [s * rows_per, min(R, (s + 1) * rows_per))).
+__global__ __launch_bounds__(kThreads) void msda_colsum_kernel(const float* g, int64_t ldg, int R,
+                                                               int N, int rows_per, float* part) {
+    const int s = blockIdx.y;
+    const int n = blockIdx.x * kThreads + threadIdx.x;
+    if (n >= N) return;
+    const int r0 = s * rows_per, r1 = min(R, r0 + rows_per);
+    float acc = 0.0f;
+    for (int r = r0; r < r1; ++r) acc += g[(int64_t)r * ldg + n];
+    part[(int64_t)s * N + n] = acc;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int splits_for(int64_t R) {
+    // about 2 blocks per CU for the weight gradient's 128 x 128 tiles
+    const int64_t want = (R + 255) / 256;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(kSplitMax, want));
+}
+
+int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+}  // namespace
+
+// Shared with the layer entry points (msda_layer.hip): C = A B (+ bias) (+ C)
+// as described at GemmArgs; a_kmajor / b_kmajor pick the operand strides.
+// With splits > 1 the reduction is split over blocks into `partials`
+// (splits * M * N floats) and summed by a second kernel.
+msda_status_t msda_gemm(bool a_kmajor, bool b_kmajor, int M, int N, int K, const float* A,
+                        int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
+                        const float* bias, bool accumulate, int splits, float* partials,
+                        hipStream_t stream) {
+    if (M == 0 || N == 0) return MSDA_SUCCESS;
+    GemmArgs g;
+    g.A = A;
+    g.B = B;
+    g.bias = bias;
+    g.lda = lda;
+    g.ldb = ldb;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    splits = std::max(1, splits);
+    g.k_split = (int)round_up((K + splits - 1) / splits, kBK);
+    if (g.k_split == 0) g.k_split = kBK;
+    splits = (int)std::max<int64_t>(1, (K + g.k_split - 1) / g.k_split);
+    g.splits = splits;
+    if (splits > 1) {
+        g.C = partials;
+        g.ldc = N;
+        g.bias = nullptr;
+        g.accumulate = 0;
+        g.split_stride = (int64_t)M * N;
+    } else {
+        g.C = C;
+        g.ldc = ldc;
+        g.accumulate = accumulate ? 1 : 0;
+        g.split_stride = 0;
+    }
+    // vector loads: the contiguous dimension of each operand a multiple of 4
+    // floats, strides too, and 16-byte aligned bases
+    const bool a_vec = aligned(A, 16) && lda % 4 == 0 && (a_kmajor ? K % 4 == 0 : M % 4 == 0);
+    const bool b_vec = aligned(B, 16) && ldb % 4 == 0 && (b_kmajor ? K % 4 == 0 : N % 4 == 0);
+    const bool vec = a_vec && b_vec;
+    const void* kern = nullptr;
+#define MSDA_PICK(AK, BKM)                                                                   \
+    if (a_kmajor == AK && b_kmajor == BKM)                                                   \
+        kern = vec ? reinterpret_cast<const void*>(&msda_gemm_kernel<AK, BKM, true>)         \
+                   : reinterpret_cast<const void*>(&msda_gemm_kernel<AK, BKM, false>);
+    MSDA_PICK(true, true)
+    MSDA_PICK(true, false)
+    MSDA_PICK(false, true)
+    MSDA_PICK(false, false)
+#undef MSDA_PICK
+    const int64_t tiles = (int64_t)((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile);
+    void* args[] = {&g};
+    hipError_t e = hipLaunchKernel(kern, dim3((unsigned)(tiles * splits)), dim3(kThreads), args, 0,
+                                   stream);
+    if (e != hipSuccess) return MSDA_ERROR_LAUNCH;
+    if (splits > 1) {
+        const int64_t n = (int64_t)M * N;
+        int acc = accumulate ? 1 : 0;
+        void* rargs[] = {&partials, &splits, &M, &N, &C, &ldc, &bias, &acc};
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&msda_split_reduce_kernel),
+                            dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), rargs,
+                            0, stream);
+        if (e != hipSuccess) return MSDA_ERROR_LAUNCH;
+    }
+    return MSDA_SUCCESS;
+}
+
+// grad_bias[n] = sum over rows of g[r * ldg + n], through `partials`
+// (splits * N floats).
+msda_status_t msda_colsum(int R, int N, const float* g, int64_t ldg, float* out, int splits,
+                          float* partials, bool accumulate, hipStream_t stream) {
+    if (N == 0) return MSDA_SUCCESS;
+    splits = std::max(1, std::min(splits, std::max(R, 1)));
+    int rows_per = (R + splits - 1) / splits;
+    if (rows_per == 0) rows_per = 1;
+    void* args[] = {&g, &ldg, &R, &N, &rows_per, &partials};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&msda_colsum_kernel),
+                                   dim3((unsigned)((N + kThreads - 1) / kThreads), (unsigned)splits),
+                                   dim3(kThreads), args, 0, stream);
+    if (e != hipSuccess) return MSDA_ERROR_LAUNCH;
+    int one = 1, acc = accumulate ? 1 : 0;
+    const float* no_bias = nullptr;
+    int64_t ldo = N;
+    void* rargs[] = {&partials, &splits, &one, &N, &out, &ldo, &no_bias, &acc};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&msda_split_reduce_kernel),
+                        dim3((unsigned)((N + kThreads - 1) / kThreads)), dim3(kThreads), rargs, 0,
+                        stream);
+    return e == hipSuccess ? MSDA_SUCCESS : MSDA_ERROR_LAUNCH;
+}
+
+// Workspace of a linear backward: the weight gradient's split partials and
+// the bias gradient's.
+size_t msda_linear_workspace_floats(int64_t rows, int64_t in_features, int64_t out_features) {
+    const int s = splits_for(rows);
+    return (size_t)s * (size_t)in_features * (size_t)out_features + (size_t)s * (size_t)out_features;
+}
+
+int msda_linear_splits(int64_t rows) { return splits_for(rows); }
+
+namespace {
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+msda_status_t check_linear(int64_t rows, int64_t in_f, int64_t out_f) {
+    if (rows < 0 || in_f < 1 || out_f < 1) return MSDA_ERROR_INVALID_VALUE;
+    if (rows >= kMaxDim || in_f >= (1 << 20) || out_f >= (1 << 20)) return MSDA_ERROR_NOT_SUPPORTED;
+    return MSDA_SUCCESS;
+}
+}  // namespace
+
+extern "C" {
+
+msda_status_t msda_linear_forward(int64_t rows, int64_t in_features, int64_t out_features,
+                                  const float* x, const float* weight, const float* bias, float* y,
+                                  hipStream_t stream) {
+    const msda_status_t st = check_linear(rows, in_features, out_features);
+    if (st != MSDA_SUCCESS) return st;
+    if (rows == 0) return MSDA_SUCCESS;
+    if (!x || !weight || !y) return MSDA_ERROR_INVALID_VALUE;
+    if (!aligned(x, 4) || !aligned(weight, 4) || !aligned(y, 4) || !aligned(bias, 4))
+        return MSDA_ERROR_INVALID_VALUE;
+    // y[r, o] = sum_i x[r, i] W[o, i]: A = x (i-contiguous), B(i, o) = W[o, i]
+    return msda_gemm(true, true, (int)rows, (int)out_features, (int)in_features, x, in_features,
+                     weight, in_features, y, out_features, bias, false, 1, nullptr, stream);
+}
+
+msda_status_t msda_linear_backward_workspace_size(int64_t rows, int64_t in_features,
+                                                  int64_t out_features, size_t* bytes) {
+    if (!bytes) return MSDA_ERROR_INVALID_VALUE;
+    const msda_status_t st = check_linear(rows, in_features, out_features);
+    if (st != MSDA_SUCCESS) return st;
+    *bytes = msda_linear_workspace_floats(rows, in_features, out_features) * sizeof(float);
+    return MSDA_SUCCESS;
+}
+
+msda_status_t msda_linear_backward(int64_t rows, int64_t in_features, int64_t out_features,
+                                   const float* x, const float* weight, const float* grad_y,
+                                   float* grad_x, float* grad_weight, float* grad_bias,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const msda_status_t st = check_linear(rows, in_features, out_features);
+    if (st != MSDA_SUCCESS) return st;
+    if (!aligned(x, 4) || !aligned(weight, 4) || !aligned(grad_y, 4) || !aligned(grad_x, 4) ||
+        !aligned(grad_weight, 4) || !aligned(grad_bias, 4) || !aligned(workspace, 16))
+        return MSDA_ERROR_INVALID_VALUE;
+    if (rows > 0 && (!grad_y || (grad_x && !weight) || (grad_weight && !x)))
+        return MSDA_ERROR_INVALID_VALUE;
+    const bool need_ws = grad_weight || grad_bias;
+    if (need_ws) {
+        const size_t need =
+            msda_linear_workspace_floats(rows, in_features, out_features) * sizeof(float);
+        if (!workspace || workspace_bytes < need) return MSDA_ERROR_INVALID_VALUE;
+    }
+    const int R = (int)rows, I = (int)in_features, O = (int)out_features;
+    const int splits = splits_for(rows);
+    float* part_w = static_cast<float*>(workspace);
+    float* part_b = part_w ? part_w + (size_t)splits * I * O : nullptr;
+    msda_status_t s = MSDA_SUCCESS;
+    if (grad_x && R > 0) {
+        // dx[r, i] = sum_o dy[r, o] W[o, i]: A = dy (o-contiguous), B(o, i) = W[o * I + i]
+        s = msda_gemm(true, false, R, I, O, grad_y, O, weight, I, grad_x, I, nullptr, false, 1,
+                      nullptr, stream);
+        if (s != MSDA_SUCCESS) return s;
+    }
+    if (grad_weight) {
+        // dW[o, i] = sum_r dy[r, o] x[r, i]: A(o, r) = dy[r * O + o], B(r, i) = x[r * I + i]
+        if (R == 0) {
+            s = msda_gemm(false, false, O, I, 0, grad_y, O, x, I, grad_weight, I, nullptr, false, 1,
+                          nullptr, stream);   // writes zeros
+        } else {
+            s = msda_gemm(false, false, O, I, R, grad_y, O, x, I, grad_weight, I, nullptr, false,
+                          splits, part_w, stream);
+        }
+        if (s != MSDA_SUCCESS) return s;
+    }
+    if (grad_bias) s = msda_colsum(R, O, grad_y, O, grad_bias, splits, part_b, false, stream);
+    return s;
+}
+
+}  // extern "C"

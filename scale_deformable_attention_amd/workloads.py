@@ -196,3 +196,63 @@ def generate(w: Workload, batch_slice=None):
             if key in out:
                 out[key] = np.ascontiguousarray(out[key][batch_slice])
     return out
+
+
+def _dyadic(rng, shape, bound, step_log2):
+    """Uniform draws on the grid k * 2^-step_log2 within [-bound, bound], as
+    float32 (exactly representable)."""
+    n = int(round(bound * 2.0 ** step_log2))
+    return (rng.integers(-n, n + 1, size=shape).astype(np.float64) *
+            2.0 ** -step_log2).astype(np.float32)
+
+
+def generate_layer(w: Workload, offset_px=8.0):
+    """Seeded inputs and parameters of the MSDeformAttn layer around the core
+    at the workload's sizes (C = M * D channels).
+
+    Every activation, weight, bias and upstream gradient is drawn uniformly on
+    a dyadic grid (a stand-in for xavier-uniform weights and normalized
+    activations): query and input_flatten in [-1, 1] with step 1/16, weights
+    with step 2^-9 and biases with step 2^-9 or 1/16. With C <= 256 channels
+    every product and partial sum of the offset, logit, value and
+    upstream-gradient projections then stays on a grid of 2^-13 with magnitude
+    below 2^10 (at most 23 significant bits), so those projections are exact in
+    single precision whatever the summation order, and two correct
+    implementations sample at exactly the same locations.
+
+    Offset weights are scaled so that the offsets have a standard deviation of
+    about ``offset_px`` level pixels; their bias follows the pages' start-up
+    pattern rounded to 1/16 (head m points along angle 2 pi m / M, point k at
+    k + 1 pixels; DETR-to-Deformable-DETR article, section 3.2).
+    """
+    rng = np.random.default_rng(w.seed + 7919)
+    B, M, D, L, K, Nv, Nq = w.B, w.M, w.D, w.L, w.K, w.Nv, w.num_queries
+    C = M * D
+    if C > 256:
+        raise ValueError("exactness of the projections is arranged for C <= 256")
+    A = M * L * K
+    x = {}
+    x["query"] = _dyadic(rng, (B, Nq, C), 1.0, 4)
+    x["input_flatten"] = _dyadic(rng, (B, Nv, C), 1.0, 4)
+    # std of sum_i q_i w_i with q ~ U[-1,1], w ~ U[-a,a]: a * sqrt(C) / 3
+    a_off = min(4.0, offset_px * 3.0 / np.sqrt(C))
+    x["offset_weight"] = _dyadic(rng, (2 * A, C), a_off, 9)
+    th = 2.0 * np.pi * np.arange(M) / M
+    dirs = np.stack([np.cos(th), np.sin(th)], -1)
+    dirs = dirs / np.abs(dirs).max(-1, keepdims=True)
+    grid = np.repeat(dirs[:, None, None, :], L, 1).repeat(K, 2) * \
+        (np.arange(K) + 1)[None, None, :, None]
+    x["offset_bias"] = (np.round(grid.reshape(-1) * 16) / 16).astype(np.float32)
+    x["attn_weight"] = _dyadic(rng, (A, C), 0.125, 9)
+    x["attn_bias"] = _dyadic(rng, (A,), 0.25, 9)
+    x["value_weight"] = _dyadic(rng, (C, C), 0.125, 9)
+    x["value_bias"] = _dyadic(rng, (C,), 0.125, 9)
+    x["output_weight"] = _dyadic(rng, (C, C), 0.125, 9)
+    x["output_bias"] = _dyadic(rng, (C,), 0.125, 9)
+    x["grad_output"] = _dyadic(rng, (B, Nq, C), 1.0, 4)
+    ref = _reference_points(w, rng).astype(np.float32)
+    x["reference_points"] = np.ascontiguousarray(
+        np.broadcast_to(ref[None, :, None, :], (B, Nq, L, 2)))
+    x["spatial_shapes"] = np.asarray(w.shapes, np.int64).reshape(L, 2)
+    x["level_start_index"] = w.level_start_index()
+    return x

@@ -457,29 +457,27 @@ def random_fused_case(rng, B=2, M=3, D=4, shapes=((4, 6), (3, 5), (2, 2)), Nq=5,
     return value, shapes, lsi, ref, off, logits, g
 
 
-def _fused_torch_reference(value, shapes, lsi, ref, off, logits, g):
-    """The fused front-end and the core as torch float64 autograd: torch's
-    softmax for the weights, per-level grid_sample (bilinear, zeros padding,
-    align_corners=False) for the samples. The normalized location carries the
-    single-precision value the core samples at (the quotient and the sum
-    rounded to float) while its gradient flows through the exact float64
-    expression."""
+def fused_torch(V, R, O, Z, shapes, lsi, ref32, off32):
+    """The fused front-end and the core on torch float64 tensors V [B,Nv,M,D],
+    R [B,Nq,L,2], O [B,Nq,M,L,K,2], Z [B,Nq,M,L*K] (any of them may be
+    non-leaf): torch's softmax for the weights, per-level grid_sample
+    (bilinear, zeros padding, align_corners=False) for the samples. The
+    normalized location carries the single-precision value the core samples
+    at, formed from the float32 arrays ref32 and off32 (the quotient and the
+    sum rounded to float), while its gradient flows through the exact float64
+    expression of R and O. Returns out [B,Nq,M,D]."""
     import torch
     import torch.nn.functional as F
-    B, Nv, M, D = value.shape
-    _, Nq, _, L, K, _ = off.shape
-    V = torch.tensor(value, dtype=torch.float64, requires_grad=True)
-    R = torch.tensor(ref.astype(np.float64), requires_grad=True)
-    O = torch.tensor(off.astype(np.float64), requires_grad=True)
-    Z = torch.tensor(logits.astype(np.float64), requires_grad=True)
+    B, Nv, M, D = V.shape
+    _, Nq, _, L, K, _ = O.shape
     A = torch.softmax(Z, dim=-1).reshape(B, Nq, M, L, K)
     out = torch.zeros(B, Nq, M, D, dtype=torch.float64)
     for l in range(L):
         H, W = int(shapes[l][0]), int(shapes[l][1])
         norm = torch.tensor([W, H], dtype=torch.float64)
         u = R[:, :, None, l, None, :] + O[:, :, :, l] / norm          # [B, Nq, M, K, 2]
-        q32 = (off[:, :, :, l] / np.array([W, H], np.float32)).astype(np.float32)
-        u32 = (ref[:, :, None, l, None, :] + q32).astype(np.float32)
+        q32 = (off32[:, :, :, l] / np.array([W, H], np.float32)).astype(np.float32)
+        u32 = (ref32[:, :, None, l, None, :] + q32).astype(np.float32)
         x32 = np.stack([coord32(u32[..., 0], W), coord32(u32[..., 1], H)], -1)
         u_at = torch.tensor((x32.astype(np.float64) + 0.5) / np.array([W, H], np.float64))
         u_used = u + (u_at - u).detach()
@@ -489,6 +487,18 @@ def _fused_torch_reference(value, shapes, lsi, ref, off, logits, g):
                           align_corners=False)                            # [B*M, D, Nq, K]
         s = s.reshape(B, M, D, Nq, K).permute(0, 3, 1, 4, 2)              # [B, Nq, M, K, D]
         out = out + (A[:, :, :, l, :, None] * s).sum(3)
+    return out
+
+
+def _fused_torch_reference(value, shapes, lsi, ref, off, logits, g):
+    """fused_torch on leaf tensors made from numpy inputs, with the
+    gradients of sum(g * out)."""
+    import torch
+    V = torch.tensor(value, dtype=torch.float64, requires_grad=True)
+    R = torch.tensor(ref.astype(np.float64), requires_grad=True)
+    O = torch.tensor(off.astype(np.float64), requires_grad=True)
+    Z = torch.tensor(logits.astype(np.float64), requires_grad=True)
+    out = fused_torch(V, R, O, Z, shapes, lsi, ref, off)
     (out * torch.tensor(g, dtype=torch.float64)).sum().backward()
     return (out.detach().numpy(), V.grad.numpy(), R.grad.numpy(), O.grad.numpy(),
             Z.grad.numpy())

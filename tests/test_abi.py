@@ -25,7 +25,12 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == ["msda_backward", "msda_backward_fused",
                                     "msda_backward_fused_workspace_size",
                                     "msda_backward_workspace_size", "msda_check_tables",
-                                    "msda_forward", "msda_forward_fused", "msda_status_string",
+                                    "msda_forward", "msda_forward_fused",
+                                    "msda_layer_backward", "msda_layer_forward",
+                                    "msda_layer_saved_size", "msda_layer_workspace_size",
+                                    "msda_linear_backward",
+                                    "msda_linear_backward_workspace_size",
+                                    "msda_linear_forward", "msda_status_string",
                                     "msda_version"]
 
 
@@ -37,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = msda.library()
-    assert lib.msda_version() == 300
+    assert lib.msda_version() == 400
     for s in range(4):
         assert len(lib.msda_status_string(s)) > 0
     assert lib.msda_status_string(99) == b"unknown status"
@@ -198,3 +203,48 @@ def test_binding_rejects_cpu_tensors():
         msda.msda_forward_fused(v, torch.zeros(2, 2, dtype=torch.int64),
                                 torch.zeros(2, dtype=torch.int64), torch.zeros(1, 16, 2, 2),
                                 torch.zeros(1, 16, 2, 2, 2, 2), torch.zeros(1, 16, 2, 4))
+
+
+def test_linear_argument_checks():
+    lib = msda.library()
+    assert lib.msda_linear_forward(-1, 4, 4, FAKE, FAKE, None, FAKE, None) == INVALID
+    assert lib.msda_linear_forward(4, 0, 4, FAKE, FAKE, None, FAKE, None) == INVALID
+    assert lib.msda_linear_forward(4, 4, 4, None, FAKE, None, FAKE, None) == INVALID
+    assert lib.msda_linear_forward(4, 4, 4, ctypes.c_void_p(0x10002), FAKE, None, FAKE,
+                                   None) == INVALID
+    assert lib.msda_linear_forward(1 << 30, 4, 4, FAKE, FAKE, None, FAKE, None) == UNSUPPORTED
+    n = ctypes.c_size_t(0)
+    assert lib.msda_linear_backward_workspace_size(1000, 256, 256, ctypes.byref(n)) == 0
+    assert n.value >= 256 * 256 * 4
+    # weight gradient without (enough) workspace
+    assert lib.msda_linear_backward(1000, 256, 256, FAKE, FAKE, FAKE, None, FAKE, None, None, 0,
+                                    None) == INVALID
+    assert lib.msda_linear_backward(1000, 256, 256, FAKE, FAKE, FAKE, None, FAKE, None, FAKE,
+                                    n.value - 1, None) == INVALID
+
+
+def test_layer_sizes_and_checks():
+    lib = msda.library()
+    d = dims(M=2, D=8, K=2)
+    a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.msda_layer_saved_size(ctypes.byref(d), ctypes.byref(a)) == 0
+    assert lib.msda_layer_workspace_size(ctypes.byref(d), ctypes.byref(b)) == 0
+    # saved: value [B,Nv,C], offsets, logits, core
+    C, A = 16, 2 * 2 * 2
+    assert a.value >= 4 * (80 * C + 16 * (2 * A) + 16 * A + 16 * C)
+    assert b.value > 0 and a.value % 256 == 0 and b.value % 256 == 0
+    assert lib.msda_layer_saved_size(ctypes.byref(dims(D=12)), ctypes.byref(a)) == UNSUPPORTED
+    assert lib.msda_layer_saved_size(ctypes.byref(dims(K=0)), ctypes.byref(a)) == UNSUPPORTED
+    assert lib.msda_layer_saved_size(None, ctypes.byref(a)) == INVALID
+    params = _binding.MsdaLayerParams()
+    for n in _binding.LAYER_PARAMS:
+        setattr(params, n, 0x10000)
+    lib.msda_layer_saved_size(ctypes.byref(d), ctypes.byref(a))
+    args = (ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(params), FAKE)
+    # saved buffer missing, too small or misaligned
+    assert lib.msda_layer_forward(*args, None, a.value, None) == INVALID
+    assert lib.msda_layer_forward(*args, FAKE, a.value - 1, None) == INVALID
+    assert lib.msda_layer_forward(*args, ctypes.c_void_p(0x10010), a.value, None) == INVALID
+    # a weight missing
+    params.attn_weight = None
+    assert lib.msda_layer_forward(*args, FAKE, a.value, None) == INVALID
