@@ -17,8 +17,14 @@ the same workload: the kernels take the raw reference points, pixel offsets
 and attention logits and form the locations and softmax weights themselves,
 and the backward returns the offset, reference-point and logit gradients.
 
+With --frontend layer the step is the whole MSDeformAttn layer,
+msda_layer_forward + msda_layer_backward: the value, offset, logit and output
+projections on the matrix cores (fp32) around the fused core, with every
+input and parameter gradient. The roofline is then the matrix-core one of the
+dominant GEMM (fp32 dense peak 157.3 TFLOP/s).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--workload NAME] [--frontend core|fused]
+                       [--workload NAME] [--frontend core|fused|layer]
        python bench.py --calibrate-copy MIB   (a plain copy-like kernel of known size,
                                                run under the counter profiler to scale
                                                its byte counters)
@@ -36,6 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix, published
 METRIC = "sampled points/sec (B·Nq·M·L·K) fwd+bwd; achieved HBM GB/s vs peak"
 
 
@@ -153,15 +160,168 @@ def cpu_baseline(w, x, budget_s, fused=False):
                       f"double accumulation"}
 
 
+def layer_flops(w):
+    """Multiply-add flops (2 per multiply-add) of the layer's GEMMs per step:
+    forward value (Nv rows), offset + logit and output (Nq rows) projections;
+    the backward does twice as many (input and weight gradients of each)."""
+    C, A = w.M * w.D, w.M * w.L * w.K
+    Rq, Rv = w.B * w.num_queries, w.B * w.Nv
+    fwd = 2 * Rv * C * C + 2 * Rq * C * (3 * A) + 2 * Rq * C * C
+    return fwd, 2 * fwd
+
+
+def bench_layer(args, w, dev):
+    import torch
+    import scale_deformable_attention_amd as msda
+    from scale_deformable_attention_amd import workloads as wl
+    x = wl.generate_layer(w)
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in x.items()}
+    params = {k: t[k] for k in msda._binding.LAYER_PARAMS}
+    largs = (t["query"], t["input_flatten"], t["reference_points"], t["spatial_shapes"],
+             t["level_start_index"], params, w.M, w.K)
+    nsaved, nws = msda.msda_layer_sizes(t["query"], t["input_flatten"], t["spatial_shapes"],
+                                        w.M, w.K)
+    saved = torch.empty(nsaved, dtype=torch.uint8, device=dev)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(t["query"])
+    grads = {k: torch.empty_like(t[k]) for k in ("query", "input_flatten", "reference_points")}
+    grads.update({k: torch.empty_like(v) for k, v in params.items()})
+    stream = torch.cuda.current_stream(dev)
+
+    def fwd():
+        msda.msda_layer_forward(*largs, output=out, saved=saved)
+
+    def bwd():
+        msda.msda_layer_backward(*largs, saved, t["grad_output"], grads=grads, workspace=ws)
+
+    def step():
+        fwd()
+        bwd()
+
+    def timed(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(stop) / args.steps
+
+    # the pieces on their own, same stream: the layer's forward and backward;
+    # the value projection's forward GEMM (Nv rows x C x C, one launch of
+    # msda_gemm_kernel) and its weight-gradient GEMM (split over the rows,
+    # plus the split reduction)
+    C = w.M * w.D
+    Rv = w.B * w.Nv
+    X = t["input_flatten"].reshape(Rv, C)
+    Wv = params["value_weight"]
+    Y = torch.empty(Rv, C, device=dev)
+    G = t["input_flatten"].reshape(Rv, C)
+    lws = torch.empty(msda.msda_linear_backward_workspace_size(Rv, C, C), dtype=torch.uint8,
+                      device=dev)
+    kernels = {
+        "layer_forward": timed(fwd, args.steps),
+        "layer_backward": timed(bwd, args.steps),
+        "msda_gemm_kernel (forward, value projection)": timed(
+            lambda: msda.msda_linear_forward(X, Wv, params["value_bias"], output=Y), args.steps),
+        "msda_gemm_kernel+msda_split_reduce_kernel (weight gradient, value projection)": timed(
+            lambda: msda.msda_linear_backward(X, Wv, G, needs=(False, True, False),
+                                              workspace=lws), args.steps),
+    }
+    step()
+    torch.cuda.synchronize()
+    f_fwd, f_bwd = layer_flops(w)
+    gemm_flops = 2 * Rv * C * C
+    gemm_name = "msda_gemm_kernel (forward, value projection)"
+    g_ms = kernels[gemm_name]
+    achieved = gemm_flops / (g_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": w.points / (ms_per_step * 1e-3),
+        "unit": "points/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (dyadic-grid activations and weights)",
+        "config": {"workload": f"{w.name}: MSDeformAttn layer (value, offset, logit and "
+                               f"output projections around the fused core), fwd+bwd; B={w.B} "
+                               f"M={w.M} D={w.D} C={C} L={w.L} K={w.K} Nq={w.num_queries} "
+                               f"Nv={w.Nv} shapes={list(w.shapes)}",
+                   "frontend": "layer", "points_per_step": w.points, "global_batch": w.B,
+                   "parallelism": "none"},
+        "roofline": {"bound": "mfma", "kernel": gemm_name, "achieved": achieved,
+                     "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_F32_PEAK_TFLOPS, "traffic": None,
+                     "algorithmic_flops": gemm_flops, "avg_ms": g_ms, "launches": 1},
+        "step_gemm_tflops": (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12,
+        "gemm_flops_per_step": f_fwd + f_bwd,
+        "kernels_ms": kernels,
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_layer(w, x, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_layer(w, x, budget_s):
+    """The layer oracle (numpy double GEMMs + the C oracle's fused core) on
+    whole batch entries until the budget is used."""
+    from oracle import layer as olayer
+    names = {"value_weight": "w_value", "value_bias": "b_value", "offset_weight": "w_offset",
+             "offset_bias": "b_offset", "attn_weight": "w_attn", "attn_bias": "b_attn",
+             "output_weight": "w_out", "output_bias": "b_out"}
+    p = {names[k]: x[k] for k in names}
+    done, t_total, batches = 0, 0.0, 0
+    for b in range(w.B):
+        sl = slice(b, b + 1)
+        args = (p, x["query"][sl], x["input_flatten"][sl], x["reference_points"][sl],
+                x["spatial_shapes"], x["level_start_index"], w.M, w.L, w.K)
+        t0 = time.perf_counter()
+        olayer.layer_forward(*args)
+        olayer.layer_backward(*args, x["grad_output"][sl])
+        t_total += time.perf_counter() - t0
+        done += w.points // w.B
+        batches += 1
+        if t_total >= budget_s:
+            break
+    import os as _os
+    return {"value": done / t_total, "unit": "points/s",
+            "cores": len(_os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{batches} of {w.B} batch entries, layer forward + backward, {done} "
+                      f"points in {t_total:.1f} s (numpy double GEMMs on the host's BLAS "
+                      f"threads, the C oracle's core on one thread)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="encoder_train")
-    ap.add_argument("--frontend", choices=("core", "fused"), default="core",
+    ap.add_argument("--frontend", choices=("core", "fused", "layer"), default="core",
                     help="core: locations and weights given; fused: formed in the kernels "
-                         "from reference points, offsets and logits")
+                         "from reference points, offsets and logits; layer: the whole "
+                         "MSDeformAttn layer with its four projections")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline sample")
@@ -183,6 +343,8 @@ def main():
     w = wl.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     msda.library()
+    if args.frontend == "layer":
+        return bench_layer(args, w, dev)
     x = wl.generate(w)
     if w.value_dtype == "bf16":
         value = torch.from_numpy(x["value_bf16"].view(np.int16)).to(dev).view(torch.bfloat16)

@@ -9,11 +9,14 @@
 //   a_kmajor: A(m, k) = A[m * lda + k], else A[k * lda + m]
 //   b_kmajor: B(k, n) = B[n * ldb + k], else B[k * ldb + n]
 // splits > 1 splits the reduction over blocks into `partials` (splits * M * N
-// floats, device) and sums them with a second kernel.
+// floats, device) and sums them with a second kernel. With a_colsum set, the
+// same pass also writes a_colsum[m] = sum over k of A(m, k) (through
+// a_colsum_partials, splits * M floats, when splits > 1).
 msda_status_t msda_gemm(bool a_kmajor, bool b_kmajor, int M, int N, int K, const float* A,
                         int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
                         const float* bias, bool accumulate, int splits, float* partials,
-                        hipStream_t stream);
+                        hipStream_t stream, float* a_colsum = nullptr,
+                        float* a_colsum_partials = nullptr);
 
 // out[n] (+)= sum over the R rows of g[r * ldg + n], through `partials`
 // (splits * N floats, device).

@@ -118,6 +118,18 @@ bool params_ok(const msda_layer_params_t* w) {
            aligned_to(w->attn_bias, 4) && aligned_to(w->output_bias, 4);
 }
 
+// Weight gradient dW[o, i] = sum_r dy[r, o] x[r, i] with the bias gradient
+// (sum_r dy[r, o]) from the same pass; either may be null.
+msda_status_t weight_and_bias(int O, int I, int R, const float* dy, const float* x, float* gw,
+                              float* gb, int splits, float* part, float* part_b,
+                              hipStream_t stream) {
+    if (gw)
+        return msda_gemm(false, false, O, I, R, dy, O, x, I, gw, I, nullptr, false,
+                         R == 0 ? 1 : splits, part, stream, gb, part_b);
+    if (gb) return msda_colsum(R, O, dy, O, gb, splits, part_b, false, stream);
+    return MSDA_SUCCESS;
+}
+
 template <typename T>
 T* at(void* base, size_t off) {
     return reinterpret_cast<T*>(static_cast<char*>(base) + off);
@@ -241,15 +253,9 @@ msda_status_t msda_layer_backward(const msda_dims_t* dims, const float* query,
     r = msda_gemm(true, false, Rq, C, C, grad_output, C, w.output_weight, C, dcore, C, nullptr,
                   false, 1, nullptr, stream);
     if (r != MSDA_SUCCESS) return r;
-    if (g.output_weight) {
-        r = msda_gemm(false, false, C, C, Rq, grad_output, C, core, C, g.output_weight, C, nullptr,
-                      false, sq, part, stream);
-        if (r != MSDA_SUCCESS) return r;
-    }
-    if (g.output_bias) {
-        r = msda_colsum(Rq, C, grad_output, C, g.output_bias, sq, part_bq, false, stream);
-        if (r != MSDA_SUCCESS) return r;
-    }
+    r = weight_and_bias(C, C, Rq, grad_output, core, g.output_weight, g.output_bias, sq, part,
+                        part_bq, stream);
+    if (r != MSDA_SUCCESS) return r;
 
     // the fused core: value, reference-point, offset and logit gradients
     const bool want_value = grad_input_flatten || g.value_weight || g.value_bias;
@@ -270,24 +276,12 @@ msda_status_t msda_layer_backward(const msda_dims_t* dims, const float* query,
                       true, 1, nullptr, stream);
         if (r != MSDA_SUCCESS) return r;
     }
-    if (g.offset_weight) {
-        r = msda_gemm(false, false, P, C, Rq, doff, P, query, C, g.offset_weight, C, nullptr, false,
-                      sq, part, stream);
-        if (r != MSDA_SUCCESS) return r;
-    }
-    if (g.offset_bias) {
-        r = msda_colsum(Rq, P, doff, P, g.offset_bias, sq, part_bq, false, stream);
-        if (r != MSDA_SUCCESS) return r;
-    }
-    if (g.attn_weight) {
-        r = msda_gemm(false, false, A, C, Rq, dlogits, A, query, C, g.attn_weight, C, nullptr, false,
-                      sq, part, stream);
-        if (r != MSDA_SUCCESS) return r;
-    }
-    if (g.attn_bias) {
-        r = msda_colsum(Rq, A, dlogits, A, g.attn_bias, sq, part_bq, false, stream);
-        if (r != MSDA_SUCCESS) return r;
-    }
+    r = weight_and_bias(P, C, Rq, doff, query, g.offset_weight, g.offset_bias, sq, part, part_bq,
+                        stream);
+    if (r != MSDA_SUCCESS) return r;
+    r = weight_and_bias(A, C, Rq, dlogits, query, g.attn_weight, g.attn_bias, sq, part, part_bq,
+                        stream);
+    if (r != MSDA_SUCCESS) return r;
 
     // value projection: dinput = dvalue W_v; dW_v = dvalue^T input; db_v = sum dvalue
     if (grad_input_flatten && Rv > 0) {
@@ -295,16 +289,8 @@ msda_status_t msda_layer_backward(const msda_dims_t* dims, const float* query,
                       nullptr, false, 1, nullptr, stream);
         if (r != MSDA_SUCCESS) return r;
     }
-    if (g.value_weight) {
-        r = msda_gemm(false, false, C, C, Rv, dvalue, C, input_flatten, C, g.value_weight, C,
-                      nullptr, false, sv, part, stream);
-        if (r != MSDA_SUCCESS) return r;
-    }
-    if (g.value_bias) {
-        r = msda_colsum(Rv, C, dvalue, C, g.value_bias, sv, part_bv, false, stream);
-        if (r != MSDA_SUCCESS) return r;
-    }
-    return MSDA_SUCCESS;
+    return weight_and_bias(C, C, Rv, dvalue, input_flatten, g.value_weight, g.value_bias, sv, part,
+                           part_bv, stream);
 }
 
 }  // extern "C"

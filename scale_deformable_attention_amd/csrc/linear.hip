@@ -46,6 +46,7 @@ struct GemmArgs {
     int splits;
     int accumulate;        // C += result (splits == 1 only)
     int64_t split_stride;  // elements between consecutive splits' partial outputs
+    float* asum;           // if set: sum over this split's k of A(m, k), at asum[z * M + m]
 };
 
 // Blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous
@@ -149,6 +150,11 @@ __global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmArgs g) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
+    // column sums of A (a bias gradient rides along with its weight gradient):
+    // the blocks of column tile 0, one thread per row of the tile
+    const bool do_asum = g.asum != nullptr && n0 == 0 && tid < kTile;
+    float asum = 0.0f;
+
     int buf = 0;
     if (kbeg < kend) {
         load(g.A, g.lda, kAK, g.M, m0, kbeg, ra);
@@ -175,6 +181,10 @@ __global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmArgs g) {
             acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
             acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
         }
+        if (do_asum) {
+#pragma unroll
+            for (int s = 0; s < kBK; ++s) asum += Ab[s * kLdsRow + tid];
+        }
         if (more) {
             store(As[buf ^ 1], kAK, ra);
             store(Bs[buf ^ 1], kBKm, rb);
@@ -182,6 +192,8 @@ __global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmArgs g) {
         __syncthreads();
         buf ^= 1;
     }
+
+    if (do_asum && m0 + tid < g.M) g.asum[(int64_t)z * g.M + m0 + tid] = asum;
 
     // ---- epilogue: 32x32 accumulator register r of lane (li, lk) holds
     // row 8 * (r / 4) + 4 * lk + r % 4, column li
@@ -208,34 +220,61 @@ __global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmArgs g) {
 }
 
 // out[m, n] (row stride ldo) = sum over s < splits of part[s * M * N + m * N + n]
-// (+ bias[n]) (+ out[m, n] if accumulate). One thread per element.
+// (+ bias[n]) (+ out[m, n] if accumulate). A block takes 64 consecutive
+// elements; its four waves take every fourth split each (four independent
+// partial sums per thread) and combine through LDS, in a fixed order.
 __global__ __launch_bounds__(kThreads) void msda_split_reduce_kernel(const float* part, int splits,
                                                                      int M, int N, float* out,
                                                                      int64_t ldo, const float* bias,
                                                                      int accumulate) {
-    const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    __shared__ float red[4][64];
     const int64_t MN = (int64_t)M * N;
-    if (e >= MN) return;
-    float s = 0.0f;
-    for (int i = 0; i < splits; ++i) s += part[(int64_t)i * MN + e];
+    const int c = threadIdx.x & 63, j = threadIdx.x >> 6;
+    const int64_t e = (int64_t)blockIdx.x * 64 + c;
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+    if (e < MN) {
+        int s = j;
+        for (; s + 12 < splits; s += 16) {
+            a0 += part[(int64_t)s * MN + e];
+            a1 += part[(int64_t)(s + 4) * MN + e];
+            a2 += part[(int64_t)(s + 8) * MN + e];
+            a3 += part[(int64_t)(s + 12) * MN + e];
+        }
+        for (; s < splits; s += 4) a0 += part[(int64_t)s * MN + e];
+    }
+    red[j][c] = (a0 + a1) + (a2 + a3);
+    __syncthreads();
+    if (j != 0 || e >= MN) return;
+    float v = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
     const int m = (int)(e / N), n = (int)(e - (int64_t)m * N);
-    if (bias) s += bias[n];
+    if (bias) v += bias[n];
     float* dst = out + (int64_t)m * ldo + n;
-    if (accumulate) s += *dst;
-    *dst = s;
+    if (accumulate) v += *dst;
+    *dst = v;
 }
 
-// part[s * N + n] = sum of g[r * ldg + n] over rows r of split s
-// (rows [s * rows_per, min(R, (s + 1) * rows_per))).
+// part[s * N + n] = sum of g[r * ldg + n] over the rows of chunk s
+// ([s * rows_per, min(R, (s + 1) * rows_per))): 64 columns per block, its four
+// waves taking every fourth row, combined through LDS.
 __global__ __launch_bounds__(kThreads) void msda_colsum_kernel(const float* g, int64_t ldg, int R,
                                                                int N, int rows_per, float* part) {
+    __shared__ float red[4][64];
     const int s = blockIdx.y;
-    const int n = blockIdx.x * kThreads + threadIdx.x;
-    if (n >= N) return;
+    const int c = threadIdx.x & 63, j = threadIdx.x >> 6;
+    const int n = blockIdx.x * 64 + c;
     const int r0 = s * rows_per, r1 = min(R, r0 + rows_per);
-    float acc = 0.0f;
-    for (int r = r0; r < r1; ++r) acc += g[(int64_t)r * ldg + n];
-    part[(int64_t)s * N + n] = acc;
+    float a0 = 0.0f, a1 = 0.0f;
+    if (n < N) {
+        int r = r0 + j;
+        for (; r + 4 < r1; r += 8) {
+            a0 += g[(int64_t)r * ldg + n];
+            a1 += g[(int64_t)(r + 4) * ldg + n];
+        }
+        for (; r < r1; r += 4) a0 += g[(int64_t)r * ldg + n];
+    }
+    red[j][c] = a0 + a1;
+    __syncthreads();
+    if (j == 0 && n < N) part[(int64_t)s * N + n] = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -254,10 +293,23 @@ int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 // as described at GemmArgs; a_kmajor / b_kmajor pick the operand strides.
 // With splits > 1 the reduction is split over blocks into `partials`
 // (splits * M * N floats) and summed by a second kernel.
+namespace {
+msda_status_t launch_reduce(const float* part, int splits, int M, int N, float* out, int64_t ldo,
+                            const float* bias, bool accumulate, hipStream_t stream) {
+    const int64_t n = (int64_t)M * N;
+    int acc = accumulate ? 1 : 0;
+    void* rargs[] = {&part, &splits, &M, &N, &out, &ldo, &bias, &acc};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&msda_split_reduce_kernel),
+                                         dim3((unsigned)((n + 63) / 64)), dim3(kThreads), rargs, 0,
+                                         stream);
+    return e == hipSuccess ? MSDA_SUCCESS : MSDA_ERROR_LAUNCH;
+}
+}  // namespace
+
 msda_status_t msda_gemm(bool a_kmajor, bool b_kmajor, int M, int N, int K, const float* A,
                         int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
                         const float* bias, bool accumulate, int splits, float* partials,
-                        hipStream_t stream) {
+                        hipStream_t stream, float* a_colsum, float* a_colsum_partials) {
     if (M == 0 || N == 0) return MSDA_SUCCESS;
     GemmArgs g;
     g.A = A;
@@ -279,11 +331,13 @@ msda_status_t msda_gemm(bool a_kmajor, bool b_kmajor, int M, int N, int K, const
         g.bias = nullptr;
         g.accumulate = 0;
         g.split_stride = (int64_t)M * N;
+        g.asum = a_colsum ? a_colsum_partials : nullptr;
     } else {
         g.C = C;
         g.ldc = ldc;
         g.accumulate = accumulate ? 1 : 0;
         g.split_stride = 0;
+        g.asum = a_colsum;
     }
     // vector loads: the contiguous dimension of each operand a multiple of 4
     // floats, strides too, and 16-byte aligned bases
@@ -306,13 +360,13 @@ msda_status_t msda_gemm(bool a_kmajor, bool b_kmajor, int M, int N, int K, const
                                    stream);
     if (e != hipSuccess) return MSDA_ERROR_LAUNCH;
     if (splits > 1) {
-        const int64_t n = (int64_t)M * N;
-        int acc = accumulate ? 1 : 0;
-        void* rargs[] = {&partials, &splits, &M, &N, &C, &ldc, &bias, &acc};
-        e = hipLaunchKernel(reinterpret_cast<const void*>(&msda_split_reduce_kernel),
-                            dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), rargs,
-                            0, stream);
-        if (e != hipSuccess) return MSDA_ERROR_LAUNCH;
+        msda_status_t st = launch_reduce(partials, splits, M, N, C, ldc, bias, accumulate, stream);
+        if (st != MSDA_SUCCESS) return st;
+        if (a_colsum) {
+            st = launch_reduce(a_colsum_partials, splits, 1, M, a_colsum, M, nullptr, false,
+                               stream);
+            if (st != MSDA_SUCCESS) return st;
+        }
     }
     return MSDA_SUCCESS;
 }
@@ -326,18 +380,11 @@ msda_status_t msda_colsum(int R, int N, const float* g, int64_t ldg, float* out,
     int rows_per = (R + splits - 1) / splits;
     if (rows_per == 0) rows_per = 1;
     void* args[] = {&g, &ldg, &R, &N, &rows_per, &partials};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&msda_colsum_kernel),
-                                   dim3((unsigned)((N + kThreads - 1) / kThreads), (unsigned)splits),
-                                   dim3(kThreads), args, 0, stream);
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&msda_colsum_kernel),
+                                         dim3((unsigned)((N + 63) / 64), (unsigned)splits),
+                                         dim3(kThreads), args, 0, stream);
     if (e != hipSuccess) return MSDA_ERROR_LAUNCH;
-    int one = 1, acc = accumulate ? 1 : 0;
-    const float* no_bias = nullptr;
-    int64_t ldo = N;
-    void* rargs[] = {&partials, &splits, &one, &N, &out, &ldo, &no_bias, &acc};
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&msda_split_reduce_kernel),
-                        dim3((unsigned)((N + kThreads - 1) / kThreads)), dim3(kThreads), rargs, 0,
-                        stream);
-    return e == hipSuccess ? MSDA_SUCCESS : MSDA_ERROR_LAUNCH;
+    return launch_reduce(partials, splits, 1, N, out, N, nullptr, accumulate, stream);
 }
 
 // Workspace of a linear backward: the weight gradient's split partials and
@@ -413,15 +460,11 @@ msda_status_t msda_linear_backward(int64_t rows, int64_t in_features, int64_t ou
         if (s != MSDA_SUCCESS) return s;
     }
     if (grad_weight) {
-        // dW[o, i] = sum_r dy[r, o] x[r, i]: A(o, r) = dy[r * O + o], B(r, i) = x[r * I + i]
-        if (R == 0) {
-            s = msda_gemm(false, false, O, I, 0, grad_y, O, x, I, grad_weight, I, nullptr, false, 1,
-                          nullptr, stream);   // writes zeros
-        } else {
-            s = msda_gemm(false, false, O, I, R, grad_y, O, x, I, grad_weight, I, nullptr, false,
-                          splits, part_w, stream);
-        }
-        if (s != MSDA_SUCCESS) return s;
+        // dW[o, i] = sum_r dy[r, o] x[r, i]: A(o, r) = dy[r * O + o], B(r, i) = x[r * I + i];
+        // grad_bias, the sum of A over r, comes out of the same pass
+        s = msda_gemm(false, false, O, I, R, grad_y, O, x, I, grad_weight, I, nullptr, false,
+                      R == 0 ? 1 : splits, part_w, stream, grad_bias, part_b);
+        return s;
     }
     if (grad_bias) s = msda_colsum(R, O, grad_y, O, grad_bias, splits, part_b, false, stream);
     return s;
