@@ -28,9 +28,19 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;          // 4 waves
 constexpr int kTile = 128;             // block tile, rows and columns
-constexpr int kBK = 16;                // reduction slice per iteration
+#ifndef MSDA_GEMM_BK
+#define MSDA_GEMM_BK 16
+#endif
+constexpr int kBK = MSDA_GEMM_BK;      // reduction slice per iteration
+constexpr int kPerThread = kTile * kBK / 256;   // staged elements of an operand per thread
+constexpr int kHalf = kBK / 2;         // reduction steps of one MFMA lane half per slice
+constexpr int kRowK = kBK + 4;         // padded LDS row of the [row][k] layout (floats)
+#ifndef MSDA_GEMM_KLAYOUT
+#define MSDA_GEMM_KLAYOUT 1
+#endif
 constexpr int kLdsRow = kTile + 4;     // padded LDS row (floats)
 constexpr int kSplitMax = 256;         // reduction splits of a weight gradient at most
+constexpr int kLdsFloats = (kTile * kRowK > kBK * kLdsRow) ? kTile * kRowK : kBK * kLdsRow;
 
 // C = A B (+ bias) (+ C) with A(m, k), B(k, n) read through strides:
 //   kAK: A(m, k) = A[m * lda + k]   else A[k * lda + m]
@@ -60,8 +70,13 @@ __device__ inline int xcd_work_item() {
 
 template <bool kAK, bool kBKm, bool kVec>
 __global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmArgs g) {
-    __shared__ float As[2][kBK * kLdsRow];
-    __shared__ float Bs[2][kBK * kLdsRow];
+    // LDS layout of a staged operand: [row][k] (k contiguous) when its global
+    // rows are k-contiguous and loaded as float4s -- stored as loaded, read
+    // back as float4s; otherwise [k][row]
+    constexpr bool kAmk = MSDA_GEMM_KLAYOUT && kAK && kVec;
+    constexpr bool kBmk = MSDA_GEMM_KLAYOUT && kBKm && kVec;
+    __shared__ float As[2][kLdsFloats];
+    __shared__ float Bs[2][kLdsFloats];
     const int tid = threadIdx.x;
     const int mt = (g.M + kTile - 1) / kTile, nt = (g.N + kTile - 1) / kTile;
     const int work = xcd_work_item();
@@ -71,21 +86,21 @@ __global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmArgs g) {
     const int kbeg = z * g.k_split;
     const int kend = min(g.K, kbeg + g.k_split);
 
-    // ---- staging: 2048 elements of each operand per slice, 8 per thread
-    float ra[8], rb[8];
+    // ---- staging: kTile * kBK elements of each operand per slice
+    float ra[kPerThread], rb[kPerThread];
     auto load = [&](const float* P, int64_t ld, bool kmajor, int lim_mn, int base_mn, int k0,
                     float* r) {
         if constexpr (kVec) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < kPerThread / 4; ++i) {
                 const int idx = tid + kThreads * i;
                 int mn, k;
                 if (kmajor) {
-                    mn = idx >> 2;
-                    k = (idx & 3) * 4;
+                    mn = idx / (kBK / 4);
+                    k = (idx % (kBK / 4)) * 4;
                 } else {
-                    k = idx >> 5;
-                    mn = (idx & 31) * 4;
+                    k = idx / (kTile / 4);
+                    mn = (idx % (kTile / 4)) * 4;
                 }
                 const bool ok = base_mn + mn < lim_mn && k0 + k < kend;
                 float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -101,10 +116,10 @@ __global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmArgs g) {
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < kPerThread; ++i) {
                 const int idx = tid + kThreads * i;
-                const int mn = kmajor ? idx >> 4 : idx & (kTile - 1);
-                const int k = kmajor ? idx & (kBK - 1) : idx >> 7;
+                const int mn = kmajor ? idx / kBK : idx % kTile;
+                const int k = kmajor ? idx % kBK : idx / kTile;
                 const bool ok = base_mn + mn < lim_mn && k0 + k < kend;
                 r[i] = ok ? (kmajor ? P[(int64_t)(base_mn + mn) * ld + (k0 + k)]
                                     : P[(int64_t)(k0 + k) * ld + (base_mn + mn)])
@@ -112,27 +127,32 @@ __global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmArgs g) {
             }
         }
     };
-    auto store = [&](float* S, bool kmajor, const float* r) {
+    auto store = [&](float* S, bool kmajor, bool mk, const float* r) {
         if constexpr (kVec) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < kPerThread / 4; ++i) {
                 const int idx = tid + kThreads * i;
                 if (kmajor) {
-                    const int mn = idx >> 2, k = (idx & 3) * 4;
+                    const int mn = idx / (kBK / 4), k = (idx % (kBK / 4)) * 4;
+                    if (mk) {
+                        *reinterpret_cast<float4*>(&S[mn * kRowK + k]) =
+                            make_float4(r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]);
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) S[(k + e) * kLdsRow + mn] = r[4 * i + e];
+                        for (int e = 0; e < 4; ++e) S[(k + e) * kLdsRow + mn] = r[4 * i + e];
+                    }
                 } else {
-                    const int k = idx >> 5, mn = (idx & 31) * 4;
+                    const int k = idx / (kTile / 4), mn = (idx % (kTile / 4)) * 4;
                     *reinterpret_cast<float4*>(&S[k * kLdsRow + mn]) =
                         make_float4(r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]);
                 }
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < kPerThread; ++i) {
                 const int idx = tid + kThreads * i;
-                const int mn = kmajor ? idx >> 4 : idx & (kTile - 1);
-                const int k = kmajor ? idx & (kBK - 1) : idx >> 7;
+                const int mn = kmajor ? idx / kBK : idx % kTile;
+                const int k = kmajor ? idx % kBK : idx / kTile;
                 S[k * kLdsRow + mn] = r[i];
             }
         }
@@ -159,8 +179,8 @@ __global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmArgs g) {
     if (kbeg < kend) {
         load(g.A, g.lda, kAK, g.M, m0, kbeg, ra);
         load(g.B, g.ldb, kBKm, g.N, n0, kbeg, rb);
-        store(As[0], kAK, ra);
-        store(Bs[0], kBKm, rb);
+        store(As[0], kAK, kAmk, ra);
+        store(Bs[0], kBKm, kBmk, rb);
     }
     __syncthreads();
     for (int k0 = kbeg; k0 < kend; k0 += kBK) {
@@ -171,23 +191,44 @@ __global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmArgs g) {
         }
         const float* Ab = As[buf];
         const float* Bb = Bs[buf];
+        // MFMA step s sums over k = lk * kHalf + s (the lane halves take the
+        // slice's two halves): a lane's operands of a slice are then kHalf
+        // consecutive k of one row
+        float a0v[kHalf], a1v[kHalf], b0v[kHalf], b1v[kHalf];
+        auto frag = [&](const float* S, bool mk, int row, float* v) {
+            if (mk) {
 #pragma unroll
-        for (int s = 0; s < kBK; s += 2) {
-            const float* Ar = Ab + (s + lk) * kLdsRow + wm + li;
-            const float* Br = Bb + (s + lk) * kLdsRow + wn + li;
-            const float a0 = Ar[0], a1 = Ar[32], b0 = Br[0], b1 = Br[32];
-            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+                for (int q = 0; q < kHalf; q += 4) {
+                    const float4 f = *reinterpret_cast<const float4*>(&S[row * kRowK + lk * kHalf + q]);
+                    v[q] = f.x;
+                    v[q + 1] = f.y;
+                    v[q + 2] = f.z;
+                    v[q + 3] = f.w;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < kHalf; ++q) v[q] = S[(lk * kHalf + q) * kLdsRow + row];
+            }
+        };
+        frag(Ab, kAmk, wm + li, a0v);
+        frag(Ab, kAmk, wm + 32 + li, a1v);
+        frag(Bb, kBmk, wn + li, b0v);
+        frag(Bb, kBmk, wn + 32 + li, b1v);
+#pragma unroll
+        for (int q = 0; q < kHalf; ++q) {
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0v[q], b0v[q], acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0v[q], b1v[q], acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1v[q], b0v[q], acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1v[q], b1v[q], acc[1][1], 0, 0, 0);
         }
         if (do_asum) {
 #pragma unroll
-            for (int s = 0; s < kBK; ++s) asum += Ab[s * kLdsRow + tid];
+            for (int q = 0; q < kBK; ++q)
+                asum += kAmk ? Ab[tid * kRowK + q] : Ab[q * kLdsRow + tid];
         }
         if (more) {
-            store(As[buf ^ 1], kAK, ra);
-            store(Bs[buf ^ 1], kBKm, rb);
+            store(As[buf ^ 1], kAK, kAmk, ra);
+            store(Bs[buf ^ 1], kBKm, kBmk, rb);
         }
         __syncthreads();
         buf ^= 1;
