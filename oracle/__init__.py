@@ -191,3 +191,69 @@ def backward_fused(value, spatial_shapes, level_start_index, reference_points, s
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return tuple(outs) + (tuple(abss) if with_abs else ())
+
+
+# ----------------------------------------------------------------------------- DCNv3
+def _bind_dcn(lib):
+    if getattr(lib, "_dcn_bound", False):
+        return lib
+    lib.msda_oracle_dcn_forward.restype = ctypes.c_int
+    lib.msda_oracle_dcn_forward.argtypes = [_i64] * 15 + [_pd, _pf, _pd, _pd, _pd]
+    lib.msda_oracle_dcn_backward.restype = ctypes.c_int
+    lib.msda_oracle_dcn_backward.argtypes = [_i64] * 15 + [_pd, _pf, _pd, _pd] + [_pd] * 6
+    lib._dcn_bound = True
+    return lib
+
+
+def _prep_dcn(inp, offset, mask, kernel, stride, pad, dilation):
+    inp = np.ascontiguousarray(inp, dtype=np.float64)
+    off = np.ascontiguousarray(offset, dtype=np.float32)
+    m = np.ascontiguousarray(mask, dtype=np.float64)
+    B, H, W, G, D = inp.shape
+    kh, kw = kernel
+    if off.ndim != 6 or off.shape[0] != B or off.shape[3] != G or off.shape[4] != kh * kw \
+            or off.shape[5] != 2:
+        raise ValueError("offset must be [B, H_out, W_out, G, K, 2]")
+    Ho, Wo = off.shape[1], off.shape[2]
+    if m.shape != off.shape[:5]:
+        raise ValueError("mask must be [B, H_out, W_out, G, K]")
+    dims = (B, H, W, G, D, kh, kw, stride[0], stride[1], pad[0], pad[1], dilation[0],
+            dilation[1], Ho, Wo)
+    return dims, inp, off, m
+
+
+def dcn_forward(inp, offset, mask, kernel, stride=(1, 1), pad=(0, 0), dilation=(1, 1),
+                with_abs=False, lib=None):
+    """DCNv3 aggregation in double (see msda_oracle.c): input [B,H,W,G,D],
+    offset [B,Ho,Wo,G,K,2] pixels (x, y), mask [B,Ho,Wo,G,K] -> out
+    [B,Ho,Wo,G,D] (and the absolute term sums with ``with_abs``)."""
+    dims, inp, off, m = _prep_dcn(inp, offset, mask, kernel, stride, pad, dilation)
+    B, H, W, G, D = inp.shape
+    Ho, Wo = dims[13], dims[14]
+    out = np.empty((B, Ho, Wo, G, D))
+    out_abs = np.empty_like(out) if with_abs else None
+    rc = _bind_dcn(lib or library()).msda_oracle_dcn_forward(
+        *dims, _ptr(inp, ctypes.c_double), _ptr(off, ctypes.c_float), _ptr(m, ctypes.c_double),
+        _ptr(out, ctypes.c_double), _ptr(out_abs, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return (out, out_abs) if with_abs else out
+
+
+def dcn_backward(inp, offset, mask, grad_output, kernel, stride=(1, 1), pad=(0, 0),
+                 dilation=(1, 1), with_abs=False, lib=None):
+    """Gradients of dcn_forward: (grad_input, grad_offset, grad_mask), then
+    their absolute term sums with ``with_abs``."""
+    dims, inp, off, m = _prep_dcn(inp, offset, mask, kernel, stride, pad, dilation)
+    B, H, W, G, D = inp.shape
+    Ho, Wo = dims[13], dims[14]
+    g = np.ascontiguousarray(grad_output, dtype=np.float64).reshape(B, Ho, Wo, G, D)
+    outs = [np.empty(inp.shape), np.empty(off.shape), np.empty(m.shape)]
+    abss = [np.empty_like(o) for o in outs] if with_abs else [None] * 3
+    rc = _bind_dcn(lib or library()).msda_oracle_dcn_backward(
+        *dims, _ptr(inp, ctypes.c_double), _ptr(off, ctypes.c_float), _ptr(m, ctypes.c_double),
+        _ptr(g, ctypes.c_double), *[_ptr(o, ctypes.c_double) for o in outs],
+        *[_ptr(a, ctypes.c_double) for a in abss])
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return tuple(outs) + (tuple(abss) if with_abs else ())

@@ -394,4 +394,147 @@ int msda_oracle_backward_fused(int64_t B, int64_t Nv, int64_t M, int64_t D, int6
 }
 
 /* Version tag so a test can tell a stale build from the current source. */
-int msda_oracle_version(void) { return 2; }
+/*
+ * Grouped single-level deformable aggregation (DCNv3, deformable-attention
+ * practice guide section 4.2):
+ *
+ *   y(p0) = sum_g sum_k w_g m_gk x_g(p0 + p_k + dp_gk)
+ *
+ * The oracle computes the aggregation before the shared projection w_g (a
+ * linear layer): for every output pixel p0 = (ho, wo), group g, grid point k,
+ *
+ *   out[b,ho,wo,g,:] = sum_k mask[b,ho,wo,g,k] * x_g(P)
+ *   P = (wo*stride_w - pad_w + kx*dil_w + off_x,  ho*stride_h - pad_h + ky*dil_h + off_y)
+ *
+ * with k = ky * kernel_w + kx (p_k the dilated kernel grid; stride and
+ * padding as in a convolution), P in input pixels (pixel (i, j) at x = j,
+ * y = i), x_g bilinear over the four surrounding pixels with zero outside
+ * the H x W input (the same interpolation as the core), and the modulation
+ * scalars used as given. The page leaves the precision of P open; both sides
+ * form it in single precision: the integer grid coordinate converted to
+ * float (exact) plus the offset, one correctly rounded float addition.
+ *
+ * Layouts: input [B, H, W, G, D] (= [B, H*W, G, D]); offset
+ * [B, Ho, Wo, G, K, 2] (x, y); mask [B, Ho, Wo, G, K]; out [B, Ho, Wo, G, D].
+ * Backward: grad_input[b, pixel, g, :] += m * w_c * g; grad_mask = sum_d g .
+ * sample; grad_off = m * sum_d g . d sample / d (x, y) (dP / d off = 1).
+ */
+static int dcn_check(int64_t B, int64_t H, int64_t W, int64_t G, int64_t D, int64_t kh,
+                     int64_t kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh,
+                     int64_t dw, int64_t Ho, int64_t Wo) {
+    if (B < 0 || H < 1 || W < 1 || G < 1 || D < 1 || kh < 1 || kw < 1 || sh < 1 || sw < 1 ||
+        ph < 0 || pw < 0 || dh < 1 || dw < 1 || Ho < 0 || Wo < 0)
+        return ORACLE_BAD_ARGS;
+    return ORACLE_OK;
+}
+
+static void dcn_point(int64_t ho, int64_t wo, int64_t k, int64_t kw, int64_t sh, int64_t sw,
+                      int64_t ph, int64_t pw, int64_t dh, int64_t dw, const float *off,
+                      double *x, double *y) {
+    const int64_t ky = k / kw, kx = k % kw;
+    const float gx = (float)(wo * sw - pw + kx * dw);
+    const float gy = (float)(ho * sh - ph + ky * dh);
+    *x = (double)(float)(gx + off[0]);
+    *y = (double)(float)(gy + off[1]);
+}
+
+int msda_oracle_dcn_forward(int64_t B, int64_t H, int64_t W, int64_t G, int64_t D, int64_t kh,
+                            int64_t kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw,
+                            int64_t dh, int64_t dw, int64_t Ho, int64_t Wo, const double *input,
+                            const float *offset, const double *mask, double *out,
+                            double *out_abs) {
+    if (dcn_check(B, H, W, G, D, kh, kw, sh, sw, ph, pw, dh, dw, Ho, Wo) != ORACLE_OK)
+        return ORACLE_BAD_ARGS;
+    const int64_t K = kh * kw, Nv = H * W;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t ho = 0; ho < Ho; ++ho)
+            for (int64_t wo = 0; wo < Wo; ++wo)
+                for (int64_t g = 0; g < G; ++g) {
+                    const int64_t t = ((b * Ho + ho) * Wo + wo) * G + g;
+                    double *o = out + t * D;
+                    double *oa = out_abs ? out_abs + t * D : NULL;
+                    for (int64_t d = 0; d < D; ++d) {
+                        o[d] = 0.0;
+                        if (oa) oa[d] = 0.0;
+                    }
+                    for (int64_t k = 0; k < K; ++k) {
+                        const int64_t p = t * K + k;
+                        double x, y;
+                        corner_t c[4];
+                        dcn_point(ho, wo, k, kw, sh, sw, ph, pw, dh, dw, offset + 2 * p, &x, &y);
+                        bilinear_corners(x, y, H, W, 0, c);
+                        const double m = mask[p];
+                        for (int i = 0; i < 4; ++i) {
+                            if (!c[i].valid) continue;
+                            const double *v = input + ((b * Nv + c[i].row) * G + g) * D;
+                            for (int64_t d = 0; d < D; ++d) {
+                                const double term = m * c[i].w * v[d];
+                                o[d] += term;
+                                if (oa) oa[d] += fabs(term);
+                            }
+                        }
+                    }
+                }
+    return ORACLE_OK;
+}
+
+int msda_oracle_dcn_backward(int64_t B, int64_t H, int64_t W, int64_t G, int64_t D, int64_t kh,
+                             int64_t kw, int64_t sh, int64_t sw, int64_t ph, int64_t pw,
+                             int64_t dh, int64_t dw, int64_t Ho, int64_t Wo, const double *input,
+                             const float *offset, const double *mask, const double *grad_out,
+                             double *grad_input, double *grad_offset, double *grad_mask,
+                             double *grad_input_abs, double *grad_offset_abs,
+                             double *grad_mask_abs) {
+    if (dcn_check(B, H, W, G, D, kh, kw, sh, sw, ph, pw, dh, dw, Ho, Wo) != ORACLE_OK)
+        return ORACLE_BAD_ARGS;
+    const int64_t K = kh * kw, Nv = H * W;
+    const size_t nin = (size_t)(B * Nv * G * D);
+    if (grad_input) memset(grad_input, 0, nin * sizeof(double));
+    if (grad_input_abs) memset(grad_input_abs, 0, nin * sizeof(double));
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t ho = 0; ho < Ho; ++ho)
+            for (int64_t wo = 0; wo < Wo; ++wo)
+                for (int64_t g = 0; g < G; ++g) {
+                    const int64_t t = ((b * Ho + ho) * Wo + wo) * G + g;
+                    const double *gr = grad_out + t * D;
+                    for (int64_t k = 0; k < K; ++k) {
+                        const int64_t p = t * K + k;
+                        double x, y;
+                        corner_t c[4];
+                        dcn_point(ho, wo, k, kw, sh, sw, ph, pw, dh, dw, offset + 2 * p, &x, &y);
+                        bilinear_corners(x, y, H, W, 0, c);
+                        const double m = mask[p];
+                        double gm = 0.0, gm_abs = 0.0, gx = 0.0, gx_abs = 0.0, gy = 0.0,
+                               gy_abs = 0.0;
+                        for (int i = 0; i < 4; ++i) {
+                            if (!c[i].valid) continue;
+                            const size_t base = (size_t)(((b * Nv + c[i].row) * G + g) * D);
+                            for (int64_t d = 0; d < D; ++d) {
+                                const double v = input[base + d];
+                                gm += gr[d] * c[i].w * v;
+                                gm_abs += fabs(gr[d] * c[i].w * v);
+                                gx += gr[d] * c[i].dw_dx * v;
+                                gx_abs += fabs(gr[d] * c[i].dw_dx * v);
+                                gy += gr[d] * c[i].dw_dy * v;
+                                gy_abs += fabs(gr[d] * c[i].dw_dy * v);
+                                const double term = m * c[i].w * gr[d];
+                                if (grad_input) grad_input[base + d] += term;
+                                if (grad_input_abs) grad_input_abs[base + d] += fabs(term);
+                            }
+                        }
+                        if (grad_mask) grad_mask[p] = gm;
+                        if (grad_mask_abs) grad_mask_abs[p] = gm_abs;
+                        if (grad_offset) {
+                            grad_offset[2 * p] = m * gx;
+                            grad_offset[2 * p + 1] = m * gy;
+                        }
+                        if (grad_offset_abs) {
+                            grad_offset_abs[2 * p] = fabs(m) * gx_abs;
+                            grad_offset_abs[2 * p + 1] = fabs(m) * gy_abs;
+                        }
+                    }
+                }
+    return ORACLE_OK;
+}
+
+int msda_oracle_version(void) { return 3; }

@@ -608,3 +608,158 @@ ALL_PINS = [pin_golden_hand_worked, pin_pixel_centres, pin_constant_field, pin_b
             pin_out_of_bounds, pin_linearity, pin_grid_sample, pin_brute_force,
             pin_finite_differences, pin_single_scale_resampling, pin_scatter_conservation,
             pin_permutation, pin_fused_torch, pin_fused_pixel_shift, pin_fused_finite_differences]
+
+
+# ----------------------------------------------------------------------------- DCNv3 aggregation
+def _dcn_out_size(H, W, kernel, stride, pad, dilation):
+    return ((H + 2 * pad[0] - dilation[0] * (kernel[0] - 1) - 1) // stride[0] + 1,
+            (W + 2 * pad[1] - dilation[1] * (kernel[1] - 1) - 1) // stride[1] + 1)
+
+
+def _depthwise_correlation(x, kern, stride, pad, dilation):
+    """scipy.signal.correlate2d of each channel plane of x [H, W, G, D] with
+    its group's kernel kern [G, kh, kw], dilated by inserting zeros, over the
+    zero-padded input, then strided: a depthwise convolution layer."""
+    from scipy.signal import correlate2d
+    H, W, G, D = x.shape
+    kh, kw = kern.shape[1:]
+    Ho, Wo = _dcn_out_size(H, W, (kh, kw), stride, pad, dilation)
+    out = np.zeros((Ho, Wo, G, D))
+    for g in range(G):
+        kd = np.zeros(((kh - 1) * dilation[0] + 1, (kw - 1) * dilation[1] + 1))
+        kd[::dilation[0], ::dilation[1]] = kern[g]
+        for d in range(D):
+            xp = np.pad(x[:, :, g, d], ((pad[0], pad[0]), (pad[1], pad[1])))
+            full = correlate2d(xp, kd, mode="valid")
+            out[:, :, g, d] = full[::stride[0], ::stride[1]][:Ho, :Wo]
+    return out
+
+
+DCN_CONFIGS = [((3, 3), (1, 1), (1, 1), (1, 1)), ((3, 3), (2, 2), (1, 1), (1, 1)),
+               ((5, 3), (1, 2), (4, 1), (2, 1)), ((3, 2), (2, 1), (2, 3), (1, 3)),
+               ((1, 1), (1, 1), (0, 0), (1, 1))]
+
+
+def pin_dcn_depthwise_conv(lib=None):
+    """Zero offsets and a mask that depends only on (g, k): the aggregation is
+    a depthwise convolution (scipy correlate2d over the zero-padded input,
+    dilated kernel, strided), for several kernel/stride/pad/dilation sets."""
+    rng = np.random.default_rng(51)
+    for kernel, stride, pad, dil in DCN_CONFIGS:
+        H, W, G, D = 7, 9, 2, 3
+        x = rng.standard_normal((1, H, W, G, D))
+        Ho, Wo = _dcn_out_size(H, W, kernel, stride, pad, dil)
+        K = kernel[0] * kernel[1]
+        kern = rng.standard_normal((G, kernel[0], kernel[1]))
+        mask = np.broadcast_to(kern.reshape(1, 1, 1, G, K), (1, Ho, Wo, G, K)).copy()
+        off = np.zeros((1, Ho, Wo, G, K, 2), np.float32)
+        got = oracle.dcn_forward(x, off, mask, kernel, stride, pad, dil, lib=lib)
+        want = _depthwise_correlation(x[0], kern, stride, pad, dil)
+        _close(got[0], want, 1e-12, f"dcn as depthwise conv {kernel} {stride} {pad} {dil}")
+
+
+def pin_dcn_integer_shift(lib=None):
+    """Whole-pixel offsets (dx, dy), the same for every sample: the result is
+    the zero-offset aggregation of the input translated by (-dx, -dy)."""
+    rng = np.random.default_rng(52)
+    H, W, G, D = 8, 10, 2, 2
+    x = rng.standard_normal((1, H, W, G, D))
+    kernel, stride, pad, dil = (3, 3), (1, 1), (1, 1), (1, 1)
+    Ho, Wo = _dcn_out_size(H, W, kernel, stride, pad, dil)
+    mask = rng.standard_normal((1, Ho, Wo, G, 9))
+    for dx, dy in ((1, 0), (0, -2), (3, 1)):
+        off = np.zeros((1, Ho, Wo, G, 9, 2), np.float32)
+        off[..., 0], off[..., 1] = dx, dy
+        xs = np.zeros_like(x)
+        ys, ye = max(0, -dy), min(H, H - dy)
+        xs_, xe = max(0, -dx), min(W, W - dx)
+        xs[0, ys:ye, xs_:xe] = x[0, ys + dy:ye + dy, xs_ + dx:xe + dx]
+        got = oracle.dcn_forward(x, off, mask, kernel, stride, pad, dil, lib=lib)
+        want = oracle.dcn_forward(xs, np.zeros_like(off), mask, kernel, stride, pad, dil, lib=lib)
+        # compare the output pixels whose grid points, shifted or not, all lie
+        # inside the input (elsewhere the translated copy has lost pixels)
+        ho, wo = np.arange(Ho)[:, None], np.arange(Wo)[None, :]
+        inside = (ho - 1 >= 0) & (ho + 1 < H) & (wo - 1 >= 0) & (wo + 1 < W) & \
+            (ho - 1 + dy >= 0) & (ho + 1 + dy < H) & (wo - 1 + dx >= 0) & (wo + 1 + dx < W)
+        assert inside.sum() >= 6
+        _close(got[0][inside], want[0][inside], 1e-12, f"dcn integer shift ({dx}, {dy})")
+
+
+def pin_dcn_matches_core(lib=None):
+    """On power-of-two sizes with dyadic offsets the pixel point P maps to the
+    normalized location (P + 0.5) / (W, H) exactly, so the aggregation equals
+    the core on one level (heads = groups, weights = mask), and its gradients
+    equal the core's: grad_offset = grad_loc / (W, H), grad_mask = grad_attn."""
+    rng = np.random.default_rng(53)
+    H, W, G, D = 8, 16, 2, 3
+    kernel, stride, pad, dil = (3, 3), (1, 2), (1, 1), (2, 1)
+    Ho, Wo = _dcn_out_size(H, W, kernel, stride, pad, dil)
+    K = 9
+    x = rng.standard_normal((2, H, W, G, D))
+    off = (rng.integers(-48, 49, size=(2, Ho, Wo, G, K, 2)) / 16.0).astype(np.float32)
+    mask = rng.standard_normal((2, Ho, Wo, G, K))
+    g = rng.standard_normal((2, Ho, Wo, G, D))
+    ky, kx = np.divmod(np.arange(K), kernel[1])
+    ho = np.arange(Ho)[None, :, None, None, None]
+    wo = np.arange(Wo)[None, None, :, None, None]
+    kx, ky = kx[None, None, None, None, :], ky[None, None, None, None, :]
+    Px = (wo * stride[1] - pad[1] + kx * dil[1]) + off[..., 0].astype(np.float64)
+    Py = (ho * stride[0] - pad[0] + ky * dil[0]) + off[..., 1].astype(np.float64)
+    loc = np.stack([(Px + 0.5) / W, (Py + 0.5) / H], -1)                # [2,Ho,Wo,G,K,2]
+    loc = loc.reshape(2, Ho * Wo, G, 1, K, 2).astype(np.float32)
+    shapes, lsi = level_tables([(H, W)])
+    value = x.reshape(2, H * W, G, D)
+    attn = mask.reshape(2, Ho * Wo, G, 1, K)
+    want = oracle.forward(value, shapes, lsi, loc, attn, lib=lib)
+    got = oracle.dcn_forward(x, off, mask, kernel, stride, pad, dil, lib=lib)
+    _close(got.reshape(want.shape), want, 1e-12, "dcn forward vs core")
+    rgv, rgl, rga = oracle.backward(value, shapes, lsi, loc, attn, g.reshape(2, Ho * Wo, G, D),
+                                    lib=lib)
+    gi, go, gm = oracle.dcn_backward(x, off, mask, g, kernel, stride, pad, dil, lib=lib)
+    _close(gi.reshape(rgv.shape), rgv, 1e-12, "dcn grad_input vs core grad_value")
+    _close(gm.reshape(rga.shape), rga, 1e-12, "dcn grad_mask vs core grad_attn")
+    _close(go.reshape(rgl.shape), rgl / np.array([W, H], np.float64), 1e-12,
+           "dcn grad_offset vs core grad_loc / (W, H)")
+
+
+def pin_dcn_finite_differences(lib=None):
+    """Gradients of L = sum(g * out) equal difference quotients: exact for the
+    mask and the input (L is linear in them), and for offsets moved by less
+    than the distance to the next pixel line (L is bilinear inside a cell)."""
+    rng = np.random.default_rng(54)
+    H, W, G, D = 5, 6, 2, 2
+    kernel, stride, pad, dil = (3, 3), (1, 1), (1, 1), (1, 1)
+    Ho, Wo = _dcn_out_size(H, W, kernel, stride, pad, dil)
+    x = rng.standard_normal((1, H, W, G, D))
+    off = (rng.uniform(-1.5, 1.5, size=(1, Ho, Wo, G, 9, 2))).astype(np.float32)
+    # keep offsets away from pixel lines so a small step stays in its cell
+    off = (np.floor(off) + 0.25 + 0.5 * (off - np.floor(off))).astype(np.float32)
+    mask = rng.standard_normal((1, Ho, Wo, G, 9))
+    g = rng.standard_normal((1, Ho, Wo, G, D))
+    loss = lambda x_, o_, m_: float((oracle.dcn_forward(x_, o_, m_, kernel, stride, pad, dil,  # noqa: E731
+                                                        lib=lib) * g).sum())
+    gi, go, gm = oracle.dcn_backward(x, off, mask, g, kernel, stride, pad, dil, lib=lib)
+    for idx in [(0, 1, 2, 1, 4), (0, 0, 0, 0, 0), (0, 3, 5, 1, 8)]:
+        mp, mm = mask.copy(), mask.copy()
+        mp[idx] += 0.5
+        mm[idx] -= 0.5
+        fd = (loss(x, off, mp) - loss(x, off, mm)) / 1.0
+        assert abs(fd - gm[idx]) <= 1e-9 * max(1.0, abs(fd)), f"d/dmask{idx}: {fd} vs {gm[idx]}"
+        for c in range(2):
+            op, om = off.copy(), off.copy()
+            h = 2.0 ** -10
+            op[idx + (c,)] += h
+            om[idx + (c,)] -= h
+            fd = (loss(x, op, mask) - loss(x, om, mask)) / (2 * h)
+            assert abs(fd - go[idx + (c,)]) <= 1e-6 * max(1.0, abs(fd)), \
+                f"d/doffset{idx + (c,)}: {fd} vs {go[idx + (c,)]}"
+    for idx in [(0, 2, 3, 1, 0), (0, 4, 5, 0, 1)]:
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += 0.5
+        xm[idx] -= 0.5
+        fd = loss(xp, off, mask) - loss(xm, off, mask)
+        assert abs(fd - gi[idx]) <= 1e-9 * max(1.0, abs(fd)), f"d/dinput{idx}: {fd} vs {gi[idx]}"
+
+
+ALL_PINS += [pin_dcn_depthwise_conv, pin_dcn_integer_shift, pin_dcn_matches_core,
+             pin_dcn_finite_differences]

@@ -46,6 +46,20 @@ MUTANTS = {
                                      "if (grad_logits) grad_logits[p] = a * ga[p];"),
     "fused_ref_grad_one_head": ("grad_ref[r] += gloc[2 * p];", "grad_ref[r] += m == 0 ? gloc[2 * p] : 0.0;"),
     "fused_offset_grad_times_W": ("grad_off[2 * p] = gloc[2 * p] / (double)W;", "grad_off[2 * p] = gloc[2 * p] * (double)W;"),
+    "dcn_grid_ignores_dilation": ("const float gx = (float)(wo * sw - pw + kx * dw);",
+                                  "const float gx = (float)(wo * sw - pw + kx);"),
+    "dcn_stride_of_other_axis": ("const float gy = (float)(ho * sh - ph + ky * dh);",
+                                 "const float gy = (float)(ho * sw - ph + ky * dh);"),
+    "dcn_padding_added": ("const float gx = (float)(wo * sw - pw + kx * dw);",
+                          "const float gx = (float)(wo * sw + pw + kx * dw);"),
+    "dcn_kernel_index_transposed": ("const int64_t ky = k / kw, kx = k % kw;",
+                                    "const int64_t kx = k / kw, ky = k % kw;"),
+    "dcn_offset_axes_swapped": ("*x = (double)(float)(gx + off[0]);\n    *y = (double)(float)(gy + off[1]);",
+                                "*x = (double)(float)(gx + off[1]);\n    *y = (double)(float)(gy + off[0]);"),
+    "dcn_mask_ignored": ("const double term = m * c[i].w * v[d];", "const double term = c[i].w * v[d];"),
+    "dcn_offset_grad_without_mask": ("grad_offset[2 * p] = m * gx;", "grad_offset[2 * p] = gx;"),
+    "dcn_input_grad_wrong_group": ("const size_t base = (size_t)(((b * Nv + c[i].row) * G + g) * D);\n                            for (int64_t d = 0; d < D; ++d) {\n                                const double v = input[base + d];",
+                                   "const size_t base = (size_t)(((b * Nv + c[i].row) * G + (G - 1 - g)) * D);\n                            for (int64_t d = 0; d < D; ++d) {\n                                const double v = input[base + d];"),
 }
 
 CHILD = r"""
