@@ -23,8 +23,13 @@ projections on the matrix cores (fp32) around the fused core, with every
 input and parameter gradient. The roofline is then the matrix-core one of the
 dominant GEMM (fp32 dense peak 157.3 TFLOP/s).
 
+With --frontend dcn the step is the grouped single-level aggregation
+(DCNv3), msda_dcn_forward + msda_dcn_backward, on a DCNv3 workload
+(default dcnv3_stage2: the stride-8 stage of the 800x1333 input, 100x167
+pixels, 8 groups of 16 channels, 3x3 grid).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--workload NAME] [--frontend core|fused|layer]
+                       [--workload NAME] [--frontend core|fused|layer|dcn]
        python bench.py --calibrate-copy MIB   (a plain copy-like kernel of known size,
                                                run under the counter profiler to scale
                                                its byte counters)
@@ -72,6 +77,8 @@ def algorithmic_bytes(w, value_bytes_per_elem=4, fused=False):
 
 KERNEL_NAMES = {
     "core": ("msda_fwd_kernel", "msda_bwd_point_kernel", "msda_bin_kernel+msda_tile_kernel"),
+    "dcn": ("msda_fwd_kernel<dcn>", "msda_bwd_point_kernel<dcn>",
+            "msda_bin_kernel<dcn>+msda_tile_kernel"),
     "fused": ("msda_fwd_kernel<fused>",
               "msda_softmax_stats_kernel+msda_bwd_point_kernel<fused>+msda_ref_grad_kernel",
               "msda_softmax_stats_kernel+msda_bin_kernel<fused>+msda_tile_kernel"),
@@ -312,13 +319,132 @@ def cpu_baseline_layer(w, x, budget_s):
                       f"threads, the C oracle's core on one thread)"}
 
 
+class _DcnShape:
+    """A DCNv3 workload seen as a core problem (one level, groups as heads,
+    output pixels as queries), for the byte counts."""
+
+    def __init__(self, w):
+        Ho, Wo = w.out_size
+        self.B, self.M, self.D, self.L, self.K = w.B, w.G, w.D, 1, w.K
+        self.num_queries, self.Nv, self.points = Ho * Wo, w.H * w.W, w.points
+
+
+def bench_dcn(args, w, dev):
+    import torch
+    import scale_deformable_attention_amd as msda
+    from scale_deformable_attention_amd import workloads as wl
+    x = wl.generate_dcn(w)
+    if w.value_dtype == "bf16":
+        inp = torch.from_numpy(x["input_bf16"].view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        inp = torch.from_numpy(x["input"]).to(dev)
+    off = torch.from_numpy(x["offset"]).to(dev)
+    mask = torch.from_numpy(x["mask"]).to(dev)
+    gout = torch.from_numpy(x["grad_output"]).to(dev)
+    geo = dict(kernel=w.kernel, stride=w.stride, pad=w.pad, dilation=w.dilation)
+    Ho, Wo = w.out_size
+    out = torch.empty(w.B, Ho, Wo, w.G * w.D, device=dev)
+    gi = torch.empty(inp.shape, dtype=torch.float32, device=dev)
+    go = torch.empty_like(off)
+    gm = torch.empty_like(mask)
+    ws = torch.empty(max(msda.msda_dcn_backward_workspace_size(inp, off, **geo), 1),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def fwd():
+        msda.msda_dcn_forward(inp, off, mask, output=out, **geo)
+
+    def bwd(needs=(True, True, True)):
+        msda.msda_dcn_backward(inp, off, mask, gout, needs=needs, grad_input=gi, grad_offset=go,
+                               grad_mask=gm, workspace=ws, **geo)
+
+    def step():
+        fwd()
+        bwd()
+
+    def timed(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    names = KERNEL_NAMES["dcn"]
+    kernels = {names[0]: timed(fwd, args.steps),
+               names[1]: timed(lambda: bwd((False, True, True)), args.steps),
+               names[2]: timed(lambda: bwd((True, False, False)), args.steps)}
+    step()
+    torch.cuda.synchronize()
+    shape = _DcnShape(w)
+    ab = algorithmic_bytes(shape, 2 if w.value_dtype == "bf16" else 4)
+    kernel_bytes = dict(zip(names, (ab["forward"], ab["bwd_point"], ab["bwd_value"])))
+    dom = max(kernels, key=kernels.get)
+    achieved = kernel_bytes[dom] / (kernels[dom] * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": w.points / (ms_per_step * 1e-3),
+        "unit": "points/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.value_dtype == "f32" else "bf16 input, f32 math",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: DCNv3 aggregation, {w.note}; B={w.B} H={w.H} "
+                               f"W={w.W} G={w.G} D={w.D} kernel={w.kernel} stride={w.stride} "
+                               f"pad={w.pad} dilation={w.dilation} offsets N(0,{w.sigma_px} px)",
+                   "frontend": "dcn", "points_per_step": w.points, "global_batch": w.B,
+                   "parallelism": "none"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes": kernel_bytes[dom],
+                     "avg_ms": kernels[dom], "launches": len(dom.split("+"))},
+        "kernels_ms": kernels,
+        "kernels_frac": {k: kernel_bytes[k] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS
+                         for k, v in kernels.items()},
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        oracle.dcn_forward(x["input"][:1], x["offset"][:1], x["mask"][:1], **geo)
+        oracle.dcn_backward(x["input"][:1], x["offset"][:1], x["mask"][:1], x["grad_output"][:1],
+                            **geo)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": (w.points // w.B) / dt, "unit": "points/s",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": f"1 of {w.B} batch entries, forward + backward, "
+                                            f"{w.points // w.B} points in {dt:.1f} s, single "
+                                            f"thread, double accumulation"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="encoder_train")
-    ap.add_argument("--frontend", choices=("core", "fused", "layer"), default="core",
+    ap.add_argument("--frontend", choices=("core", "fused", "layer", "dcn"), default="core",
                     help="core: locations and weights given; fused: formed in the kernels "
                          "from reference points, offsets and logits; layer: the whole "
                          "MSDeformAttn layer with its four projections")
@@ -340,9 +466,12 @@ def main():
     import scale_deformable_attention_amd as msda
     from scale_deformable_attention_amd import workloads as wl
 
-    w = wl.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     msda.library()
+    if args.frontend == "dcn":
+        name = args.workload if args.workload in wl.DCN_WORKLOADS else "dcnv3_stage2"
+        return bench_dcn(args, wl.DCN_WORKLOADS[name], dev)
+    w = wl.WORKLOADS[args.workload]
     if args.frontend == "layer":
         return bench_layer(args, w, dev)
     x = wl.generate(w)

@@ -67,7 +67,7 @@ extern "C" {
 #endif
 
 #define MSDA_VERSION_MAJOR 0
-#define MSDA_VERSION_MINOR 4
+#define MSDA_VERSION_MINOR 5
 #define MSDA_VERSION_PATCH 0
 
 /* Largest number of feature levels the kernels accept. */
@@ -320,6 +320,61 @@ msda_status_t msda_layer_backward(const msda_dims_t *dims, const float *query,
  * No HIP call. */
 msda_status_t msda_layer_saved_size(const msda_dims_t *dims, size_t *bytes);
 msda_status_t msda_layer_workspace_size(const msda_dims_t *dims, size_t *bytes);
+
+/*
+ * Grouped single-level deformable aggregation (DCNv3; deformable-attention
+ * practice guide, section 4.2): for every output pixel p0 = (ho, wo), group g
+ * and kernel point k = ky * kernel_w + kx,
+ *
+ *   output[b, ho, wo, g, :] = sum_k mask[b, ho, wo, g, k] *
+ *                             bilinear(input[b, :, :, g, :], p0 + p_k + offset[b, ho, wo, g, k])
+ *
+ * with the convolution grid  p0 + p_k = (wo * stride_w - pad_w + kx * dilation_w,
+ *                                         ho * stride_h - pad_h + ky * dilation_h)
+ * in input pixels (x along W, y along H; pixel (i, j) sits at x = j, y = i),
+ * the offset (x, y) in pixels added in fp32, bilinear interpolation over the
+ * four surrounding pixels with zero outside the input, and the modulation
+ * scalars used as given (no normalization). It is the core on one level with
+ * the groups as heads (the shared projection w_g is a separate linear layer).
+ *
+ *   input   [B, H, W, G, D]           fp32 or bf16 (channels-last, grouped)
+ *   offset  [B, H_out, W_out, G, K, 2] fp32, K = kernel_h * kernel_w
+ *   mask    [B, H_out, W_out, G, K]    fp32
+ *   output  [B, H_out, W_out, G * D]   fp32
+ * D in {8, 16, 32, 64}; coordinates of the grid below 2^24.
+ */
+typedef struct {
+    int64_t B, H, W, G, D;
+    int64_t kernel_h, kernel_w;
+    int64_t stride_h, stride_w;
+    int64_t pad_h, pad_w;
+    int64_t dilation_h, dilation_w;
+    int64_t H_out, W_out;
+} msda_dcn_dims_t;
+
+/* Forward. Alignment: input and output 16-byte, offset 8-byte, mask 4-byte. */
+msda_status_t msda_dcn_forward(const msda_dcn_dims_t *dims, msda_dtype_t input_dtype,
+                               const void *input, const float *offset, const float *mask,
+                               float *output, hipStream_t stream);
+
+/*
+ * Backward for grad_output [B, H_out, W_out, G * D]:
+ *   grad_input  [B, H, W, G, D] fp32   (scattered without atomics, as grad_value)
+ *   grad_offset [B, H_out, W_out, G, K, 2] = mask * sum_d g * d sample / d (x, y)
+ *   grad_mask   [B, H_out, W_out, G, K]    = sum_d g * sample
+ * each overwritten, each may be NULL. workspace as msda_backward: at least
+ * msda_dcn_backward_workspace_size() bytes, 256-byte aligned, when
+ * grad_input is requested.
+ */
+msda_status_t msda_dcn_backward(const msda_dcn_dims_t *dims, msda_dtype_t input_dtype,
+                                const void *input, const float *offset, const float *mask,
+                                const float *grad_output, float *grad_input, float *grad_offset,
+                                float *grad_mask, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/* Bytes of workspace msda_dcn_backward needs. No HIP call. */
+msda_status_t msda_dcn_backward_workspace_size(const msda_dcn_dims_t *dims,
+                                               msda_dtype_t input_dtype, size_t *bytes);
 
 /* Host-side check of a HOST copy of the level tables against Nv: every
  * H_l, W_l >= 1, level_start_index the prefix sums, sum H_l*W_l == Nv.

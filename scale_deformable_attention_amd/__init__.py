@@ -5,7 +5,9 @@ package is its Python binding. Importing the package does not load the
 library; the first call does, and raises if it has not been built.
 """
 from ._binding import (MSDA_DTYPE_BF16, MSDA_DTYPE_F32, MsdaError, MSDeformAttnFunction,
-                       MSDeformAttnFusedFunction, library, ms_deform_attn, ms_deform_attn_fused,
+                       MSDeformAttnFusedFunction, dcn_output_size, library, ms_deform_attn,
+                       ms_deform_attn_fused, msda_dcn_backward, msda_dcn_backward_workspace_size,
+                       msda_dcn_forward,
                        msda_backward, msda_backward_fused, msda_backward_fused_workspace_size,
                        msda_backward_workspace_size, msda_check_tables, msda_forward,
                        msda_forward_fused, msda_layer_backward, msda_layer_forward,
@@ -16,6 +18,7 @@ __all__ = ["msda_forward", "msda_backward", "msda_backward_workspace_size",
            "msda_forward_fused", "msda_backward_fused", "msda_backward_fused_workspace_size",
            "msda_linear_forward", "msda_linear_backward", "msda_linear_backward_workspace_size",
            "msda_layer_forward", "msda_layer_backward", "msda_layer_sizes",
-           "msda_check_tables", "msda_version", "library", "ms_deform_attn",
+           "msda_dcn_forward", "msda_dcn_backward", "msda_dcn_backward_workspace_size",
+           "dcn_output_size", "msda_check_tables", "msda_version", "library", "ms_deform_attn",
            "MSDeformAttnFunction", "ms_deform_attn_fused", "MSDeformAttnFusedFunction",
            "MsdaError", "MSDA_DTYPE_F32", "MSDA_DTYPE_BF16"]

@@ -35,6 +35,12 @@ class MsdaLayerGrads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in LAYER_PARAMS]
 
 
+class MsdaDcnDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("B", "H", "W", "G", "D", "kernel_h", "kernel_w", "stride_h", "stride_w", "pad_h",
+                 "pad_w", "dilation_h", "dilation_w", "H_out", "W_out")]
+
+
 class MsdaError(RuntimeError):
     def __init__(self, status, where):
         super().__init__(f"{where}: {STATUS.get(status, status)} "
@@ -97,6 +103,15 @@ def library():
             getattr(lib, name).restype = ctypes.c_int
             getattr(lib, name).argtypes = [ctypes.POINTER(MsdaDims),
                                            ctypes.POINTER(ctypes.c_size_t)]
+        dp = ctypes.POINTER(MsdaDcnDims)
+        lib.msda_dcn_forward.restype = ctypes.c_int
+        lib.msda_dcn_forward.argtypes = [dp, ctypes.c_int, vp, fp, fp, fp, vp]
+        lib.msda_dcn_backward.restype = ctypes.c_int
+        lib.msda_dcn_backward.argtypes = [dp, ctypes.c_int, vp, fp, fp, fp, fp, fp, fp, vp,
+                                          ctypes.c_size_t, vp]
+        lib.msda_dcn_backward_workspace_size.restype = ctypes.c_int
+        lib.msda_dcn_backward_workspace_size.argtypes = [dp, ctypes.c_int,
+                                                         ctypes.POINTER(ctypes.c_size_t)]
         lib.msda_backward_fused_workspace_size.restype = ctypes.c_int
         lib.msda_backward_fused_workspace_size.argtypes = [ctypes.POINTER(MsdaDims), ctypes.c_int,
                                                            ctypes.POINTER(ctypes.c_size_t)]
@@ -612,3 +627,96 @@ def msda_layer_backward(query, input_flatten, reference_points, spatial_shapes,
     if st != 0:
         raise MsdaError(st, "msda_layer_backward")
     return out
+
+
+# ----------------------------------------------------------------------------- DCNv3
+def dcn_output_size(H, W, kernel, stride=(1, 1), pad=(0, 0), dilation=(1, 1)):
+    """Output rows and columns of the convolution grid."""
+    return ((H + 2 * pad[0] - dilation[0] * (kernel[0] - 1) - 1) // stride[0] + 1,
+            (W + 2 * pad[1] - dilation[1] * (kernel[1] - 1) - 1) // stride[1] + 1)
+
+
+def _dcn_dims(inp, offset, kernel, stride, pad, dilation):
+    if inp.dim() != 5:
+        raise ValueError("input must be [B, H, W, G, D]")
+    B, H, W, G, D = inp.shape
+    if offset.dim() != 6 or offset.shape[-1] != 2 or offset.shape[0] != B or \
+            offset.shape[3] != G or offset.shape[4] != kernel[0] * kernel[1]:
+        raise ValueError("offset must be [B, H_out, W_out, G, kernel_h * kernel_w, 2]")
+    Ho, Wo = offset.shape[1], offset.shape[2]
+    return MsdaDcnDims(B, H, W, G, D, kernel[0], kernel[1], stride[0], stride[1], pad[0], pad[1],
+                       dilation[0], dilation[1], Ho, Wo)
+
+
+def _dcn_checks(inp, offset, mask, dev):
+    _check(inp, "input", (torch.float32, torch.bfloat16), dev)
+    _check(offset, "offset", (torch.float32,), dev)
+    _check(mask, "mask", (torch.float32,), dev)
+    if tuple(mask.shape) != tuple(offset.shape[:5]):
+        raise ValueError("mask must be [B, H_out, W_out, G, K]")
+
+
+def msda_dcn_forward(inp, offset, mask, kernel, stride=(1, 1), pad=(0, 0), dilation=(1, 1),
+                     output=None, stream=None):
+    """Grouped single-level deformable aggregation (include/msda.h
+    msda_dcn_forward): input [B,H,W,G,D], offset [B,Ho,Wo,G,K,2] (pixels),
+    mask [B,Ho,Wo,G,K] -> output [B,Ho,Wo,G*D] (fp32)."""
+    dev = inp.device
+    if dev.type != "cuda":
+        raise ValueError("input must be a GPU tensor")
+    _dcn_checks(inp, offset, mask, dev)
+    dims = _dcn_dims(inp, offset, kernel, stride, pad, dilation)
+    if output is None:
+        output = torch.empty((dims.B, dims.H_out, dims.W_out, dims.G * dims.D),
+                             dtype=torch.float32, device=dev)
+    st = library().msda_dcn_forward(ctypes.byref(dims), _value_dtype(inp), _ptr(inp),
+                                    _ptr(offset), _ptr(mask), _ptr(output), _stream(dev, stream))
+    if st != 0:
+        raise MsdaError(st, "msda_dcn_forward")
+    return output
+
+
+def msda_dcn_backward_workspace_size(inp, offset, kernel, stride=(1, 1), pad=(0, 0),
+                                     dilation=(1, 1)):
+    dims = _dcn_dims(inp, offset, kernel, stride, pad, dilation)
+    n = ctypes.c_size_t(0)
+    st = library().msda_dcn_backward_workspace_size(ctypes.byref(dims), _value_dtype(inp),
+                                                    ctypes.byref(n))
+    if st != 0:
+        raise MsdaError(st, "msda_dcn_backward_workspace_size")
+    return n.value
+
+
+def msda_dcn_backward(inp, offset, mask, grad_output, kernel, stride=(1, 1), pad=(0, 0),
+                      dilation=(1, 1), needs=(True, True, True), grad_input=None,
+                      grad_offset=None, grad_mask=None, workspace=None, stream=None):
+    """Gradients of msda_dcn_forward: (grad_input [B,H,W,G,D] fp32,
+    grad_offset, grad_mask), None where ``needs`` is False."""
+    dev = inp.device
+    _dcn_checks(inp, offset, mask, dev)
+    _check(grad_output, "grad_output", (torch.float32,), dev)
+    dims = _dcn_dims(inp, offset, kernel, stride, pad, dilation)
+    if grad_output.numel() != dims.B * dims.H_out * dims.W_out * dims.G * dims.D:
+        raise ValueError("grad_output has the wrong number of elements")
+    outs = []
+    for need, given, like in ((needs[0], grad_input, inp), (needs[1], grad_offset, offset),
+                              (needs[2], grad_mask, mask)):
+        if not need:
+            outs.append(None)
+        elif given is None:
+            outs.append(torch.empty(like.shape, dtype=torch.float32, device=dev))
+        else:
+            outs.append(given)
+    ws_bytes = 0
+    if outs[0] is not None:
+        n = msda_dcn_backward_workspace_size(inp, offset, kernel, stride, pad, dilation)
+        if workspace is None:
+            workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = library().msda_dcn_backward(ctypes.byref(dims), _value_dtype(inp), _ptr(inp),
+                                     _ptr(offset), _ptr(mask), _ptr(grad_output),
+                                     *[_ptr(o) for o in outs], _ptr(workspace),
+                                     ctypes.c_size_t(ws_bytes), _stream(dev, stream))
+    if st != 0:
+        raise MsdaError(st, "msda_dcn_backward")
+    return tuple(outs)

@@ -130,6 +130,19 @@ struct Params {
     float2* smax;             // [T] max and 1/sum of each tuple's exp(logit - max)
     float* grad_off;          // [B, Nq, M, L, K, 2]
     float* grad_logits;       // [B, Nq, M, L*K]
+    // grouped single-level front-end (DCNv3): point k of output pixel
+    // (ho, wo) samples at (wo*stride_w - pad_w + kx*dil_w, ho*stride_h - pad_h
+    // + ky*dil_h) + offset, in pixels, k = ky*kernel_w + kx; the offsets are
+    // read from `off` and the modulation scalars from `attn`
+    int out_W, kernel_w, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w;
+    int lvl_H, lvl_W;         // the level table when shapes is null (one level)
+};
+
+// Where a kernel's sampling locations and weights come from.
+enum FrontEnd : int {
+    kFeCore = 0,    // locations and weights given
+    kFeFused = 1,   // reference point + offset / (W, H), softmax of logits
+    kFeDcn = 2      // convolution grid + pixel offset, modulation scalars given
 };
 
 // The inputs of point j (level l) of tuple t as loaded: its location and
@@ -142,11 +155,19 @@ struct PointIn {
     float z;      // weight, or the logit
 };
 
-template <bool kFused>
+template <int FE>
 __device__ inline PointIn load_point(const Params& p, int t, int j, int l) {
     PointIn in;
     const size_t pt = (size_t)t * p.LK + j;
-    if constexpr (kFused) {
+    if constexpr (FE == kFeDcn) {
+        const int q = (t / p.M) % p.Nq;
+        const int ho = q / p.out_W, wo = q - ho * p.out_W;
+        const int ky = j / p.kernel_w, kx = j - ky * p.kernel_w;
+        in.uv = make_float2((float)(wo * p.stride_w - p.pad_w + kx * p.dil_w),
+                            (float)(ho * p.stride_h - p.pad_h + ky * p.dil_h));
+        in.off = *reinterpret_cast<const float2*>(p.off + 2 * pt);
+        in.z = p.attn[pt];
+    } else if constexpr (FE == kFeFused) {
         const size_t bq = (size_t)(t / p.M);
         in.uv = *reinterpret_cast<const float2*>(p.ref + 2 * (bq * p.L + l));
         in.off = *reinterpret_cast<const float2*>(p.off + 2 * pt);
@@ -163,10 +184,15 @@ __device__ inline PointIn load_point(const Params& p, int t, int j, int l) {
 // the level's size (W for x, H for y), the quotient and the sum each rounded
 // to float; the weight is exp(z - max) / sum over the tuple's L*K logits
 // (zmax and inv_sum are that max and 1 / sum).
-template <bool kFused>
+// (DCNv3: the grid point plus the offset, one fp32 addition, in pixels.)
+template <int FE>
 __device__ inline void finish_point(const PointIn& in, int4 lv, float zmax, float inv_sum,
                                     float2& uv, float& a) {
-    if constexpr (kFused) {
+    if constexpr (FE == kFeDcn) {
+        uv.x = in.uv.x + in.off.x;
+        uv.y = in.uv.y + in.off.y;
+        a = in.z;
+    } else if constexpr (FE == kFeFused) {
         const float qx = in.off.x / (float)lv.y;
         const float qy = in.off.y / (float)lv.x;
         uv.x = in.uv.x + qx;
@@ -211,7 +237,9 @@ __device__ inline float group_sum(float v) {
 __device__ inline void load_levels(const Params& p, int4* levels) {
     if (threadIdx.x < (unsigned)p.L) {
         const int l = threadIdx.x;
-        levels[l] = make_int4((int)p.shapes[2 * l], (int)p.shapes[2 * l + 1], (int)p.lsi[l], 0);
+        levels[l] = p.shapes ? make_int4((int)p.shapes[2 * l], (int)p.shapes[2 * l + 1],
+                                         (int)p.lsi[l], 0)
+                             : make_int4(p.lvl_H, p.lvl_W, 0, 0);
     }
     __syncthreads();
 }
@@ -225,13 +253,11 @@ struct Geometry {
     uint32_t off[4];
 };
 
-__device__ inline Geometry point_geometry(float u, float v, int4 lv, uint32_t tuple_base,
-                                          uint32_t row_bytes) {
+// (x, y) in level pixels: pixel (i, j) at x = j, y = i.
+__device__ inline Geometry point_geometry_px(float x, float y, int4 lv, uint32_t tuple_base,
+                                             uint32_t row_bytes) {
     Geometry g;
     const float Hf = (float)lv.x, Wf = (float)lv.y;
-    // cell-centre map, one rounding (the oracle uses the same fp32 fma)
-    const float x = fmaf(u, Wf, -0.5f);
-    const float y = fmaf(v, Hf, -0.5f);
     const float x0f = floorf(x), y0f = floorf(y);
     g.fx = x - x0f;
     g.fy = y - y0f;
@@ -255,6 +281,21 @@ __device__ inline Geometry point_geometry(float u, float v, int4 lv, uint32_t tu
     g.off[2] = g.valid[2] ? o00 + (uint32_t)lv.y * row_bytes : kOutside;
     g.off[3] = g.valid[3] ? o00 + (uint32_t)(lv.y + 1) * row_bytes : kOutside;
     return g;
+}
+
+// (u, v) normalized: the cell-centre map first, one rounding each (the
+// oracle uses the same fp32 fma).
+__device__ inline Geometry point_geometry(float u, float v, int4 lv, uint32_t tuple_base,
+                                          uint32_t row_bytes) {
+    return point_geometry_px(fmaf(u, (float)lv.y, -0.5f), fmaf(v, (float)lv.x, -0.5f), lv,
+                             tuple_base, row_bytes);
+}
+
+template <int FE>
+__device__ inline Geometry geometry_of(float2 uv, int4 lv, uint32_t tuple_base,
+                                       uint32_t row_bytes) {
+    if constexpr (FE == kFeDcn) return point_geometry_px(uv.x, uv.y, lv, tuple_base, row_bytes);
+    return point_geometry(uv.x, uv.y, lv, tuple_base, row_bytes);
 }
 
 // Byte offset, within the value tensor, of tuple t's row 0: (b*Nv*M + m)*D*elem.
@@ -293,8 +334,9 @@ struct alignas(16) FwdRecord {
     float w[4];   // A * bilinear weight, 0 for corners outside
 };
 
-template <typename T, int D, bool kFused>
+template <typename T, int D, int FE>
 __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
+    constexpr bool kFused = FE == kFeFused;
     using S = Shape<T, D>;
     constexpr int G = S::G, TPW = S::TPW, PL = S::kPerLane;
     constexpr int kRowBytesPerHead = D * Elem<T>::kBytes;
@@ -329,7 +371,7 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
     // the current chunk's rows are gathered
     auto fetch = [&](int jc) {
         const int j = min(jc + jrow, p.LK - 1);
-        return load_point<kFused>(p, t1, j, (unsigned)j / (unsigned)p.K);
+        return load_point<FE>(p, t1, j, (unsigned)j / (unsigned)p.K);
     };
     PointIn in_next{};
     if (t1_ok && p.LK > 0) in_next = fetch(0);
@@ -383,8 +425,8 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
             const int4 lv = levels[l];
             float2 uv;
             float a;
-            finish_point<kFused>(in, lv, zmax, inv_sum, uv, a);
-            const Geometry geo = point_geometry(uv.x, uv.y, lv, base1, row_bytes);
+            finish_point<FE>(in, lv, zmax, inv_sum, uv, a);
+            const Geometry geo = geometry_of<FE>(uv, lv, base1, row_bytes);
             const float ay0 = a * (1.0f - geo.fy), ay1 = a * geo.fy;
             const float w[4] = {ay0 * (1.0f - geo.fx), ay0 * geo.fx, ay1 * (1.0f - geo.fx),
                                 ay1 * geo.fx};
@@ -454,8 +496,9 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
 // softmax max and 1/sum per tuple) and msda_ref_grad_kernel after the point
 // kernel (the reference-point gradient, a sum over heads and points).
 
-template <typename T, int D, bool kFused>
+template <typename T, int D, int FE>
 __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
+    constexpr bool kFused = FE == kFeFused;
     using S = Shape<T, D>;
     constexpr int G = S::G, TPW = S::TPW, PL = S::kPerLane;
     constexpr int kRowBytesPerHead = D * Elem<T>::kBytes;
@@ -512,7 +555,7 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
     // the current chunk's rows are gathered
     auto fetch = [&](int jc) {
         const int j = min(jc + r, p.LK - 1);
-        return load_point<kFused>(p, t, j, (unsigned)j / (unsigned)p.K);
+        return load_point<FE>(p, t, j, (unsigned)j / (unsigned)p.K);
     };
     PointIn in_next{};
     if (t_ok && p.LK > 0) in_next = fetch(0);
@@ -533,8 +576,8 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
             Hf = (float)lv.x;
             Wf = (float)lv.y;
             float2 uv;
-            finish_point<kFused>(in, lv, zmax, inv_sum, uv, a);
-            geo = point_geometry(uv.x, uv.y, lv, base, row_bytes);
+            finish_point<FE>(in, lv, zmax, inv_sum, uv, a);
+            geo = geometry_of<FE>(uv, lv, base, row_bytes);
         } else {
             geo.fx = geo.fy = 0.0f;
 #pragma unroll
@@ -595,6 +638,12 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
                     *reinterpret_cast<float2*>(p.grad_off + 2 * pt) = make_float2(a * gx, a * gy);
                 if (p.grad_logits) p.grad_logits[pt] = ga;
                 s_ag = fmaf(a, ga, s_ag);
+            } else if constexpr (FE == kFeDcn) {
+                // pixel offsets: d(x, y) / d offset = 1; the modulation
+                // scalar's gradient is the plain weight gradient
+                if (p.grad_off)
+                    *reinterpret_cast<float2*>(p.grad_off + 2 * pt) = make_float2(a * gx, a * gy);
+                if (p.grad_attn) p.grad_attn[pt] = ga;
             } else {
                 if (p.grad_attn) p.grad_attn[pt] = ga;
                 if (p.grad_loc)
@@ -647,9 +696,9 @@ __device__ inline void setup_tiles(const Params& p, LevelTiles* lt, int* total) 
         int base = 0;
         for (int l = 0; l < p.L; ++l) {
             LevelTiles t;
-            t.H = (int)p.shapes[2 * l];
-            t.W = (int)p.shapes[2 * l + 1];
-            t.start = (int)p.lsi[l];
+            t.H = p.shapes ? (int)p.shapes[2 * l] : p.lvl_H;
+            t.W = p.shapes ? (int)p.shapes[2 * l + 1] : p.lvl_W;
+            t.start = p.shapes ? (int)p.lsi[l] : 0;
             t.tile_base = base;
             t.ntx = (t.W + TW - 1) / TW;
             t.pad0 = t.pad1 = t.pad2 = 0;
@@ -717,11 +766,12 @@ __device__ inline uint32_t block_exclusive_scan(const uint32_t* a, uint32_t* o, 
 // tile of corner c (0: (y0,x0), 1: (y0,x0+1), 2: (y0+1,x0), 3: (y0+1,x0+1))
 // and emit[c] says whether corner c is inside the level and is the first
 // corner of its tile.
-template <int TW>
+// (u, v) normalized, or with kPixel already the pixel coordinates (x, y).
+template <int TW, bool kPixel>
 __device__ inline void point_tiles(float u, float v, const LevelTiles& lt, int* tile, bool* emit) {
     const float Hf = (float)lt.H, Wf = (float)lt.W;
-    const float x = fmaf(u, Wf, -0.5f);
-    const float y = fmaf(v, Hf, -0.5f);
+    const float x = kPixel ? u : fmaf(u, Wf, -0.5f);
+    const float y = kPixel ? v : fmaf(v, Hf, -0.5f);
     const float x0f = floorf(x), y0f = floorf(y);
     const bool vx0 = (x0f >= 0.0f) && (x0f < Wf);
     const bool vx1 = (x0f >= -1.0f) && (x0f < Wf - 1.0f);
@@ -787,7 +837,7 @@ struct PointWalk {
     }
 };
 
-template <int D, bool kFused>
+template <int D, int FE>
 __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
     using TS = TileShape<D>;
     __shared__ LevelTiles lt[MSDA_MAX_LEVELS];
@@ -810,14 +860,16 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
     if (blockIdx.x == 0 && tid < 8) p.counters[tid] = 0;   // for the tile kernel that follows
     // location (and weight) of the walk's current point, or of its first point
     // for lanes past the end, so that every load is unconditional
+    // (normalized, or for the DCNv3 front-end in pixels)
     auto point_of = [&](const PointWalk& it, bool ok, float2& uv, float& a, bool want_a) {
-        if constexpr (kFused) {
+        if constexpr (FE != kFeCore) {
             const int t = ok ? (int)it.t : (int)it.tuple0;
             const int j = ok ? it.j : 0;
             const int l = ok ? it.l : 0;
-            const float2 st = want_a ? p.smax[t] : make_float2(0.f, 0.f);
-            finish_point<true>(load_point<true>(p, t, j, l),
-                               make_int4(lt[l].H, lt[l].W, lt[l].start, 0), st.x, st.y, uv, a);
+            float2 st = make_float2(0.f, 0.f);
+            if constexpr (FE == kFeFused) st = want_a ? p.smax[t] : st;
+            finish_point<FE>(load_point<FE>(p, t, j, l),
+                             make_int4(lt[l].H, lt[l].W, lt[l].start, 0), st.x, st.y, uv, a);
         } else {
             const size_t pt = ok ? it.pt : it.pt0;
             uv = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
@@ -847,7 +899,7 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
             for (int u = 0; u < kBinUnroll; ++u) {
                 int tile[4];
                 bool emit[4];
-                point_tiles<TS::TW>(uv[u].x, uv[u].y, lt[lvl[u]], tile, emit);
+                point_tiles<TS::TW, FE == kFeDcn>(uv[u].x, uv[u].y, lt[lvl[u]], tile, emit);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     if (ok[u] && emit[c] && tile[c] >= r0 && tile[c] < r0 + rn)
@@ -880,12 +932,13 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
                 int tile[4];
                 bool emit[4];
                 const LevelTiles& L_ = lt[lvl[u]];
-                point_tiles<TS::TW>(uv[u].x, uv[u].y, L_, tile, emit);
+                point_tiles<TS::TW, FE == kFeDcn>(uv[u].x, uv[u].y, L_, tile, emit);
                 // the entry carries all the tile kernel needs: the tuple (its
                 // upstream-gradient row), the fp32 pixel coordinates (cell and
                 // fractions follow from them exactly as here) and the weight
-                const float4 rec = make_float4(as_float(tup[u]), fmaf(uv[u].x, (float)L_.W, -0.5f),
-                                               fmaf(uv[u].y, (float)L_.H, -0.5f), a[u]);
+                const float px = FE == kFeDcn ? uv[u].x : fmaf(uv[u].x, (float)L_.W, -0.5f);
+                const float py = FE == kFeDcn ? uv[u].y : fmaf(uv[u].y, (float)L_.H, -0.5f);
+                const float4 rec = make_float4(as_float(tup[u]), px, py, a[u]);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     if (ok[u] && emit[c] && tile[c] >= r0 && tile[c] < r0 + rn) {
@@ -1274,18 +1327,24 @@ struct Kernels {
     const void* fwd_fused = nullptr;
     const void* point_fused = nullptr;
     const void* bin_fused = nullptr;
+    const void* fwd_dcn = nullptr;
+    const void* point_dcn = nullptr;
+    const void* bin_dcn = nullptr;
     int tuples_per_block = 0;
 };
 
 template <typename T, int D>
 Kernels kernels_for() {
     Kernels k;
-    k.fwd = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D, false>);
-    k.point = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D, false>);
-    k.bin = reinterpret_cast<const void*>(&msda_bin_kernel<D, false>);
-    k.fwd_fused = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D, true>);
-    k.point_fused = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D, true>);
-    k.bin_fused = reinterpret_cast<const void*>(&msda_bin_kernel<D, true>);
+    k.fwd = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D, kFeCore>);
+    k.point = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D, kFeCore>);
+    k.bin = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCore>);
+    k.fwd_fused = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D, kFeFused>);
+    k.point_fused = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D, kFeFused>);
+    k.bin_fused = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeFused>);
+    k.fwd_dcn = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D, kFeDcn>);
+    k.point_dcn = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D, kFeDcn>);
+    k.bin_dcn = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeDcn>);
     k.tile = reinterpret_cast<const void*>(&msda_tile_kernel<D>);
     k.tuples_per_block = Shape<T, D>::TPW * kWavesPerBlock;
     return k;
@@ -1527,6 +1586,129 @@ msda_status_t msda_backward_fused(const msda_dims_t* dims, msda_dtype_t value_dt
                                          dim3((unsigned)((nref + kBlock - 1) / kBlock)), dim3(kBlock),
                                          args, 0, stream);
     return e == hipSuccess ? MSDA_SUCCESS : MSDA_ERROR_LAUNCH;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The grouped single-level problem as a core problem: one level of H x W
+// pixels, G heads of D channels, the H_out x W_out output pixels as queries
+// and the kernel_h x kernel_w grid points as the points of that level.
+msda_status_t dcn_dims(const msda_dcn_dims_t* d, msda_dims_t* o) {
+    if (!d) return MSDA_ERROR_INVALID_VALUE;
+    if (d->B < 0 || d->H < 1 || d->W < 1 || d->G < 1 || d->D < 1 || d->kernel_h < 1 ||
+        d->kernel_w < 1 || d->stride_h < 1 || d->stride_w < 1 || d->pad_h < 0 || d->pad_w < 0 ||
+        d->dilation_h < 1 || d->dilation_w < 1 || d->H_out < 0 || d->W_out < 0)
+        return MSDA_ERROR_INVALID_VALUE;
+    // grid coordinates stay exact in fp32 and in 32-bit integers
+    const int64_t lim = (int64_t)1 << 24;
+    if (d->H >= lim || d->W >= lim || d->H_out >= lim || d->W_out >= lim ||
+        d->kernel_h >= lim || d->kernel_w >= lim || d->kernel_h * d->kernel_w >= lim ||
+        d->H_out * d->stride_h + d->pad_h + d->kernel_h * d->dilation_h >= lim ||
+        d->W_out * d->stride_w + d->pad_w + d->kernel_w * d->dilation_w >= lim)
+        return MSDA_ERROR_NOT_SUPPORTED;
+    o->B = d->B;
+    o->Nv = d->H * d->W;
+    o->M = d->G;
+    o->D = d->D;
+    o->L = 1;
+    o->Nq = d->H_out * d->W_out;
+    o->K = d->kernel_h * d->kernel_w;
+    return MSDA_SUCCESS;
+}
+
+void dcn_params(Params& p, const msda_dcn_dims_t* d) {
+    p.shapes = nullptr;
+    p.lsi = nullptr;
+    p.lvl_H = (int)d->H;
+    p.lvl_W = (int)d->W;
+    p.out_W = (int)std::max<int64_t>(d->W_out, 1);
+    p.kernel_w = (int)d->kernel_w;
+    p.stride_h = (int)d->stride_h;
+    p.stride_w = (int)d->stride_w;
+    p.pad_h = (int)d->pad_h;
+    p.pad_w = (int)d->pad_w;
+    p.dil_h = (int)d->dilation_h;
+    p.dil_w = (int)d->dilation_w;
+}
+
+}  // namespace
+
+extern "C" {
+
+msda_status_t msda_dcn_forward(const msda_dcn_dims_t* dcn, msda_dtype_t input_dtype,
+                               const void* input, const float* offset, const float* mask,
+                               float* output, hipStream_t stream) {
+    msda_dims_t dims;
+    msda_status_t st = dcn_dims(dcn, &dims);
+    if (st != MSDA_SUCCESS) return st;
+    st = check_dims(&dims, input_dtype, false);
+    if (st != MSDA_SUCCESS) return st;
+    const Sizes n = sizes_of(&dims);
+    if ((n.value && !input) || (n.points && (!offset || !mask)) || (n.out && !output))
+        return MSDA_ERROR_INVALID_VALUE;
+    if (!aligned(input, 16) || !aligned(output, 16) || !aligned(offset, 8) || !aligned(mask, 4))
+        return MSDA_ERROR_INVALID_VALUE;
+    Params p = make_params(&dims, input_dtype, input, nullptr, nullptr, nullptr, mask);
+    dcn_params(p, dcn);
+    p.off = offset;
+    p.out = output;
+    if (p.T == 0) return MSDA_SUCCESS;
+    const Kernels k = pick(input_dtype, dims.D);
+    if (!k.fwd_dcn) return MSDA_ERROR_NOT_SUPPORTED;
+    return launch(k.fwd_dcn, ((int64_t)p.T + k.tuples_per_block - 1) / k.tuples_per_block, p,
+                  stream);
+}
+
+msda_status_t msda_dcn_backward_workspace_size(const msda_dcn_dims_t* dcn,
+                                               msda_dtype_t input_dtype, size_t* bytes) {
+    if (!bytes) return MSDA_ERROR_INVALID_VALUE;
+    msda_dims_t dims;
+    msda_status_t st = dcn_dims(dcn, &dims);
+    if (st != MSDA_SUCCESS) return st;
+    st = check_dims(&dims, input_dtype, true);
+    if (st != MSDA_SUCCESS) return st;
+    *bytes = plan_backward(&dims).bytes;
+    return MSDA_SUCCESS;
+}
+
+msda_status_t msda_dcn_backward(const msda_dcn_dims_t* dcn, msda_dtype_t input_dtype,
+                                const void* input, const float* offset, const float* mask,
+                                const float* grad_output, float* grad_input, float* grad_offset,
+                                float* grad_mask, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+    msda_dims_t dims;
+    msda_status_t st = dcn_dims(dcn, &dims);
+    if (st != MSDA_SUCCESS) return st;
+    st = check_dims(&dims, input_dtype, true);
+    if (st != MSDA_SUCCESS) return st;
+    const Sizes n = sizes_of(&dims);
+    if ((n.value && !input) || (n.points && (!offset || !mask)) || (n.out && !grad_output))
+        return MSDA_ERROR_INVALID_VALUE;
+    if (!aligned(input, 16) || !aligned(grad_output, 16) || !aligned(grad_input, 16) ||
+        !aligned(offset, 8) || !aligned(grad_offset, 8) || !aligned(mask, 4) ||
+        !aligned(grad_mask, 4) || !aligned(workspace, kWorkspaceAlign))
+        return MSDA_ERROR_INVALID_VALUE;
+    const BwdPlan pl = plan_backward(&dims);
+    if (grad_input && n.value && (!workspace || workspace_bytes < pl.bytes))
+        return MSDA_ERROR_INVALID_VALUE;
+    Params p = make_params(&dims, input_dtype, input, nullptr, nullptr, nullptr, mask);
+    dcn_params(p, dcn);
+    p.off = offset;
+    p.grad_out = grad_output;
+    p.grad_value = grad_input;
+    p.grad_off = grad_offset;
+    p.grad_attn = grad_mask;
+    const Kernels k = pick(input_dtype, dims.D);
+    if (!k.point_dcn) return MSDA_ERROR_NOT_SUPPORTED;
+    if (grad_input && n.value) {
+        st = launch_grad_value(p, pl, &dims, k.bin_dcn, k.tile, workspace, stream);
+        if (st != MSDA_SUCCESS) return st;
+    }
+    if (p.T == 0 || (!grad_offset && !grad_mask)) return MSDA_SUCCESS;
+    return launch(k.point_dcn, ((int64_t)p.T + k.tuples_per_block - 1) / k.tuples_per_block, p,
+                  stream);
 }
 
 msda_status_t msda_check_tables(const int64_t* host_spatial_shapes,

@@ -256,3 +256,80 @@ def generate_layer(w: Workload, offset_px=8.0):
     x["spatial_shapes"] = np.asarray(w.shapes, np.int64).reshape(L, 2)
     x["level_start_index"] = w.level_start_index()
     return x
+
+
+@dataclass(frozen=True)
+class DcnWorkload:
+    """One synthetic workload of the grouped single-level aggregation (DCNv3):
+    input [B, H, W, G, D], a kernel_h x kernel_w grid per output pixel."""
+    name: str
+    B: int
+    H: int
+    W: int
+    G: int
+    D: int
+    kernel: Tuple[int, int] = (3, 3)
+    stride: Tuple[int, int] = (1, 1)
+    pad: Tuple[int, int] = (1, 1)
+    dilation: Tuple[int, int] = (1, 1)
+    sigma_px: float = 1.0
+    value_dtype: str = "f32"
+    seed: int = 0
+    note: str = field(default="", compare=False)
+
+    @property
+    def K(self):
+        return self.kernel[0] * self.kernel[1]
+
+    @property
+    def out_size(self):
+        return ((self.H + 2 * self.pad[0] - self.dilation[0] * (self.kernel[0] - 1) - 1)
+                // self.stride[0] + 1,
+                (self.W + 2 * self.pad[1] - self.dilation[1] * (self.kernel[1] - 1) - 1)
+                // self.stride[1] + 1)
+
+    @property
+    def points(self):
+        Ho, Wo = self.out_size
+        return self.B * Ho * Wo * self.G * self.K
+
+
+# InternImage-style stages on the 800x1333 detection input: 16 channels per
+# group at every stage (64 channels in 4 groups at stride 4, 128 in 8 at
+# stride 8), 3x3 grids (deformable-attention practice guide, sections 4.2 and
+# 5.2: G between 4 and 16, G=8 with K=9 as the typical pairing).
+DCN_WORKLOADS = {
+    "dcn_tiny": DcnWorkload("dcn_tiny", B=1, H=6, W=7, G=2, D=8, sigma_px=1.0, seed=2001,
+                            note="tiny 3x3 fp32 fwd+bwd"),
+    "dcnv3_stage2": DcnWorkload("dcnv3_stage2", B=4, H=100, W=167, G=8, D=16, sigma_px=2.0,
+                                seed=2002, note="stride-8 stage of the 800x1333 input, "
+                                                "C=128 in 8 groups, 3x3, fp32 fwd+bwd"),
+    "dcnv3_stage1": DcnWorkload("dcnv3_stage1", B=2, H=200, W=334, G=4, D=16, sigma_px=2.0,
+                                seed=2003, note="stride-4 stage of the 800x1333 input, "
+                                                "C=64 in 4 groups, 3x3, fp32 fwd+bwd"),
+}
+
+
+def generate_dcn(w: DcnWorkload):
+    """Seeded inputs of a DCNv3 workload: input normal (bf16-rounded for bf16
+    workloads), offsets normal with standard deviation sigma_px pixels,
+    modulation scalars a softmax over the K grid points of normal logits (the
+    normalization InternImage applies; the aggregation itself uses them as
+    given), upstream gradient normal."""
+    rng = np.random.default_rng(w.seed)
+    Ho, Wo = w.out_size
+    x = {}
+    inp = rng.standard_normal((w.B, w.H, w.W, w.G, w.D), dtype=np.float32)
+    off = (rng.standard_normal((w.B, Ho, Wo, w.G, w.K, 2)) * w.sigma_px).astype(np.float32)
+    z = rng.standard_normal((w.B, Ho, Wo, w.G, w.K))
+    e = np.exp(z - z.max(-1, keepdims=True))
+    x["mask"] = (e / e.sum(-1, keepdims=True)).astype(np.float32)
+    x["offset"] = off
+    x["grad_output"] = rng.standard_normal((w.B, Ho, Wo, w.G * w.D), dtype=np.float32)
+    if w.value_dtype == "bf16":
+        bits = bf16_round(inp)
+        x["input_bf16"] = bits
+        x["input"] = bf16_to_f32(bits)
+    else:
+        x["input"] = inp
+    return x

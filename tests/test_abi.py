@@ -25,7 +25,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == ["msda_backward", "msda_backward_fused",
                                     "msda_backward_fused_workspace_size",
                                     "msda_backward_workspace_size", "msda_check_tables",
-                                    "msda_forward", "msda_forward_fused",
+                                    "msda_dcn_backward", "msda_dcn_backward_workspace_size",
+                                    "msda_dcn_forward", "msda_forward", "msda_forward_fused",
                                     "msda_layer_backward", "msda_layer_forward",
                                     "msda_layer_saved_size", "msda_layer_workspace_size",
                                     "msda_linear_backward",
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = msda.library()
-    assert lib.msda_version() == 400
+    assert lib.msda_version() == 500
     for s in range(4):
         assert len(lib.msda_status_string(s)) > 0
     assert lib.msda_status_string(99) == b"unknown status"
@@ -248,3 +249,34 @@ def test_layer_sizes_and_checks():
     # a weight missing
     params.attn_weight = None
     assert lib.msda_layer_forward(*args, FAKE, a.value, None) == INVALID
+
+
+def dcn_dims(**kw):
+    d = dict(B=1, H=6, W=7, G=2, D=8, kernel_h=3, kernel_w=3, stride_h=1, stride_w=1, pad_h=1,
+             pad_w=1, dilation_h=1, dilation_w=1, H_out=6, W_out=7)
+    d.update(kw)
+    return _binding.MsdaDcnDims(*[d[f] for f, _ in _binding.MsdaDcnDims._fields_])
+
+
+def test_dcn_argument_checks():
+    lib = msda.library()
+    fwd = lambda d, **p: lib.msda_dcn_forward(  # noqa: E731
+        None if d is None else ctypes.byref(d), 0, p.get("inp", FAKE), p.get("off", FAKE),
+        p.get("mask", FAKE), p.get("out", FAKE), None)
+    assert fwd(None) == INVALID
+    for bad in (dict(H=0), dict(G=0), dict(kernel_w=0), dict(stride_h=0), dict(pad_w=-1),
+                dict(dilation_h=0), dict(H_out=-1), dict(B=-1)):
+        assert fwd(dcn_dims(**bad)) == INVALID, bad
+    assert fwd(dcn_dims(D=12)) == UNSUPPORTED
+    assert fwd(dcn_dims(W_out=1 << 24)) == UNSUPPORTED
+    for key in ("inp", "off", "mask", "out"):
+        assert fwd(dcn_dims(), **{key: None}) == INVALID, key
+    assert fwd(dcn_dims(), off=ctypes.c_void_p(0x10004)) == INVALID
+    n = ctypes.c_size_t(0)
+    assert lib.msda_dcn_backward_workspace_size(ctypes.byref(dcn_dims()), 0, ctypes.byref(n)) == 0
+    assert n.value > 0 and n.value % 256 == 0
+    bwd = lambda ws, nbytes: lib.msda_dcn_backward(  # noqa: E731
+        ctypes.byref(dcn_dims()), 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, ws,
+        ctypes.c_size_t(nbytes), None)
+    assert bwd(None, 0) == INVALID
+    assert bwd(FAKE, n.value - 1) == INVALID
