@@ -67,15 +67,16 @@ extern "C" {
 #endif
 
 #define MSDA_VERSION_MAJOR 0
-#define MSDA_VERSION_MINOR 5
+#define MSDA_VERSION_MINOR 6
 #define MSDA_VERSION_PATCH 0
 
 /* Largest number of feature levels the kernels accept. */
 #define MSDA_MAX_LEVELS 16
 
 typedef enum {
-    MSDA_DTYPE_F32 = 0,  /* value stored as IEEE binary32            */
-    MSDA_DTYPE_BF16 = 1  /* value stored as bfloat16 (fp32 math)      */
+    MSDA_DTYPE_F32 = 0,  /* IEEE binary32                             */
+    MSDA_DTYPE_BF16 = 1, /* bfloat16 (fp32 math)                       */
+    MSDA_DTYPE_F16 = 2   /* IEEE binary16 (fp32 math)                  */
 } msda_dtype_t;
 
 typedef enum {
@@ -153,6 +154,40 @@ msda_status_t msda_backward(const msda_dims_t *dims, msda_dtype_t value_dtype,
  * backward's size checks would. No HIP call. */
 msda_status_t msda_backward_workspace_size(const msda_dims_t *dims, msda_dtype_t value_dtype,
                                            size_t *bytes);
+
+/*
+ * Reduced-precision storage (guide, section 4.1 and the CSDN explainer's
+ * notes on mixed precision): the tensors of the core that may be stored
+ * narrower than fp32. The arithmetic stays fp32: narrow inputs are widened
+ * exactly, a narrow grad_value is the fp32 result rounded to nearest even.
+ *   value       F32, BF16 or F16
+ *   locations   sampling_locations and attention_weights: F32 or F16
+ *               (binary16 pairs (x, y) and scalars, same layouts)
+ *   grad_value  the backward's value gradient: F32 or BF16
+ * The location gradients stay fp32. Alignment of F16 locations 4-byte, F16
+ * weights 2-byte; the rest as msda_forward / msda_backward.
+ */
+typedef struct {
+    msda_dtype_t value;
+    msda_dtype_t locations;
+    msda_dtype_t grad_value;
+} msda_precision_t;
+
+/* msda_forward with the storage precisions of *precision. */
+msda_status_t msda_forward_ex(const msda_dims_t *dims, const msda_precision_t *precision,
+                              const void *value, const int64_t *spatial_shapes,
+                              const int64_t *level_start_index, const void *sampling_locations,
+                              const void *attention_weights, float *output, hipStream_t stream);
+
+/* msda_backward with the storage precisions of *precision (workspace size as
+ * msda_backward_workspace_size). */
+msda_status_t msda_backward_ex(const msda_dims_t *dims, const msda_precision_t *precision,
+                               const void *value, const int64_t *spatial_shapes,
+                               const int64_t *level_start_index, const void *sampling_locations,
+                               const void *attention_weights, const float *grad_output,
+                               void *grad_value, float *grad_sampling_locations,
+                               float *grad_attention_weights, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Fused front-end: the same core with its two preceding model steps done

@@ -15,6 +15,7 @@ LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsda.so")
 
 MSDA_DTYPE_F32 = 0
 MSDA_DTYPE_BF16 = 1
+MSDA_DTYPE_F16 = 2
 STATUS = {0: "MSDA_SUCCESS", 1: "MSDA_ERROR_INVALID_VALUE", 2: "MSDA_ERROR_NOT_SUPPORTED",
           3: "MSDA_ERROR_LAUNCH"}
 
@@ -33,6 +34,10 @@ class MsdaLayerParams(ctypes.Structure):
 
 class MsdaLayerGrads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in LAYER_PARAMS]
+
+
+class MsdaPrecision(ctypes.Structure):
+    _fields_ = [("value", ctypes.c_int), ("locations", ctypes.c_int), ("grad_value", ctypes.c_int)]
 
 
 class MsdaDcnDims(ctypes.Structure):
@@ -112,6 +117,13 @@ def library():
         lib.msda_dcn_backward_workspace_size.restype = ctypes.c_int
         lib.msda_dcn_backward_workspace_size.argtypes = [dp, ctypes.c_int,
                                                          ctypes.POINTER(ctypes.c_size_t)]
+        pp = ctypes.POINTER(MsdaPrecision)
+        lib.msda_forward_ex.restype = ctypes.c_int
+        lib.msda_forward_ex.argtypes = [ctypes.POINTER(MsdaDims), pp, vp, i64p, i64p, vp, vp, fp,
+                                        vp]
+        lib.msda_backward_ex.restype = ctypes.c_int
+        lib.msda_backward_ex.argtypes = [ctypes.POINTER(MsdaDims), pp, vp, i64p, i64p, vp, vp, fp,
+                                         vp, fp, fp, vp, ctypes.c_size_t, vp]
         lib.msda_backward_fused_workspace_size.restype = ctypes.c_int
         lib.msda_backward_fused_workspace_size.argtypes = [ctypes.POINTER(MsdaDims), ctypes.c_int,
                                                            ctypes.POINTER(ctypes.c_size_t)]
@@ -154,23 +166,35 @@ def _check(t, name, dtypes, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+VALUE_DTYPES = (torch.float32, torch.bfloat16, torch.float16)
+
+
 def _value_dtype(value):
     if value.dtype == torch.float32:
         return MSDA_DTYPE_F32
     if value.dtype == torch.bfloat16:
         return MSDA_DTYPE_BF16
-    raise ValueError(f"value dtype {value.dtype} is not supported (float32 or bfloat16)")
+    if value.dtype == torch.float16:
+        return MSDA_DTYPE_F16
+    raise ValueError(f"value dtype {value.dtype} is not supported (float32, bfloat16, float16)")
+
+
+def _precision(value, sampling_locations, grad_value_dtype=torch.float32):
+    return MsdaPrecision(_value_dtype(value),
+                         MSDA_DTYPE_F16 if sampling_locations.dtype == torch.float16
+                         else MSDA_DTYPE_F32,
+                         MSDA_DTYPE_BF16 if grad_value_dtype == torch.bfloat16 else MSDA_DTYPE_F32)
 
 
 def _common(value, spatial_shapes, level_start_index, sampling_locations, attention_weights):
     dev = value.device
     if dev.type != "cuda":
         raise ValueError("value must be a GPU tensor")
-    _check(value, "value", (torch.float32, torch.bfloat16), dev)
+    _check(value, "value", VALUE_DTYPES, dev)
     _check(spatial_shapes, "spatial_shapes", (torch.int64,), dev)
     _check(level_start_index, "level_start_index", (torch.int64,), dev)
-    _check(sampling_locations, "sampling_locations", (torch.float32,), dev)
-    _check(attention_weights, "attention_weights", (torch.float32,), dev)
+    _check(sampling_locations, "sampling_locations", (torch.float32, torch.float16), dev)
+    _check(attention_weights, "attention_weights", (sampling_locations.dtype,), dev)
     dims = _dims(value, spatial_shapes, sampling_locations, attention_weights)
     if tuple(level_start_index.shape) != (dims.L,):
         raise ValueError("level_start_index must be [L]")
@@ -189,10 +213,11 @@ def msda_forward(value, spatial_shapes, level_start_index, sampling_locations, a
         _check(output, "output", (torch.float32,), dev)
         if output.numel() != dims.B * dims.Nq * dims.M * dims.D:
             raise ValueError("output has the wrong number of elements")
-    st = library().msda_forward(ctypes.byref(dims), _value_dtype(value), _ptr(value),
-                                _ptr(spatial_shapes), _ptr(level_start_index),
-                                _ptr(sampling_locations), _ptr(attention_weights), _ptr(output),
-                                _stream(dev, stream))
+    pr = _precision(value, sampling_locations)
+    st = library().msda_forward_ex(ctypes.byref(dims), ctypes.byref(pr), _ptr(value),
+                                   _ptr(spatial_shapes), _ptr(level_start_index),
+                                   _ptr(sampling_locations), _ptr(attention_weights), _ptr(output),
+                                   _stream(dev, stream))
     if st != 0:
         raise MsdaError(st, "msda_forward")
     return output
@@ -214,30 +239,35 @@ def msda_backward_workspace_size(value, sampling_locations, D=None):
 def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,
                   grad_output, grad_value=None, grad_sampling_locations=None,
                   grad_attention_weights=None, needs=(True, True, True), workspace=None,
-                  stream=None):
-    """Core backward (include/msda.h msda_backward). Returns (grad_value,
-    grad_sampling_locations, grad_attention_weights), fp32; an entry of
-    ``needs`` set to False skips (and returns None for) that gradient.
-    ``workspace`` (a uint8 GPU tensor of at least msda_backward_workspace_size
-    bytes) is allocated here when not given and grad_value is needed."""
+                  stream=None, grad_value_dtype=torch.float32):
+    """Core backward (include/msda.h msda_backward / msda_backward_ex).
+    Returns (grad_value, grad_sampling_locations, grad_attention_weights);
+    the location and weight gradients are fp32, grad_value is fp32 or, with
+    ``grad_value_dtype=torch.bfloat16``, bf16. An entry of ``needs`` set to
+    False skips (and returns None for) that gradient. ``workspace`` (a uint8
+    GPU tensor of at least msda_backward_workspace_size bytes) is allocated
+    here when not given and grad_value is needed."""
     dev, dims = _common(value, spatial_shapes, level_start_index, sampling_locations,
                         attention_weights)
     _check(grad_output, "grad_output", (torch.float32,), dev)
     if grad_output.numel() != dims.B * dims.Nq * dims.M * dims.D:
         raise ValueError("grad_output has the wrong number of elements")
+    if grad_value_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("grad_value_dtype must be float32 or bfloat16")
     outs = []
-    for need, given, shape, name in (
-            (needs[0], grad_value, (dims.B, dims.Nv, dims.M, dims.D), "grad_value"),
+    for need, given, shape, name, dt in (
+            (needs[0], grad_value, (dims.B, dims.Nv, dims.M, dims.D), "grad_value",
+             grad_value_dtype),
             (needs[1], grad_sampling_locations, tuple(sampling_locations.shape),
-             "grad_sampling_locations"),
+             "grad_sampling_locations", torch.float32),
             (needs[2], grad_attention_weights, tuple(attention_weights.shape),
-             "grad_attention_weights")):
+             "grad_attention_weights", torch.float32)):
         if not need:
             outs.append(None)
         elif given is None:
-            outs.append(torch.empty(shape, dtype=torch.float32, device=dev))
+            outs.append(torch.empty(shape, dtype=dt, device=dev))
         else:
-            _check(given, name, (torch.float32,), dev)
+            _check(given, name, (dt,), dev)
             if tuple(given.shape) != shape:
                 raise ValueError(f"{name} must have shape {shape}")
             outs.append(given)
@@ -255,12 +285,13 @@ def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, 
         ws_bytes = workspace.numel() * workspace.element_size()
     else:
         workspace = None
-    st = library().msda_backward(ctypes.byref(dims), _value_dtype(value), _ptr(value),
-                                 _ptr(spatial_shapes), _ptr(level_start_index),
-                                 _ptr(sampling_locations), _ptr(attention_weights),
-                                 _ptr(grad_output), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
-                                 _ptr(workspace), ctypes.c_size_t(ws_bytes),
-                                 _stream(dev, stream))
+    pr = _precision(value, sampling_locations, grad_value_dtype)
+    st = library().msda_backward_ex(ctypes.byref(dims), ctypes.byref(pr), _ptr(value),
+                                    _ptr(spatial_shapes), _ptr(level_start_index),
+                                    _ptr(sampling_locations), _ptr(attention_weights),
+                                    _ptr(grad_output), _ptr(outs[0]), _ptr(outs[1]),
+                                    _ptr(outs[2]), _ptr(workspace), ctypes.c_size_t(ws_bytes),
+                                    _stream(dev, stream))
     if st != 0:
         raise MsdaError(st, "msda_backward")
     return tuple(outs)
@@ -293,10 +324,16 @@ class MSDeformAttnFunction(torch.autograd.Function):
     def backward(ctx, grad_output):
         value, shapes, lsi, loc, attn = ctx.saved_tensors
         needs = (ctx.needs_input_grad[0], ctx.needs_input_grad[3], ctx.needs_input_grad[4])
+        # a bf16 value takes its gradient as bf16 straight from the kernel
+        gdt = torch.bfloat16 if value.dtype == torch.bfloat16 else torch.float32
         gv, gl, ga = msda_backward(value, shapes, lsi, loc, attn, grad_output.contiguous(),
-                                   needs=needs)
-        if gv is not None and value.dtype != torch.float32:
+                                   needs=needs, grad_value_dtype=gdt)
+        if gv is not None and gv.dtype != value.dtype:
             gv = gv.to(value.dtype)
+        if gl is not None and gl.dtype != loc.dtype:
+            gl = gl.to(loc.dtype)
+        if ga is not None and ga.dtype != attn.dtype:
+            ga = ga.to(attn.dtype)
         return gv, None, None, gl, ga
 
 
@@ -313,7 +350,7 @@ def _common_fused(value, spatial_shapes, level_start_index, reference_points, sa
     dev = value.device
     if dev.type != "cuda":
         raise ValueError("value must be a GPU tensor")
-    _check(value, "value", (torch.float32, torch.bfloat16), dev)
+    _check(value, "value", VALUE_DTYPES, dev)
     _check(spatial_shapes, "spatial_shapes", (torch.int64,), dev)
     _check(level_start_index, "level_start_index", (torch.int64,), dev)
     _check(reference_points, "reference_points", (torch.float32,), dev)
@@ -649,7 +686,7 @@ def _dcn_dims(inp, offset, kernel, stride, pad, dilation):
 
 
 def _dcn_checks(inp, offset, mask, dev):
-    _check(inp, "input", (torch.float32, torch.bfloat16), dev)
+    _check(inp, "input", VALUE_DTYPES, dev)
     _check(offset, "offset", (torch.float32,), dev)
     _check(mask, "mask", (torch.float32,), dev)
     if tuple(mask.shape) != tuple(offset.shape[:5]):

@@ -52,12 +52,27 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 struct bf16_t {
     uint16_t bits;
 };
+struct f16_t {
+    uint16_t bits;
+};
 
 // Reinterpret bits as fp32. Takes the word by value on purpose: this compiler
 // miscompiles __builtin_bit_cast applied directly to an element of an
 // ext_vector_type value (it reads element 0 whatever the index).
 __device__ inline float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ inline uint32_t as_uint(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// IEEE binary16 in the low 16 bits -> fp32 (exact).
+__device__ inline float half_bits_to_float(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(bits & 0xFFFFu));
+}
+
+// fp32 -> bf16 bits, rounded to nearest even (NaN stays a quiet NaN).
+__device__ inline uint32_t float_to_bf16_bits(float f) {
+    const uint32_t u = as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
 
 // A 16-byte load marked non-temporal: for data read exactly once (the bin
 // entries), so that it does not push reused rows out of L2.
@@ -88,6 +103,20 @@ struct Elem<bf16_t> {
         for (int i = 0; i < 4; ++i) {
             v[2 * i] = as_float(raw[i] << 16);
             v[2 * i + 1] = as_float(raw[i] & 0xFFFF0000u);
+        }
+    }
+};
+
+template <>
+struct Elem<f16_t> {
+    static constexpr int kPerLane = 8;
+    static constexpr int kBytes = 2;
+    __device__ static inline void widen(u32x4 raw, float* v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w = raw[i];
+            v[2 * i] = half_bits_to_float(w);
+            v[2 * i + 1] = half_bits_to_float(w >> 16);
         }
     }
 };
@@ -142,7 +171,8 @@ struct Params {
 enum FrontEnd : int {
     kFeCore = 0,    // locations and weights given
     kFeFused = 1,   // reference point + offset / (W, H), softmax of logits
-    kFeDcn = 2      // convolution grid + pixel offset, modulation scalars given
+    kFeDcn = 2,     // convolution grid + pixel offset, modulation scalars given
+    kFeCoreHalf = 3 // locations and weights given as IEEE binary16
 };
 
 // The inputs of point j (level l) of tuple t as loaded: its location and
@@ -172,6 +202,12 @@ __device__ inline PointIn load_point(const Params& p, int t, int j, int l) {
         in.uv = *reinterpret_cast<const float2*>(p.ref + 2 * (bq * p.L + l));
         in.off = *reinterpret_cast<const float2*>(p.off + 2 * pt);
         in.z = p.logits[pt];
+    } else if constexpr (FE == kFeCoreHalf) {
+        // binary16 pairs and scalars, widened exactly
+        const uint32_t xy = reinterpret_cast<const uint32_t*>(p.loc)[pt];
+        in.uv = make_float2(half_bits_to_float(xy), half_bits_to_float(xy >> 16));
+        in.off = make_float2(0.0f, 0.0f);
+        in.z = half_bits_to_float(reinterpret_cast<const uint16_t*>(p.attn)[pt]);
     } else {
         in.uv = *reinterpret_cast<const float2*>(p.loc + 2 * pt);
         in.off = make_float2(0.0f, 0.0f);
@@ -958,7 +994,7 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
 // (b, m) = x mod 8, so an XCD's L2 sees only its own (b, m)), coarse levels
 // first: those tiles have the most points per pixel and the longest lists, and
 // start first.
-template <int D>
+template <int D, bool kBf16Out>
 __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
     using TS = TileShape<D>;
     constexpr int TW = TS::TW, G = TS::G, kCells = TS::kCells;
@@ -1121,7 +1157,15 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
                 const int y = y_base + yy;
                 if (y < L_.H) {
                     const size_t rowi = (size_t)b * p.Nv + L_.start + (size_t)y * L_.W + x;
-                    *reinterpret_cast<float4*>(p.grad_value + (rowi * p.M + m) * D + r * 4) = acc[yy];
+                    const size_t e = (rowi * p.M + m) * D + r * 4;
+                    if constexpr (kBf16Out) {
+                        // rounded once, from the fp32 sum
+                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.grad_value) + e) =
+                            make_uint2(float_to_bf16_bits(acc[yy].x) | (float_to_bf16_bits(acc[yy].y) << 16),
+                                       float_to_bf16_bits(acc[yy].z) | (float_to_bf16_bits(acc[yy].w) << 16));
+                    } else {
+                        *reinterpret_cast<float4*>(p.grad_value + e) = acc[yy];
+                    }
                 }
             }
         }
@@ -1207,7 +1251,8 @@ msda_status_t check_dims(const msda_dims_t* d, msda_dtype_t dt, bool backward) {
     if (!d) return MSDA_ERROR_INVALID_VALUE;
     if (d->B < 0 || d->Nq < 0 || d->K < 0 || d->M < 1 || d->Nv < 1 || d->L < 1 || d->D < 1)
         return MSDA_ERROR_INVALID_VALUE;
-    if (dt != MSDA_DTYPE_F32 && dt != MSDA_DTYPE_BF16) return MSDA_ERROR_INVALID_VALUE;
+    if (dt != MSDA_DTYPE_F32 && dt != MSDA_DTYPE_BF16 && dt != MSDA_DTYPE_F16)
+        return MSDA_ERROR_INVALID_VALUE;
     if (d->L > MSDA_MAX_LEVELS) return MSDA_ERROR_NOT_SUPPORTED;
     if (d->D != 8 && d->D != 16 && d->D != 32 && d->D != 64) return MSDA_ERROR_NOT_SUPPORTED;
     const int64_t lim = k2GiB - 1;
@@ -1283,7 +1328,7 @@ Params make_params(const msda_dims_t* d, msda_dtype_t dt, const void* value, con
     p.LK = (int)(d->L * d->K);
     p.T = (int)(d->B * d->Nq * d->M);
     const int64_t elems = d->B * d->Nv * d->M * d->D;
-    p.value_bytes = (uint32_t)(elems * (dt == MSDA_DTYPE_BF16 ? 2 : 4));
+    p.value_bytes = (uint32_t)(elems * (dt == MSDA_DTYPE_F32 ? 4 : 2));
     return p;
 }
 
@@ -1301,9 +1346,9 @@ Sizes sizes_of(const msda_dims_t* d) {
 
 // Blocks of the tile kernel that fit on one CU, asked of the runtime once per
 // kernel and kept.
-int tile_blocks_per_cu(int64_t D, const void* kernel) {
-    static std::atomic<int> known[4];
-    std::atomic<int>& slot = known[D == 8 ? 0 : D == 16 ? 1 : D == 32 ? 2 : 3];
+int tile_blocks_per_cu(int64_t D, const void* kernel, bool bf16_out) {
+    static std::atomic<int> known[8];
+    std::atomic<int>& slot = known[(D == 8 ? 0 : D == 16 ? 1 : D == 32 ? 2 : 3) + (bf16_out ? 4 : 0)];
     int n = slot.load(std::memory_order_relaxed);
     if (n > 0) return n;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kBlock, 0) != hipSuccess || n < 1) n = 1;
@@ -1330,6 +1375,10 @@ struct Kernels {
     const void* fwd_dcn = nullptr;
     const void* point_dcn = nullptr;
     const void* bin_dcn = nullptr;
+    const void* fwd_half = nullptr;     // binary16 locations and weights
+    const void* point_half = nullptr;
+    const void* bin_half = nullptr;
+    const void* tile_bf16 = nullptr;    // grad_value stored as bf16
     int tuples_per_block = 0;
 };
 
@@ -1345,7 +1394,11 @@ Kernels kernels_for() {
     k.fwd_dcn = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D, kFeDcn>);
     k.point_dcn = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D, kFeDcn>);
     k.bin_dcn = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeDcn>);
-    k.tile = reinterpret_cast<const void*>(&msda_tile_kernel<D>);
+    k.fwd_half = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D, kFeCoreHalf>);
+    k.point_half = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D, kFeCoreHalf>);
+    k.bin_half = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCoreHalf>);
+    k.tile = reinterpret_cast<const void*>(&msda_tile_kernel<D, false>);
+    k.tile_bf16 = reinterpret_cast<const void*>(&msda_tile_kernel<D, true>);
     k.tuples_per_block = Shape<T, D>::TPW * kWavesPerBlock;
     return k;
 }
@@ -1355,8 +1408,10 @@ Kernels pick(msda_dtype_t dt, int64_t D) {
     if (D == DD) return kernels_for<T, DD>();
     if (dt == MSDA_DTYPE_F32) {
         MSDA_PICK(float, 8) MSDA_PICK(float, 16) MSDA_PICK(float, 32) MSDA_PICK(float, 64)
-    } else {
+    } else if (dt == MSDA_DTYPE_BF16) {
         MSDA_PICK(bf16_t, 8) MSDA_PICK(bf16_t, 16) MSDA_PICK(bf16_t, 32) MSDA_PICK(bf16_t, 64)
+    } else if (dt == MSDA_DTYPE_F16) {
+        MSDA_PICK(f16_t, 8) MSDA_PICK(f16_t, 16) MSDA_PICK(f16_t, 32) MSDA_PICK(f16_t, 64)
     }
 #undef MSDA_PICK
     return Kernels();
@@ -1365,7 +1420,7 @@ Kernels pick(msda_dtype_t dt, int64_t D) {
 // grad_value: the bin kernel, then the tile kernel, on the workspace of `pl`.
 msda_status_t launch_grad_value(Params& p, const BwdPlan& pl, const msda_dims_t* dims,
                                 const void* bin, const void* tile, void* workspace,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool bf16_out = false) {
     p.nW = (int)pl.nW;
     p.Qc = (int)pl.Qc;
     p.t_stride = (int)pl.t_stride;
@@ -1383,7 +1438,7 @@ msda_status_t launch_grad_value(Params& p, const BwdPlan& pl, const msda_dims_t*
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return MSDA_ERROR_LAUNCH;
-    const int per_cu = tile_blocks_per_cu(dims->D, tile);
+    const int per_cu = tile_blocks_per_cu(dims->D, tile, bf16_out);
     const int64_t items = BM * pl.t_stride;
     const int64_t resident = ((int64_t)per_cu * (cus > 0 ? cus : 1) + 7) / 8 * 8;
     const int64_t grid = items < resident ? ((items + 7) / 8) * 8 : resident;
@@ -1413,28 +1468,112 @@ FusedPlan plan_backward_fused(const msda_dims_t* d) {
 
 extern "C" {
 
-msda_status_t msda_forward(const msda_dims_t* dims, msda_dtype_t value_dtype, const void* value,
+}  // extern "C"
+
+namespace {
+
+msda_status_t check_precision(const msda_precision_t* pr) {
+    if (!pr) return MSDA_ERROR_INVALID_VALUE;
+    if (pr->value != MSDA_DTYPE_F32 && pr->value != MSDA_DTYPE_BF16 && pr->value != MSDA_DTYPE_F16)
+        return MSDA_ERROR_INVALID_VALUE;
+    if (pr->locations != MSDA_DTYPE_F32 && pr->locations != MSDA_DTYPE_F16)
+        return MSDA_ERROR_INVALID_VALUE;
+    if (pr->grad_value != MSDA_DTYPE_F32 && pr->grad_value != MSDA_DTYPE_BF16)
+        return MSDA_ERROR_INVALID_VALUE;
+    return MSDA_SUCCESS;
+}
+
+msda_status_t forward_impl(const msda_dims_t* dims, const msda_precision_t& pr, const void* value,
                            const int64_t* spatial_shapes, const int64_t* level_start_index,
-                           const float* sampling_locations, const float* attention_weights,
+                           const void* sampling_locations, const void* attention_weights,
                            float* output, hipStream_t stream) {
-    const msda_status_t st = check_dims(dims, value_dtype, false);
+    const msda_status_t st = check_dims(dims, pr.value, false);
     if (st != MSDA_SUCCESS) return st;
+    const bool half = pr.locations == MSDA_DTYPE_F16;
     const Sizes n = sizes_of(dims);
     // a tensor with no elements may come as NULL
     if ((n.value && !value) || !spatial_shapes || !level_start_index ||
         (n.points && (!sampling_locations || !attention_weights)) || (n.out && !output))
         return MSDA_ERROR_INVALID_VALUE;
-    if (!aligned(value, 16) || !aligned(output, 16) || !aligned(sampling_locations, 8) ||
-        !aligned(attention_weights, 4) || !aligned(spatial_shapes, 8) ||
+    if (!aligned(value, 16) || !aligned(output, 16) || !aligned(sampling_locations, half ? 4 : 8) ||
+        !aligned(attention_weights, half ? 2 : 4) || !aligned(spatial_shapes, 8) ||
         !aligned(level_start_index, 8))
         return MSDA_ERROR_INVALID_VALUE;
-    Params p = make_params(dims, value_dtype, value, spatial_shapes, level_start_index,
-                           sampling_locations, attention_weights);
+    Params p = make_params(dims, pr.value, value, spatial_shapes, level_start_index,
+                           static_cast<const float*>(sampling_locations),
+                           static_cast<const float*>(attention_weights));
     p.out = output;
     if (p.T == 0) return MSDA_SUCCESS;
-    const Kernels k = pick(value_dtype, dims->D);
-    if (!k.fwd) return MSDA_ERROR_NOT_SUPPORTED;
-    return launch(k.fwd, ((int64_t)p.T + k.tuples_per_block - 1) / k.tuples_per_block, p, stream);
+    const Kernels k = pick(pr.value, dims->D);
+    const void* kern = half ? k.fwd_half : k.fwd;
+    if (!kern) return MSDA_ERROR_NOT_SUPPORTED;
+    return launch(kern, ((int64_t)p.T + k.tuples_per_block - 1) / k.tuples_per_block, p, stream);
+}
+
+msda_status_t backward_impl(const msda_dims_t* dims, const msda_precision_t& pr, const void* value,
+                            const int64_t* spatial_shapes, const int64_t* level_start_index,
+                            const void* sampling_locations, const void* attention_weights,
+                            const float* grad_output, void* grad_value,
+                            float* grad_sampling_locations, float* grad_attention_weights,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const msda_status_t st = check_dims(dims, pr.value, true);
+    if (st != MSDA_SUCCESS) return st;
+    const bool half = pr.locations == MSDA_DTYPE_F16;
+    const bool bf16_out = pr.grad_value == MSDA_DTYPE_BF16;
+    const Sizes n = sizes_of(dims);
+    if ((n.value && !value) || !spatial_shapes || !level_start_index ||
+        (n.points && (!sampling_locations || !attention_weights)) || (n.out && !grad_output))
+        return MSDA_ERROR_INVALID_VALUE;
+    if (!aligned(value, 16) || !aligned(grad_output, 16) || !aligned(grad_value, 16) ||
+        !aligned(sampling_locations, half ? 4 : 8) || !aligned(grad_sampling_locations, 8) ||
+        !aligned(attention_weights, half ? 2 : 4) || !aligned(grad_attention_weights, 4) ||
+        !aligned(spatial_shapes, 8) || !aligned(level_start_index, 8) ||
+        !aligned(workspace, kWorkspaceAlign))
+        return MSDA_ERROR_INVALID_VALUE;
+    const BwdPlan pl = plan_backward(dims);
+    if (grad_value && n.value && (!workspace || workspace_bytes < pl.bytes))
+        return MSDA_ERROR_INVALID_VALUE;
+    Params p = make_params(dims, pr.value, value, spatial_shapes, level_start_index,
+                           static_cast<const float*>(sampling_locations),
+                           static_cast<const float*>(attention_weights));
+    p.grad_out = grad_output;
+    p.grad_value = static_cast<float*>(grad_value);
+    p.grad_loc = grad_sampling_locations;
+    p.grad_attn = grad_attention_weights;
+    const Kernels k = pick(pr.value, dims->D);
+    const void* point = half ? k.point_half : k.point;
+    if (!point) return MSDA_ERROR_NOT_SUPPORTED;
+    if (grad_value && n.value) {
+        const msda_status_t s =
+            launch_grad_value(p, pl, dims, half ? k.bin_half : k.bin,
+                              bf16_out ? k.tile_bf16 : k.tile, workspace, stream, bf16_out);
+        if (s != MSDA_SUCCESS) return s;
+    }
+    if (p.T == 0 || (!grad_sampling_locations && !grad_attention_weights)) return MSDA_SUCCESS;
+    return launch(point, ((int64_t)p.T + k.tuples_per_block - 1) / k.tuples_per_block, p, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+msda_status_t msda_forward(const msda_dims_t* dims, msda_dtype_t value_dtype, const void* value,
+                           const int64_t* spatial_shapes, const int64_t* level_start_index,
+                           const float* sampling_locations, const float* attention_weights,
+                           float* output, hipStream_t stream) {
+    const msda_precision_t pr = {value_dtype, MSDA_DTYPE_F32, MSDA_DTYPE_F32};
+    return forward_impl(dims, pr, value, spatial_shapes, level_start_index, sampling_locations,
+                        attention_weights, output, stream);
+}
+
+msda_status_t msda_forward_ex(const msda_dims_t* dims, const msda_precision_t* precision,
+                              const void* value, const int64_t* spatial_shapes,
+                              const int64_t* level_start_index, const void* sampling_locations,
+                              const void* attention_weights, float* output, hipStream_t stream) {
+    const msda_status_t st = check_precision(precision);
+    if (st != MSDA_SUCCESS) return st;
+    return forward_impl(dims, *precision, value, spatial_shapes, level_start_index,
+                        sampling_locations, attention_weights, output, stream);
 }
 
 msda_status_t msda_backward_workspace_size(const msda_dims_t* dims, msda_dtype_t value_dtype,
@@ -1452,35 +1591,25 @@ msda_status_t msda_backward(const msda_dims_t* dims, msda_dtype_t value_dtype, c
                             const float* grad_output, float* grad_value,
                             float* grad_sampling_locations, float* grad_attention_weights,
                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    const msda_status_t st = check_dims(dims, value_dtype, true);
+    const msda_precision_t pr = {value_dtype, MSDA_DTYPE_F32, MSDA_DTYPE_F32};
+    return backward_impl(dims, pr, value, spatial_shapes, level_start_index, sampling_locations,
+                         attention_weights, grad_output, grad_value, grad_sampling_locations,
+                         grad_attention_weights, workspace, workspace_bytes, stream);
+}
+
+msda_status_t msda_backward_ex(const msda_dims_t* dims, const msda_precision_t* precision,
+                               const void* value, const int64_t* spatial_shapes,
+                               const int64_t* level_start_index, const void* sampling_locations,
+                               const void* attention_weights, const float* grad_output,
+                               void* grad_value, float* grad_sampling_locations,
+                               float* grad_attention_weights, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    const msda_status_t st = check_precision(precision);
     if (st != MSDA_SUCCESS) return st;
-    const Sizes n = sizes_of(dims);
-    if ((n.value && !value) || !spatial_shapes || !level_start_index ||
-        (n.points && (!sampling_locations || !attention_weights)) || (n.out && !grad_output))
-        return MSDA_ERROR_INVALID_VALUE;
-    if (!aligned(value, 16) || !aligned(grad_output, 16) || !aligned(grad_value, 16) ||
-        !aligned(sampling_locations, 8) || !aligned(grad_sampling_locations, 8) ||
-        !aligned(attention_weights, 4) || !aligned(grad_attention_weights, 4) ||
-        !aligned(spatial_shapes, 8) || !aligned(level_start_index, 8) ||
-        !aligned(workspace, kWorkspaceAlign))
-        return MSDA_ERROR_INVALID_VALUE;
-    const BwdPlan pl = plan_backward(dims);
-    if (grad_value && n.value && (!workspace || workspace_bytes < pl.bytes))
-        return MSDA_ERROR_INVALID_VALUE;
-    Params p = make_params(dims, value_dtype, value, spatial_shapes, level_start_index,
-                           sampling_locations, attention_weights);
-    p.grad_out = grad_output;
-    p.grad_value = grad_value;
-    p.grad_loc = grad_sampling_locations;
-    p.grad_attn = grad_attention_weights;
-    const Kernels k = pick(value_dtype, dims->D);
-    if (!k.point) return MSDA_ERROR_NOT_SUPPORTED;
-    if (grad_value && n.value) {
-        const msda_status_t s = launch_grad_value(p, pl, dims, k.bin, k.tile, workspace, stream);
-        if (s != MSDA_SUCCESS) return s;
-    }
-    if (p.T == 0 || (!grad_sampling_locations && !grad_attention_weights)) return MSDA_SUCCESS;
-    return launch(k.point, ((int64_t)p.T + k.tuples_per_block - 1) / k.tuples_per_block, p, stream);
+    return backward_impl(dims, *precision, value, spatial_shapes, level_start_index,
+                         sampling_locations, attention_weights, grad_output, grad_value,
+                         grad_sampling_locations, grad_attention_weights, workspace,
+                         workspace_bytes, stream);
 }
 
 msda_status_t msda_forward_fused(const msda_dims_t* dims, msda_dtype_t value_dtype,

@@ -142,7 +142,8 @@ def generate(w: Workload, batch_slice=None):
       value            [B,Nv,M,D] float32 (for bf16 workloads: the bf16-rounded
                        values widened to float32, exactly what the GPU reads)
       value_bf16       [B,Nv,M,D] uint16 bf16 bits (bf16 workloads only)
-      value_f32_orig   the unrounded float32 draws (bf16 workloads only)
+      value_f16        [B,Nv,M,D] float16 (f16 workloads only)
+      value_f32_orig   the unrounded float32 draws (bf16 and f16 workloads)
       spatial_shapes   [L,2] int64 (H, W)
       level_start_index[L] int64
       sampling_locations [B,Nq,M,L,K,2] float32
@@ -187,10 +188,15 @@ def generate(w: Workload, batch_slice=None):
         out["value_bf16"] = bits
         out["value_f32_orig"] = value
         out["value"] = bf16_to_f32(bits)
+    elif w.value_dtype == "f16":
+        half = value.astype(np.float16)          # round to nearest even
+        out["value_f16"] = half
+        out["value_f32_orig"] = value
+        out["value"] = half.astype(np.float32)   # exact
     else:
         out["value"] = value
     if batch_slice is not None:
-        for key in ("value", "value_bf16", "value_f32_orig", "sampling_locations",
+        for key in ("value", "value_bf16", "value_f16", "value_f32_orig", "sampling_locations",
                     "attention_weights", "grad_output", "reference_points_levels",
                     "sampling_offsets", "attention_logits"):
             if key in out:
@@ -330,6 +336,10 @@ def generate_dcn(w: DcnWorkload):
         bits = bf16_round(inp)
         x["input_bf16"] = bits
         x["input"] = bf16_to_f32(bits)
+    elif w.value_dtype == "f16":
+        half = inp.astype(np.float16)
+        x["input_f16"] = half
+        x["input"] = half.astype(np.float32)
     else:
         x["input"] = inp
     return x

@@ -22,11 +22,12 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["msda_backward", "msda_backward_fused",
+    assert declared_functions() == ["msda_backward", "msda_backward_ex", "msda_backward_fused",
                                     "msda_backward_fused_workspace_size",
                                     "msda_backward_workspace_size", "msda_check_tables",
                                     "msda_dcn_backward", "msda_dcn_backward_workspace_size",
-                                    "msda_dcn_forward", "msda_forward", "msda_forward_fused",
+                                    "msda_dcn_forward", "msda_forward", "msda_forward_ex",
+                                    "msda_forward_fused",
                                     "msda_layer_backward", "msda_layer_forward",
                                     "msda_layer_saved_size", "msda_layer_workspace_size",
                                     "msda_linear_backward",
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = msda.library()
-    assert lib.msda_version() == 500
+    assert lib.msda_version() == 600
     for s in range(4):
         assert len(lib.msda_status_string(s)) > 0
     assert lib.msda_status_string(99) == b"unknown status"
@@ -280,3 +281,22 @@ def test_dcn_argument_checks():
         ctypes.c_size_t(nbytes), None)
     assert bwd(None, 0) == INVALID
     assert bwd(FAKE, n.value - 1) == INVALID
+
+
+def test_precision_checks():
+    lib = msda.library()
+    P = _binding.MsdaPrecision
+    fwd = lambda pr, **p: lib.msda_forward_ex(  # noqa: E731
+        ctypes.byref(dims()), None if pr is None else ctypes.byref(pr), FAKE, FAKE, FAKE,
+        p.get("loc", FAKE), p.get("attn", FAKE), FAKE, None)
+    assert fwd(None) == INVALID
+    assert fwd(P(3, 0, 0)) == INVALID          # unknown value type
+    assert fwd(P(0, 1, 0)) == INVALID          # bf16 locations are not offered
+    assert fwd(P(0, 0, 2)) == INVALID          # f16 grad_value is not offered
+    # binary16 locations need 4-byte, weights 2-byte alignment only
+    assert fwd(P(2, 2, 0), loc=ctypes.c_void_p(0x10002)) == INVALID
+    assert fwd(P(0, 0, 0), loc=ctypes.c_void_p(0x10004)) == INVALID
+    bwd = lambda pr, gv: lib.msda_backward_ex(  # noqa: E731
+        ctypes.byref(dims()), ctypes.byref(pr), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, gv, FAKE,
+        FAKE, FAKE, ctypes.c_size_t(1 << 40), None)
+    assert bwd(P(0, 0, 1), ctypes.c_void_p(0x10008)) == INVALID   # bf16 grad_value 16-byte
