@@ -51,7 +51,7 @@ MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix, published
 METRIC = "sampled points/sec (B·Nq·M·L·K) fwd+bwd; achieved HBM GB/s vs peak"
 
 
-def algorithmic_bytes(w, value_bytes_per_elem=4, fused=False):
+def algorithmic_bytes(w, value_bytes_per_elem=4, fused=False, point_bytes=12, grad_value_bytes=4):
     """Compulsory bytes of each launch (each input read once, each output
     written once). Per sampled point: location 8 B + weight 4 B (+ their
     gradients 8 B + 4 B in the backward); fused: offset 8 B + logit 4 B (+
@@ -63,14 +63,15 @@ def algorithmic_bytes(w, value_bytes_per_elem=4, fused=False):
     T = w.B * w.num_queries * w.M
     V = w.B * w.Nv * w.M * w.D
     R = w.B * w.num_queries * w.L * 8 if fused else 0
-    fwd = V * value_bytes_per_elem + P * 12 + T * w.D * 4 + R
+    pb, gb = point_bytes, grad_value_bytes
+    fwd = V * value_bytes_per_elem + P * pb + T * w.D * 4 + R
     # location/weight gradients: value, locations, weights, upstream gradient
     # in; their gradients (12 B per point) out
-    bwd_point = V * value_bytes_per_elem + P * 12 + T * w.D * 4 + P * 12 + 2 * R
+    bwd_point = V * value_bytes_per_elem + P * pb + T * w.D * 4 + P * 12 + 2 * R
     # grad_value: locations, weights, upstream gradient in; grad_value out
-    bwd_value = P * 12 + T * w.D * 4 + V * 4 + R
+    bwd_value = P * pb + T * w.D * 4 + V * gb + R
     # the whole backward reads each input once and writes each gradient once
-    bwd = V * value_bytes_per_elem + P * 12 + T * w.D * 4 + V * 4 + P * 12 + 2 * R
+    bwd = V * value_bytes_per_elem + P * pb + T * w.D * 4 + V * gb + P * 12 + 2 * R
     return {"forward": fwd, "bwd_point": bwd_point, "bwd_value": bwd_value, "backward": bwd,
             "step": fwd + bwd}
 
@@ -448,6 +449,12 @@ def main():
                     help="core: locations and weights given; fused: formed in the kernels "
                          "from reference points, offsets and logits; layer: the whole "
                          "MSDeformAttn layer with its four projections")
+    ap.add_argument("--value-dtype", choices=("workload", "f32", "bf16", "f16"),
+                    default="workload", help="storage of the value tensor (core front-end)")
+    ap.add_argument("--loc-dtype", choices=("f32", "f16"), default="f32",
+                    help="storage of the locations and weights (core front-end)")
+    ap.add_argument("--grad-dtype", choices=("f32", "bf16"), default="f32",
+                    help="storage of grad_value (core front-end)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline sample")
@@ -474,20 +481,33 @@ def main():
     w = wl.WORKLOADS[args.workload]
     if args.frontend == "layer":
         return bench_layer(args, w, dev)
+    narrow = args.value_dtype != "workload" or args.loc_dtype != "f32" or args.grad_dtype != "f32"
+    if narrow and args.frontend != "core":
+        print("--value-dtype/--loc-dtype/--grad-dtype apply to the core front-end",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.value_dtype != "workload":
+        w = w.scaled(value_dtype=args.value_dtype)
     x = wl.generate(w)
     if w.value_dtype == "bf16":
         value = torch.from_numpy(x["value_bf16"].view(np.int16)).to(dev).view(torch.bfloat16)
+    elif w.value_dtype == "f16":
+        value = torch.from_numpy(x["value_f16"]).to(dev)
     else:
         value = torch.from_numpy(x["value"]).to(dev)
     shapes = torch.from_numpy(x["spatial_shapes"]).to(dev)
     lsi = torch.from_numpy(x["level_start_index"]).to(dev)
-    loc = torch.from_numpy(x["sampling_locations"]).to(dev)
-    attn = torch.from_numpy(x["attention_weights"]).to(dev)
+    loc_np, attn_np = x["sampling_locations"], x["attention_weights"]
+    if args.loc_dtype == "f16":
+        loc_np, attn_np = loc_np.astype(np.float16), attn_np.astype(np.float16)
+    loc = torch.from_numpy(loc_np).to(dev)
+    attn = torch.from_numpy(attn_np).to(dev)
     gout = torch.from_numpy(x["grad_output"]).to(dev)
     out = torch.empty(w.B, w.num_queries, w.M * w.D, device=dev)
-    gv = torch.empty(w.B, w.Nv, w.M, w.D, device=dev)
-    gl = torch.empty_like(loc)
-    ga = torch.empty_like(attn)
+    gdt = torch.bfloat16 if args.grad_dtype == "bf16" else torch.float32
+    gv = torch.empty(w.B, w.Nv, w.M, w.D, dtype=gdt, device=dev)
+    gl = torch.empty(loc.shape, dtype=torch.float32, device=dev)
+    ga = torch.empty(attn.shape, dtype=torch.float32, device=dev)
     ws = torch.empty(max(msda.msda_backward_workspace_size(value, loc), 1), dtype=torch.uint8,
                      device=dev)
     backward = w.backward
@@ -519,7 +539,7 @@ def main():
         def bwd(needs=(True, True, True)):
             msda.msda_backward(value, shapes, lsi, loc, attn, gout, grad_value=gv,
                                grad_sampling_locations=gl, grad_attention_weights=ga,
-                               needs=needs, workspace=ws)
+                               needs=needs, workspace=ws, grad_value_dtype=gdt)
 
     def step():
         fwd()
@@ -571,12 +591,14 @@ def main():
 
     ms_per_step = total_ms / args.steps
     pts_per_s = w.points / (ms_per_step * 1e-3)
-    ab = algorithmic_bytes(w, 2 if w.value_dtype == "bf16" else 4, fused)
+    ab = algorithmic_bytes(w, 4 if w.value_dtype == "f32" else 2, fused,
+                           6 if args.loc_dtype == "f16" else 12,
+                           2 if args.grad_dtype == "bf16" else 4)
     kernel_bytes = dict(zip(names, (ab["forward"], ab["bwd_point"], ab["bwd_value"])))
     dom_name = max(kernels, key=kernels.get)
     dom_ms, dom_bytes = kernels[dom_name], kernel_bytes[dom_name]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    measured = read_traffic(w.name + ("_fused" if fused else ""))
+    measured = None if narrow else read_traffic(w.name + ("_fused" if fused else ""))
     traffic = None
     if measured is not None and all(k in measured for k in dom_name.split("+")):
         traffic = sum(measured[k] for k in dom_name.split("+"))
@@ -594,7 +616,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if w.value_dtype == "f32" else "bf16 value, f32 math",
+        "dtype": "f32" if not narrow and w.value_dtype == "f32" else
+                 f"{w.value_dtype} value, {args.loc_dtype} locations and weights, "
+                 f"{args.grad_dtype} grad_value; f32 math",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.note}; B={w.B} M={w.M} D={w.D} L={w.L} K={w.K} "
                                f"Nq={w.num_queries} Nv={w.Nv} shapes={list(w.shapes)} "
