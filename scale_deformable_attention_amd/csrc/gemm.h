@@ -18,6 +18,35 @@ msda_status_t msda_gemm(bool a_kmajor, bool b_kmajor, int M, int N, int K, const
                         hipStream_t stream, float* a_colsum = nullptr,
                         float* a_colsum_partials = nullptr);
 
+// One product of a batch: C = A B (+ bias) (+ C), as msda_gemm, optionally
+// with a second reduction segment appended (C += A2 B2 over K2 more k; K a
+// multiple of 16, no split).
+struct GemmSpec {
+    bool a_kmajor = true, b_kmajor = true;
+    int M = 0, N = 0, K = 0;
+    const float* A = nullptr;
+    int64_t lda = 0;
+    const float* B = nullptr;
+    int64_t ldb = 0;
+    float* C = nullptr;
+    int64_t ldc = 0;
+    const float* bias = nullptr;
+    bool accumulate = false;
+    int splits = 1;
+    float* partials = nullptr;          // splits * M * N floats when splits > 1
+    float* a_colsum = nullptr;          // optional column sums of A
+    float* a_colsum_partials = nullptr; // splits * M floats when splits > 1
+    const float* A2 = nullptr;
+    int64_t lda2 = 0;
+    const float* B2 = nullptr;
+    int64_t ldb2 = 0;
+    int K2 = 0;
+};
+
+// Up to 4 independent products with the same operand layouts in one launch
+// (their split reductions follow). Distinct partial buffers per product.
+msda_status_t msda_gemm_batch(const GemmSpec* specs, int count, hipStream_t stream);
+
 // out[n] (+)= sum over the R rows of g[r * ldg + n], through `partials`
 // (splits * N floats, device).
 msda_status_t msda_colsum(int R, int N, const float* g, int64_t ldg, float* out, int splits,

@@ -63,9 +63,27 @@ SavedPlan saved_plan(const msda_dims_t* d) {
     return p;
 }
 
+// Work items one matrix-core launch should offer: 4 resident 128 x 128
+// blocks on each of the 256 CUs.
+constexpr int64_t kGemmSlots = 1024;
+
+int64_t tiles_of(int64_t rows, int64_t cols) { return ((rows + 127) / 128) * ((cols + 127) / 128); }
+
+// Reduction splits of the batched weight gradients of the offset, logit and
+// value heads (one launch): about one round of work items for all three.
+int batch_splits(const msda_dims_t* d) {
+    const int64_t C = d->M * d->D, A = d->M * d->L * d->K, P = 2 * A;
+    const int64_t tiles = tiles_of(P, C) + tiles_of(A, C) + tiles_of(C, C);
+    const int64_t rows = std::max<int64_t>(1, std::min(d->B * d->Nq, d->B * d->Nv));
+    int64_t s = kGemmSlots / tiles;
+    s = std::min<int64_t>(s, (rows + 15) / 16);
+    return (int)std::max<int64_t>(1, std::min<int64_t>(s, 256));
+}
+
 // Backward scratch: the core's input and value gradients, the offset and
 // logit gradients, the fused backward's workspace and the linear layers'
-// split partials (reused by one layer after the other: same stream).
+// split partials (the output head's first, then the three batched heads',
+// each in its own region).
 struct WsPlan {
     size_t dcore = 0, dvalue = 0, doff = 0, dlogits = 0, core_ws = 0, core_ws_bytes = 0,
            partials = 0, bytes = 0;
@@ -89,9 +107,10 @@ msda_status_t ws_plan(const msda_dims_t* d, WsPlan& p) {
     p.core_ws_bytes = core_ws;
     at += up(core_ws);
     p.partials = at;
-    const size_t part = std::max({msda_linear_workspace_floats(s.rows_q, s.C, s.C),
-                                  msda_linear_workspace_floats(s.rows_q, s.C, s.P),
-                                  msda_linear_workspace_floats(s.rows_v, s.C, s.C)});
+    const size_t sb = (size_t)batch_splits(d);
+    const size_t batched = sb * ((size_t)s.P * s.C + s.P + (size_t)s.A * s.C + s.A +
+                                 (size_t)s.C * s.C + s.C);
+    const size_t part = std::max(msda_linear_workspace_floats(s.rows_q, s.C, s.C), batched);
     at += up(part * 4);
     p.bytes = at;
     return MSDA_SUCCESS;
@@ -182,15 +201,18 @@ msda_status_t msda_layer_forward(const msda_dims_t* dims, const float* query,
     const int Rq = (int)s.rows_q, Rv = (int)s.rows_v;
     const msda_layer_params_t& w = *params;
     msda_status_t r;
-    // y[r, o] = sum_i x[r, i] W[o, i]
-    r = msda_gemm(true, true, Rv, C, C, input_flatten, C, w.value_weight, C, value, C,
-                  w.value_bias, false, 1, nullptr, stream);
-    if (r != MSDA_SUCCESS) return r;
-    r = msda_gemm(true, true, Rq, P, C, query, C, w.offset_weight, C, off, P, w.offset_bias, false,
-                  1, nullptr, stream);
-    if (r != MSDA_SUCCESS) return r;
-    r = msda_gemm(true, true, Rq, A, C, query, C, w.attn_weight, C, logits, A, w.attn_bias, false,
-                  1, nullptr, stream);
+    // y[r, o] = sum_i x[r, i] W[o, i]: the three input projections in one launch
+    GemmSpec in[3];
+    in[0].M = Rv, in[0].N = C, in[0].K = C, in[0].A = input_flatten, in[0].lda = C;
+    in[0].B = w.value_weight, in[0].ldb = C, in[0].C = value, in[0].ldc = C;
+    in[0].bias = w.value_bias;
+    in[1].M = Rq, in[1].N = P, in[1].K = C, in[1].A = query, in[1].lda = C;
+    in[1].B = w.offset_weight, in[1].ldb = C, in[1].C = off, in[1].ldc = P;
+    in[1].bias = w.offset_bias;
+    in[2].M = Rq, in[2].N = A, in[2].K = C, in[2].A = query, in[2].lda = C;
+    in[2].B = w.attn_weight, in[2].ldb = C, in[2].C = logits, in[2].ldc = A;
+    in[2].bias = w.attn_bias;
+    r = msda_gemm_batch(in, 3, stream);
     if (r != MSDA_SUCCESS) return r;
     r = msda_forward_fused(dims, MSDA_DTYPE_F32, value, spatial_shapes, level_start_index,
                            reference_points, off, logits, core, stream);
@@ -244,9 +266,7 @@ msda_status_t msda_layer_backward(const msda_dims_t* dims, const float* query,
     float* part = at<float>(workspace, wp.partials);
     const int C = (int)s.C, P = (int)s.P, A = (int)s.A;
     const int Rq = (int)s.rows_q, Rv = (int)s.rows_v;
-    const int sq = msda_linear_splits(Rq), sv = msda_linear_splits(Rv);
-    float* part_bq = part + (size_t)sq * C * std::max(C, P);   // after the largest weight partials
-    float* part_bv = part + (size_t)sv * C * C;
+    const int sq = msda_linear_splits(Rq);
     msda_status_t r;
 
     // output projection: dcore = dy W_out; dW_out = dy^T core; db_out = sum dy
@@ -254,7 +274,7 @@ msda_status_t msda_layer_backward(const msda_dims_t* dims, const float* query,
                   false, 1, nullptr, stream);
     if (r != MSDA_SUCCESS) return r;
     r = weight_and_bias(C, C, Rq, grad_output, core, g.output_weight, g.output_bias, sq, part,
-                        part_bq, stream);
+                        part + (size_t)sq * C * C, stream);
     if (r != MSDA_SUCCESS) return r;
 
     // the fused core: value, reference-point, offset and logit gradients
@@ -267,30 +287,69 @@ msda_status_t msda_layer_backward(const msda_dims_t* dims, const float* query,
                             want_q ? dlogits : nullptr, core_ws, wp.core_ws_bytes, stream);
     if (r != MSDA_SUCCESS) return r;
 
-    // offset and logit heads: dquery = doff W_o + dlogits W_a
+    // input gradients in one launch: dquery = doff W_o + dlogits W_a (two
+    // reduction segments of one product), dinput = dvalue W_v
+    GemmSpec nn[2];
+    int nnn = 0;
     if (grad_query && Rq > 0) {
-        r = msda_gemm(true, false, Rq, C, P, doff, P, w.offset_weight, C, grad_query, C, nullptr,
-                      false, 1, nullptr, stream);
+        GemmSpec& q = nn[nnn++];
+        q.a_kmajor = true, q.b_kmajor = false;
+        q.M = Rq, q.N = C, q.K = P, q.A = doff, q.lda = P, q.B = w.offset_weight, q.ldb = C;
+        q.C = grad_query, q.ldc = C;
+        if (P % 16 == 0) {
+            q.A2 = dlogits, q.lda2 = A, q.B2 = w.attn_weight, q.ldb2 = C, q.K2 = A;
+        }
+    }
+    if (grad_input_flatten && Rv > 0) {
+        GemmSpec& v = nn[nnn++];
+        v.a_kmajor = true, v.b_kmajor = false;
+        v.M = Rv, v.N = C, v.K = C, v.A = dvalue, v.lda = C, v.B = w.value_weight, v.ldb = C;
+        v.C = grad_input_flatten, v.ldc = C;
+    }
+    if (nnn > 0) {
+        r = msda_gemm_batch(nn, nnn, stream);
         if (r != MSDA_SUCCESS) return r;
+    }
+    if (grad_query && Rq > 0 && P % 16 != 0) {
         r = msda_gemm(true, false, Rq, C, A, dlogits, A, w.attn_weight, C, grad_query, C, nullptr,
                       true, 1, nullptr, stream);
         if (r != MSDA_SUCCESS) return r;
     }
-    r = weight_and_bias(P, C, Rq, doff, query, g.offset_weight, g.offset_bias, sq, part, part_bq,
-                        stream);
-    if (r != MSDA_SUCCESS) return r;
-    r = weight_and_bias(A, C, Rq, dlogits, query, g.attn_weight, g.attn_bias, sq, part, part_bq,
-                        stream);
-    if (r != MSDA_SUCCESS) return r;
 
-    // value projection: dinput = dvalue W_v; dW_v = dvalue^T input; db_v = sum dvalue
-    if (grad_input_flatten && Rv > 0) {
-        r = msda_gemm(true, false, Rv, C, C, dvalue, C, w.value_weight, C, grad_input_flatten, C,
-                      nullptr, false, 1, nullptr, stream);
-        if (r != MSDA_SUCCESS) return r;
+    // weight (and bias) gradients of the offset, logit and value heads in one
+    // launch, each product with its own partial buffers
+    const int sb = batch_splits(dims);
+    float* part_off = part;
+    float* part_off_b = part_off + (size_t)sb * P * C;
+    float* part_att = part_off_b + (size_t)sb * P;
+    float* part_att_b = part_att + (size_t)sb * A * C;
+    float* part_val = part_att_b + (size_t)sb * A;
+    float* part_val_b = part_val + (size_t)sb * C * C;
+    GemmSpec tn[3];
+    int ntn = 0;
+    struct Head {
+        float *gw, *gb;
+        int O, R;
+        const float *dy, *x;
+        float *part, *part_b;
+    } heads[3] = {{g.offset_weight, g.offset_bias, P, Rq, doff, query, part_off, part_off_b},
+                  {g.attn_weight, g.attn_bias, A, Rq, dlogits, query, part_att, part_att_b},
+                  {g.value_weight, g.value_bias, C, Rv, dvalue, input_flatten, part_val,
+                   part_val_b}};
+    for (const Head& h : heads) {
+        if (h.gw) {
+            GemmSpec& t = tn[ntn++];
+            t.a_kmajor = false, t.b_kmajor = false;
+            t.M = h.O, t.N = C, t.K = h.R, t.A = h.dy, t.lda = h.O, t.B = h.x, t.ldb = C;
+            t.C = h.gw, t.ldc = C, t.splits = h.R == 0 ? 1 : sb, t.partials = h.part;
+            t.a_colsum = h.gb, t.a_colsum_partials = h.part_b;
+        } else if (h.gb) {
+            r = msda_colsum(h.R, h.O, h.dy, h.O, h.gb, sb, h.part_b, false, stream);
+            if (r != MSDA_SUCCESS) return r;
+        }
     }
-    return weight_and_bias(C, C, Rv, dvalue, input_flatten, g.value_weight, g.value_bias, sv, part,
-                           part_bv, stream);
+    if (ntn > 0) return msda_gemm_batch(tn, ntn, stream);
+    return MSDA_SUCCESS;
 }
 
 }  // extern "C"

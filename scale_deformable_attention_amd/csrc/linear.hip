@@ -35,6 +35,9 @@ constexpr int kBK = MSDA_GEMM_BK;      // reduction slice per iteration
 constexpr int kPerThread = kTile * kBK / 256;   // staged elements of an operand per thread
 constexpr int kHalf = kBK / 2;         // reduction steps of one MFMA lane half per slice
 constexpr int kRowK = kBK + 4;         // padded LDS row of the [row][k] layout (floats)
+#ifndef MSDA_GEMM_FRAG
+#define MSDA_GEMM_FRAG 8
+#endif
 #ifndef MSDA_GEMM_KLAYOUT
 #define MSDA_GEMM_KLAYOUT 1
 #endif
@@ -57,6 +60,22 @@ struct GemmArgs {
     int accumulate;        // C += result (splits == 1 only)
     int64_t split_stride;  // elements between consecutive splits' partial outputs
     float* asum;           // if set: sum over this split's k of A(m, k), at asum[z * M + m]
+    // optional second reduction segment, k in [K, K + K2): A2, B2 with the
+    // same layouts (K a multiple of kBK, so a slice never straddles)
+    const float* A2;
+    const float* B2;
+    int64_t lda2, ldb2;
+    int K2;
+    int unit_begin;        // first work item of this problem in its group
+};
+
+// Up to kMaxGroup independent products of one operand-layout combination in
+// one launch: the work items of all of them share the grid, so the last
+// partial round of blocks is paid once.
+constexpr int kMaxGroup = 4;
+struct GemmGroup {
+    GemmArgs g[kMaxGroup];
+    int count;
 };
 
 // Blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous
@@ -68,8 +87,11 @@ __device__ inline int xcd_work_item() {
     return x * per + (x < rem ? x : rem) + i;
 }
 
+#ifndef MSDA_GEMM_WAVES_PER_EU
+#define MSDA_GEMM_WAVES_PER_EU 4
+#endif
 template <bool kAK, bool kBKm, bool kVec>
-__global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kThreads, MSDA_GEMM_WAVES_PER_EU) void msda_gemm_kernel(GemmGroup grp) {
     // LDS layout of a staged operand: [row][k] (k contiguous) when its global
     // rows are k-contiguous and loaded as float4s -- stored as loaded, read
     // back as float4s; otherwise [k][row]
@@ -78,18 +100,23 @@ __global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmArgs g) {
     __shared__ float As[2][kLdsFloats];
     __shared__ float Bs[2][kLdsFloats];
     const int tid = threadIdx.x;
-    const int mt = (g.M + kTile - 1) / kTile, nt = (g.N + kTile - 1) / kTile;
     const int work = xcd_work_item();
-    const int z = work / (mt * nt);
-    const int t = work - z * (mt * nt);
+    int pi = 0;
+    while (pi + 1 < grp.count && work >= grp.g[pi + 1].unit_begin) ++pi;
+    const GemmArgs& g = grp.g[pi];
+    const int local = work - g.unit_begin;
+    const int mt = (g.M + kTile - 1) / kTile, nt = (g.N + kTile - 1) / kTile;
+    const int z = local / (mt * nt);
+    const int t = local - z * (mt * nt);
     const int m0 = (t / nt) * kTile, n0 = (t % nt) * kTile;
     const int kbeg = z * g.k_split;
-    const int kend = min(g.K, kbeg + g.k_split);
+    const int kend = min(g.K + g.K2, kbeg + g.k_split);
 
     // ---- staging: kTile * kBK elements of each operand per slice
     float ra[kPerThread], rb[kPerThread];
+    // k0 and kend relative to the operand's own segment
     auto load = [&](const float* P, int64_t ld, bool kmajor, int lim_mn, int base_mn, int k0,
-                    float* r) {
+                    int kend, float* r) {
         if constexpr (kVec) {
 #pragma unroll
             for (int i = 0; i < kPerThread / 4; ++i) {
@@ -175,31 +202,40 @@ __global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmArgs g) {
     const bool do_asum = g.asum != nullptr && n0 == 0 && tid < kTile;
     float asum = 0.0f;
 
+    // slice k0 of the combined reduction, from its segment
+    auto fetch = [&](int k0) {
+        if (k0 >= g.K) {
+            load(g.A2, g.lda2, kAK, g.M, m0, k0 - g.K, kend - g.K, ra);
+            load(g.B2, g.ldb2, kBKm, g.N, n0, k0 - g.K, kend - g.K, rb);
+        } else {
+            load(g.A, g.lda, kAK, g.M, m0, k0, min(kend, g.K), ra);
+            load(g.B, g.ldb, kBKm, g.N, n0, k0, min(kend, g.K), rb);
+        }
+    };
+
     int buf = 0;
     if (kbeg < kend) {
-        load(g.A, g.lda, kAK, g.M, m0, kbeg, ra);
-        load(g.B, g.ldb, kBKm, g.N, n0, kbeg, rb);
+        fetch(kbeg);
         store(As[0], kAK, kAmk, ra);
         store(Bs[0], kBKm, kBmk, rb);
     }
     __syncthreads();
     for (int k0 = kbeg; k0 < kend; k0 += kBK) {
         const bool more = k0 + kBK < kend;
-        if (more) {
-            load(g.A, g.lda, kAK, g.M, m0, k0 + kBK, ra);
-            load(g.B, g.ldb, kBKm, g.N, n0, k0 + kBK, rb);
-        }
+        if (more) fetch(k0 + kBK);
         const float* Ab = As[buf];
         const float* Bb = Bs[buf];
         // MFMA step s sums over k = lk * kHalf + s (the lane halves take the
         // slice's two halves): a lane's operands of a slice are then kHalf
         // consecutive k of one row
-        float a0v[kHalf], a1v[kHalf], b0v[kHalf], b1v[kHalf];
-        auto frag = [&](const float* S, bool mk, int row, float* v) {
+        // fragments read kFrag k's at a time (fewer live registers)
+        constexpr int kFrag = MSDA_GEMM_FRAG;
+        auto frag = [&](const float* S, bool mk, int row, int q0, float* v) {
             if (mk) {
 #pragma unroll
-                for (int q = 0; q < kHalf; q += 4) {
-                    const float4 f = *reinterpret_cast<const float4*>(&S[row * kRowK + lk * kHalf + q]);
+                for (int q = 0; q < kFrag; q += 4) {
+                    const float4 f =
+                        *reinterpret_cast<const float4*>(&S[row * kRowK + lk * kHalf + q0 + q]);
                     v[q] = f.x;
                     v[q + 1] = f.y;
                     v[q + 2] = f.z;
@@ -207,19 +243,23 @@ __global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmArgs g) {
                 }
             } else {
 #pragma unroll
-                for (int q = 0; q < kHalf; ++q) v[q] = S[(lk * kHalf + q) * kLdsRow + row];
+                for (int q = 0; q < kFrag; ++q) v[q] = S[(lk * kHalf + q0 + q) * kLdsRow + row];
             }
         };
-        frag(Ab, kAmk, wm + li, a0v);
-        frag(Ab, kAmk, wm + 32 + li, a1v);
-        frag(Bb, kBmk, wn + li, b0v);
-        frag(Bb, kBmk, wn + 32 + li, b1v);
 #pragma unroll
-        for (int q = 0; q < kHalf; ++q) {
-            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0v[q], b0v[q], acc[0][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0v[q], b1v[q], acc[0][1], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1v[q], b0v[q], acc[1][0], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1v[q], b1v[q], acc[1][1], 0, 0, 0);
+        for (int q0 = 0; q0 < kHalf; q0 += kFrag) {
+            float a0v[kFrag], a1v[kFrag], b0v[kFrag], b1v[kFrag];
+            frag(Ab, kAmk, wm + li, q0, a0v);
+            frag(Ab, kAmk, wm + 32 + li, q0, a1v);
+            frag(Bb, kBmk, wn + li, q0, b0v);
+            frag(Bb, kBmk, wn + 32 + li, q0, b1v);
+#pragma unroll
+            for (int q = 0; q < kFrag; ++q) {
+                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0v[q], b0v[q], acc[0][0], 0, 0, 0);
+                acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0v[q], b1v[q], acc[0][1], 0, 0, 0);
+                acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1v[q], b0v[q], acc[1][0], 0, 0, 0);
+                acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1v[q], b1v[q], acc[1][1], 0, 0, 0);
+            }
         }
         if (do_asum) {
 #pragma unroll
@@ -259,6 +299,7 @@ __global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmArgs g) {
         }
     }
 }
+
 
 // out[m, n] (row stride ldo) = sum over s < splits of part[s * M * N + m * N + n]
 // (+ bias[n]) (+ out[m, n] if accumulate). A block takes 64 consecutive
@@ -347,47 +388,78 @@ msda_status_t launch_reduce(const float* part, int splits, int M, int N, float* 
 }
 }  // namespace
 
-msda_status_t msda_gemm(bool a_kmajor, bool b_kmajor, int M, int N, int K, const float* A,
-                        int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
-                        const float* bias, bool accumulate, int splits, float* partials,
-                        hipStream_t stream, float* a_colsum, float* a_colsum_partials) {
-    if (M == 0 || N == 0) return MSDA_SUCCESS;
-    GemmArgs g;
-    g.A = A;
-    g.B = B;
-    g.bias = bias;
-    g.lda = lda;
-    g.ldb = ldb;
-    g.M = M;
-    g.N = N;
-    g.K = K;
-    splits = std::max(1, splits);
-    g.k_split = (int)round_up((K + splits - 1) / splits, kBK);
-    if (g.k_split == 0) g.k_split = kBK;
-    splits = (int)std::max<int64_t>(1, (K + g.k_split - 1) / g.k_split);
-    g.splits = splits;
-    if (splits > 1) {
-        g.C = partials;
-        g.ldc = N;
-        g.bias = nullptr;
-        g.accumulate = 0;
-        g.split_stride = (int64_t)M * N;
-        g.asum = a_colsum ? a_colsum_partials : nullptr;
-    } else {
-        g.C = C;
-        g.ldc = ldc;
-        g.accumulate = accumulate ? 1 : 0;
-        g.split_stride = 0;
-        g.asum = a_colsum;
+namespace {
+
+bool operand_vec(const float* P, int64_t ld, bool kmajor, int rows, int K) {
+    return aligned(P, 16) && ld % 4 == 0 && (kmajor ? K % 4 == 0 : rows % 4 == 0);
+}
+
+}  // namespace
+
+msda_status_t msda_gemm_batch(const GemmSpec* specs, int count, hipStream_t stream) {
+    if (count < 1 || count > kMaxGroup) return MSDA_ERROR_INVALID_VALUE;
+    GemmGroup grp = {};
+    int src[kMaxGroup];   // the spec each launched problem came from
+    int n = 0;
+    int64_t units = 0;
+    bool vec = true;
+    for (int i = 0; i < count; ++i) {
+        const GemmSpec& sp = specs[i];
+        if (sp.a_kmajor != specs[0].a_kmajor || sp.b_kmajor != specs[0].b_kmajor)
+            return MSDA_ERROR_INVALID_VALUE;
+        if (sp.K2 > 0 && (sp.K % kBK != 0 || sp.splits > 1)) return MSDA_ERROR_INVALID_VALUE;
+        if (sp.M == 0 || sp.N == 0) continue;
+        src[n] = i;
+        GemmArgs& g = grp.g[n++];
+        g.A = sp.A;
+        g.B = sp.B;
+        g.bias = sp.bias;
+        g.lda = sp.lda;
+        g.ldb = sp.ldb;
+        g.M = sp.M;
+        g.N = sp.N;
+        g.K = sp.K;
+        g.A2 = sp.A2;
+        g.B2 = sp.B2;
+        g.lda2 = sp.lda2;
+        g.ldb2 = sp.ldb2;
+        g.K2 = sp.K2 > 0 ? sp.K2 : 0;
+        const int ktot = g.K + g.K2;
+        int splits = std::max(1, sp.splits);
+        g.k_split = (int)round_up((ktot + splits - 1) / splits, kBK);
+        if (g.k_split == 0) g.k_split = kBK;
+        splits = (int)std::max<int64_t>(1, (ktot + g.k_split - 1) / g.k_split);
+        g.splits = splits;
+        if (splits > 1) {
+            g.C = sp.partials;
+            g.ldc = sp.N;
+            g.bias = nullptr;
+            g.accumulate = 0;
+            g.split_stride = (int64_t)sp.M * sp.N;
+            g.asum = sp.a_colsum ? sp.a_colsum_partials : nullptr;
+        } else {
+            g.C = sp.C;
+            g.ldc = sp.ldc;
+            g.accumulate = sp.accumulate ? 1 : 0;
+            g.split_stride = 0;
+            g.asum = sp.a_colsum;
+        }
+        g.unit_begin = (int)units;
+        units += (int64_t)((sp.M + kTile - 1) / kTile) * ((sp.N + kTile - 1) / kTile) * splits;
+        // vector loads: every operand's contiguous dimension a multiple of 4
+        // floats, strides too, 16-byte aligned bases
+        vec = vec && operand_vec(sp.A, sp.lda, sp.a_kmajor, sp.M, sp.K) &&
+              operand_vec(sp.B, sp.ldb, sp.b_kmajor, sp.N, sp.K);
+        if (g.K2 > 0)
+            vec = vec && operand_vec(sp.A2, sp.lda2, sp.a_kmajor, sp.M, sp.K2) &&
+                  operand_vec(sp.B2, sp.ldb2, sp.b_kmajor, sp.N, sp.K2);
     }
-    // vector loads: the contiguous dimension of each operand a multiple of 4
-    // floats, strides too, and 16-byte aligned bases
-    const bool a_vec = aligned(A, 16) && lda % 4 == 0 && (a_kmajor ? K % 4 == 0 : M % 4 == 0);
-    const bool b_vec = aligned(B, 16) && ldb % 4 == 0 && (b_kmajor ? K % 4 == 0 : N % 4 == 0);
-    const bool vec = a_vec && b_vec;
+    if (n == 0) return MSDA_SUCCESS;
+    grp.count = n;
+    const bool ak = specs[0].a_kmajor, bk = specs[0].b_kmajor;
     const void* kern = nullptr;
 #define MSDA_PICK(AK, BKM)                                                                   \
-    if (a_kmajor == AK && b_kmajor == BKM)                                                   \
+    if (ak == AK && bk == BKM)                                                               \
         kern = vec ? reinterpret_cast<const void*>(&msda_gemm_kernel<AK, BKM, true>)         \
                    : reinterpret_cast<const void*>(&msda_gemm_kernel<AK, BKM, false>);
     MSDA_PICK(true, true)
@@ -395,21 +467,49 @@ msda_status_t msda_gemm(bool a_kmajor, bool b_kmajor, int M, int N, int K, const
     MSDA_PICK(false, true)
     MSDA_PICK(false, false)
 #undef MSDA_PICK
-    const int64_t tiles = (int64_t)((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile);
-    void* args[] = {&g};
-    hipError_t e = hipLaunchKernel(kern, dim3((unsigned)(tiles * splits)), dim3(kThreads), args, 0,
-                                   stream);
+    void* args[] = {&grp};
+    const hipError_t e =
+        hipLaunchKernel(kern, dim3((unsigned)units), dim3(kThreads), args, 0, stream);
     if (e != hipSuccess) return MSDA_ERROR_LAUNCH;
-    if (splits > 1) {
-        msda_status_t st = launch_reduce(partials, splits, M, N, C, ldc, bias, accumulate, stream);
+    for (int i = 0; i < n; ++i) {
+        const GemmArgs& g = grp.g[i];
+        if (g.splits <= 1) continue;
+        const GemmSpec* sp = &specs[src[i]];
+        msda_status_t st = launch_reduce(g.C, g.splits, g.M, g.N, sp->C, sp->ldc, sp->bias,
+                                         sp->accumulate, stream);
         if (st != MSDA_SUCCESS) return st;
-        if (a_colsum) {
-            st = launch_reduce(a_colsum_partials, splits, 1, M, a_colsum, M, nullptr, false,
-                               stream);
+        if (sp->a_colsum) {
+            st = launch_reduce(sp->a_colsum_partials, g.splits, 1, g.M, sp->a_colsum, g.M, nullptr,
+                               false, stream);
             if (st != MSDA_SUCCESS) return st;
         }
     }
     return MSDA_SUCCESS;
+}
+
+msda_status_t msda_gemm(bool a_kmajor, bool b_kmajor, int M, int N, int K, const float* A,
+                        int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
+                        const float* bias, bool accumulate, int splits, float* partials,
+                        hipStream_t stream, float* a_colsum, float* a_colsum_partials) {
+    GemmSpec sp;
+    sp.a_kmajor = a_kmajor;
+    sp.b_kmajor = b_kmajor;
+    sp.M = M;
+    sp.N = N;
+    sp.K = K;
+    sp.A = A;
+    sp.lda = lda;
+    sp.B = B;
+    sp.ldb = ldb;
+    sp.C = C;
+    sp.ldc = ldc;
+    sp.bias = bias;
+    sp.accumulate = accumulate;
+    sp.splits = splits;
+    sp.partials = partials;
+    sp.a_colsum = a_colsum;
+    sp.a_colsum_partials = a_colsum_partials;
+    return msda_gemm_batch(&sp, 1, stream);
 }
 
 // grad_bias[n] = sum over rows of g[r * ldg + n], through `partials`
