@@ -397,6 +397,10 @@ def bench_dcn(args, w, dev):
     kernel_bytes = dict(zip(names, (ab["forward"], ab["bwd_point"], ab["bwd_value"])))
     dom = max(kernels, key=kernels.get)
     achieved = kernel_bytes[dom] / (kernels[dom] * 1e-3) / 1e9
+    measured = read_traffic(w.name)
+    traffic = None
+    if measured is not None and all(k in measured for k in dom.split("+")):
+        traffic = sum(measured[k] for k in dom.split("+"))
     result = {
         "metric": METRIC,
         "value": w.points / (ms_per_step * 1e-3),
@@ -417,7 +421,7 @@ def bench_dcn(args, w, dev):
                    "parallelism": "none"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes": kernel_bytes[dom],
+                     "traffic": traffic, "algorithmic_bytes": kernel_bytes[dom],
                      "avg_ms": kernels[dom], "launches": len(dom.split("+"))},
         "kernels_ms": kernels,
         "kernels_frac": {k: kernel_bytes[k] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS
