@@ -146,6 +146,15 @@ def test_layer_head_widths(D):
     layer_parity(w)
 
 
+def test_layer_odd_head_sizes():
+    # M*L*K = 3: the offset (6) and logit (3) features are not multiples of 4
+    # (scalar operand loads) and the query gradient's two heads run as two
+    # products (offset features not a multiple of 16)
+    w = wl.Workload("layer_odd", B=2, M=1, D=16, K=3, shapes=((7, 9),), ref="uniform",
+                    sigma_px=2.0, Nq=21, seed=320)
+    layer_parity(w)
+
+
 def test_layer_small_encoder_grid():
     w = wl.Workload("layer_small_encoder", B=2, M=8, D=32, K=4, shapes=SMALL_PYRAMID, ref="grid",
                     sigma_px=3.0, seed=310)
