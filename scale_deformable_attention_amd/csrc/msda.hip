@@ -710,15 +710,18 @@ constexpr int kMaxSlabs = 64;       // bin blocks per (b, m) at most (a power of
 constexpr int kUnroll = 8;          // entries in flight per lane group in the sweep
 constexpr int kRecUnroll = 4;       // entries per thread in flight when building records
 
-// A tile is kTileH x TW pixels; lane group c of a tile block owns pixel column
-// c, with 4 fp32 channels per lane.
+// A tile is kTileH x TW pixels. Its pixels are fed by the cells (top-left
+// corners) in cell rows -1 .. kTileH-1 and cell columns -1 .. TW-1 relative to
+// it: NG = TW + 1 cell columns, one per lane group of a tile block (4 fp32
+// channels per lane).
 template <int D>
 struct TileShape {
     static constexpr int PL = 4;
     static constexpr int G = D / PL;
-    static constexpr int TW = kBlock / G;
-    static constexpr int kCells = (kTileH + 1) * (TW + 1);
-    static_assert(TW >= 16 && (TW & (TW - 1)) == 0, "tile width");
+    static constexpr int NG = kBlock / G;   // lane groups
+    static constexpr int TW = NG - 1;       // pixel columns per tile
+    static constexpr int kCells = (kTileH + 1) * NG;
+    static_assert(TW >= 15, "tile width");
 };
 
 struct LevelTiles {
@@ -817,7 +820,8 @@ __device__ inline void point_tiles(float u, float v, const LevelTiles& lt, int* 
     const int y0 = (int)fminf(fmaxf(y0f, -1.0f), Hf);
     // tile coordinates of the two columns and rows (only used where valid,
     // i.e. where the pixel coordinate is >= 0)
-    const int tx0 = max(x0, 0) / TW, tx1 = (x0 + 1) / TW;
+    const int tx0 = (int)((uint32_t)max(x0, 0) / (uint32_t)TW);
+    const int tx1 = (int)((uint32_t)(x0 + 1) / (uint32_t)TW);
     const int ty0 = max(y0, 0) / kTileH, ty1 = (y0 + 1) / kTileH;
     const bool v00 = vx0 && vy0, v01 = vx1 && vy0, v10 = vx0 && vy1, v11 = vx1 && vy1;
     const bool same_x = tx0 == tx1, same_y = ty0 == ty1;
@@ -997,7 +1001,8 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
 template <int D, bool kBf16Out>
 __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
     using TS = TileShape<D>;
-    constexpr int TW = TS::TW, G = TS::G, kCells = TS::kCells;
+    constexpr int TW = TS::TW, NG = TS::NG, G = TS::G, kCells = TS::kCells;
+    static_assert(kTileH * kBlock <= kChunk, "the column exchange reuses the record buffer");
     __shared__ LevelTiles lt[MSDA_MAX_LEVELS];
     __shared__ int s_tiles, s_item;
     __shared__ uint32_t wcnt[kMaxSlabs], wstart[kMaxSlabs], woff[kMaxSlabs];
@@ -1049,9 +1054,12 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
         __syncthreads();
         const uint32_t E = block_exclusive_scan(wcnt, wstart, p.nW, scratch);
 
-        float4 acc[kTileH];
+        float4 own[kTileH], prev[kTileH];
 #pragma unroll
-        for (int y = 0; y < kTileH; ++y) acc[y] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int y = 0; y < kTileH; ++y) {
+            own[y] = make_float4(0.f, 0.f, 0.f, 0.f);
+            prev[y] = own[y];
+        }
 
         for (uint32_t c0 = 0; c0 < E; c0 += kChunk) {
             const int n = (int)min((uint32_t)kChunk, E - c0);
@@ -1084,7 +1092,7 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
                     // one pixel of it; clamp anyway to stay in bounds
                     const int cy = min(max((int)y0f - y_base, -1), kTileH - 1);
                     const int cx = min(max((int)x0f - x_base, -1), TW - 1);
-                    const int cell = (cy + 1) * (TW + 1) + (cx + 1);
+                    const int cell = (cy + 1) * NG + (cx + 1);
                     rec[e] = make_float4(as_float(as_uint(ent[u].x) * (uint32_t)D), a * (1.0f - fy),
                                          a * fy, fx);
                     cell_of[e] = (uint16_t)cell;
@@ -1100,19 +1108,19 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
                 sorted[cstart[c] + atomicAdd(&ccount[c], 1u)] = (uint16_t)e;
             }
             __syncthreads();
-            // column sweep: cells (y0, col-1) and (y0, col) feed pixel column
-            // col; their ids are consecutive, so their entries form one sorted
-            // range [s, e) that splits at the second cell's start. kUnroll
-            // entries are in flight at once (indices past the end are clamped
-            // to the last entry and weighted 0).
+            // cell-column sweep: lane group col takes the cells of cell column
+            // col - 1 (one sorted range per cell row) and adds each entry's
+            // right corners to pixel column col (own) and its left corners to
+            // pixel column col - 1 (prev), one upstream-gradient row per entry.
+            // kUnroll entries are in flight at once (indices past the end are
+            // clamped to the last entry and weighted 0).
 #pragma unroll
             for (int cr = 0; cr <= kTileH; ++cr) {   // cell row cy = cr - 1
-                const int lc = cr * (TW + 1) + col;
-                const uint32_t s0 = cstart[lc], split = cstart[lc + 1];
-                const uint32_t e = split + ccount[lc + 1];
+                const int lc = cr * NG + col;
+                const uint32_t s0 = cstart[lc], e = cstart[lc + 1];
                 for (uint32_t k = s0; k < e; k += kUnroll) {
                     float4 gv[kUnroll];
-                    float wt[kUnroll], wb[kUnroll];
+                    float wtr[kUnroll], wbr[kUnroll], wtl[kUnroll], wbl[kUnroll];
 #pragma unroll
                     for (int u = 0; u < kUnroll; ++u) {
                         const uint32_t i = min(k + u, e - 1);
@@ -1121,37 +1129,63 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
                             grsrc, (as_uint(rv.x) + (uint32_t)r * 4u) * 4u, 0, 0);
                         gv[u] = make_float4(as_float(graw[0]), as_float(graw[1]), as_float(graw[2]),
                                             as_float(graw[3]));
-                        // the cell left of the column gives its right corners
-                        // (fx), the cell at the column its left corners (1 - fx)
-                        const float wx = i >= split ? 1.0f - rv.w : rv.w;
                         const bool live = k + u < e;
-                        wt[u] = live ? rv.y * wx : 0.0f;
-                        wb[u] = live ? rv.z * wx : 0.0f;
+                        const float at = live ? rv.y : 0.0f, ab = live ? rv.z : 0.0f;
+                        const float fx = rv.w, gx = 1.0f - rv.w;
+                        wtr[u] = at * fx;
+                        wbr[u] = ab * fx;
+                        wtl[u] = at * gx;
+                        wbl[u] = ab * gx;
                     }
 #pragma unroll
                     for (int u = 0; u < kUnroll; ++u) {
                         // a cell in cell row cr has its top corners on pixel row
                         // cr - 1 and its bottom corners on pixel row cr
                         if (cr >= 1) {
-                            acc[cr - 1].x = fmaf(wt[u], gv[u].x, acc[cr - 1].x);
-                            acc[cr - 1].y = fmaf(wt[u], gv[u].y, acc[cr - 1].y);
-                            acc[cr - 1].z = fmaf(wt[u], gv[u].z, acc[cr - 1].z);
-                            acc[cr - 1].w = fmaf(wt[u], gv[u].w, acc[cr - 1].w);
+                            own[cr - 1].x = fmaf(wtr[u], gv[u].x, own[cr - 1].x);
+                            own[cr - 1].y = fmaf(wtr[u], gv[u].y, own[cr - 1].y);
+                            own[cr - 1].z = fmaf(wtr[u], gv[u].z, own[cr - 1].z);
+                            own[cr - 1].w = fmaf(wtr[u], gv[u].w, own[cr - 1].w);
+                            prev[cr - 1].x = fmaf(wtl[u], gv[u].x, prev[cr - 1].x);
+                            prev[cr - 1].y = fmaf(wtl[u], gv[u].y, prev[cr - 1].y);
+                            prev[cr - 1].z = fmaf(wtl[u], gv[u].z, prev[cr - 1].z);
+                            prev[cr - 1].w = fmaf(wtl[u], gv[u].w, prev[cr - 1].w);
                         }
                         if (cr < kTileH) {
-                            acc[cr].x = fmaf(wb[u], gv[u].x, acc[cr].x);
-                            acc[cr].y = fmaf(wb[u], gv[u].y, acc[cr].y);
-                            acc[cr].z = fmaf(wb[u], gv[u].z, acc[cr].z);
-                            acc[cr].w = fmaf(wb[u], gv[u].w, acc[cr].w);
+                            own[cr].x = fmaf(wbr[u], gv[u].x, own[cr].x);
+                            own[cr].y = fmaf(wbr[u], gv[u].y, own[cr].y);
+                            own[cr].z = fmaf(wbr[u], gv[u].z, own[cr].z);
+                            own[cr].w = fmaf(wbr[u], gv[u].w, own[cr].w);
+                            prev[cr].x = fmaf(wbl[u], gv[u].x, prev[cr].x);
+                            prev[cr].y = fmaf(wbl[u], gv[u].y, prev[cr].y);
+                            prev[cr].z = fmaf(wbl[u], gv[u].z, prev[cr].z);
+                            prev[cr].w = fmaf(wbl[u], gv[u].w, prev[cr].w);
                         }
                     }
                 }
             }
             __syncthreads();
         }
+        // pixel column col = own (cell column col - 1) + the prev sums of lane
+        // group col + 1 (cell column col), passed through the record buffer,
+        // which no thread reads any more
+        float4* xch = rec;
+#pragma unroll
+        for (int yy = 0; yy < kTileH; ++yy) xch[yy * kBlock + tid] = prev[yy];
+        __syncthreads();
+        if (col < TW) {
+#pragma unroll
+            for (int yy = 0; yy < kTileH; ++yy) {
+                const float4 nb = xch[yy * kBlock + tid + G];
+                own[yy].x += nb.x;
+                own[yy].y += nb.y;
+                own[yy].z += nb.z;
+                own[yy].w += nb.w;
+            }
+        }
         // every pixel of the tile that is inside the level, written once
         const int x = x_base + col;
-        if (x < L_.W) {
+        if (col < TW && x < L_.W) {
 #pragma unroll
             for (int yy = 0; yy < kTileH; ++yy) {
                 const int y = y_base + yy;
@@ -1161,10 +1195,10 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
                     if constexpr (kBf16Out) {
                         // rounded once, from the fp32 sum
                         *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.grad_value) + e) =
-                            make_uint2(float_to_bf16_bits(acc[yy].x) | (float_to_bf16_bits(acc[yy].y) << 16),
-                                       float_to_bf16_bits(acc[yy].z) | (float_to_bf16_bits(acc[yy].w) << 16));
+                            make_uint2(float_to_bf16_bits(own[yy].x) | (float_to_bf16_bits(own[yy].y) << 16),
+                                       float_to_bf16_bits(own[yy].z) | (float_to_bf16_bits(own[yy].w) << 16));
                     } else {
-                        *reinterpret_cast<float4*>(p.grad_value + e) = acc[yy];
+                        *reinterpret_cast<float4*>(p.grad_value + e) = own[yy];
                     }
                 }
             }
@@ -1275,8 +1309,8 @@ msda_status_t check_dims(const msda_dims_t* d, msda_dtype_t dt, bool backward) {
 // (count, offset) per tile and a slab of 16-byte entries (at most 4 per point:
 // one per corner tile). The
 // tile count of one (b, m) is bounded from Nv and L alone: a level of H x W
-// pixels has ceil(H/4) ceil(W/TW) tiles (TW >= 16), which is at most
-// H/4 + 3/4 when W <= TW and at most (H+3) W / (2 TW) <= H W / 8 otherwise,
+// pixels has ceil(H/4) ceil(W/TW) tiles (TW >= 15), which is at most
+// H/4 + 3/4 when W <= TW and below (H+3) W / (2 TW) <= 2 H W / 15 otherwise,
 // so sum_l <= Nv/4 + L.
 struct BwdPlan {
     int64_t nW = 0, Qc = 0, t_stride = 0, slab_per_block = 0;
