@@ -44,6 +44,9 @@ constexpr int kBlock = kWave * kWavesPerBlock;
 // every buffer the kernels build (all are smaller than 2 GiB), also after the
 // bf16 -> fp32 doubling of the backward's grad_value offsets.
 constexpr uint32_t kOutside = 0xC0000000u;
+// The tile kernel's eight work counters (one per XCD group) sit 256 bytes
+// apart: device-scope atomics on one shared line serialize across the XCDs.
+constexpr int kCounterStride = 64;
 // Word 3 of a raw (untyped, stride 0) buffer descriptor on gfx9-family GPUs.
 constexpr int kBufferWord3 = 0x00020000;
 
@@ -244,6 +247,12 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                              kBufferWord3);
 }
+
+// A value that every lane of the block holds alike (read back from LDS after a
+// barrier), taken from the first lane so that the compiler sees it as
+// wave-uniform: loops bounded by it, with barriers inside, then branch on a
+// scalar and no lane can leave such a loop apart from the rest of its wave.
+__device__ inline int block_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ inline void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -708,7 +717,6 @@ constexpr int kChunk = 2048;        // entries a tile block sorts in LDS at once
 constexpr int kMinQueries = 64;     // queries per bin block at least (when there are enough)
 constexpr int kMaxSlabs = 64;       // bin blocks per (b, m) at most (a power of two)
 constexpr int kUnroll = 8;          // entries in flight per lane group in the sweep
-constexpr int kRecUnroll = 4;       // entries per thread in flight when building records
 
 // A tile is kTileH x TW pixels. Its pixels are fed by the cells (top-left
 // corners) in cell rows -1 .. kTileH-1 and cell columns -1 .. TW-1 relative to
@@ -888,7 +896,7 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
     setup_tiles<TS::TW>(p, lt, &s_tiles);
     // tables inconsistent with Nv could exceed the row: drop those tiles
     // rather than write past the workspace
-    const int T = min(s_tiles, p.t_stride);
+    const int T = block_uniform(min(s_tiles, p.t_stride));
     const int tid = threadIdx.x;
     const int bm = blockIdx.x / p.nW, w = blockIdx.x - bm * p.nW;
     const int b = bm / p.M, m = bm - b * p.M;
@@ -897,7 +905,7 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
     // this block's column of the (tile, bin block) table of its (b, m)
     uint2* row = p.table + (size_t)bm * p.t_stride * p.nW + w;
     float4* slab = p.slab + (size_t)blockIdx.x * p.slab_per_block;
-    if (blockIdx.x == 0 && tid < 8) p.counters[tid] = 0;   // for the tile kernel that follows
+    if (blockIdx.x == 0 && tid < 8) p.counters[tid * kCounterStride] = 0;   // for the tile kernel that follows
     // location (and weight) of the walk's current point, or of its first point
     // for lanes past the end, so that every load is unconditional
     // (normalized, or for the DCNv3 front-end in pixels)
@@ -997,23 +1005,34 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
 // from a counter per XCD group (blocks i = x mod 8 run on XCD x and serve the
 // (b, m) = x mod 8, so an XCD's L2 sees only its own (b, m)), coarse levels
 // first: those tiles have the most points per pixel and the longest lists, and
-// start first.
+// start first. A block takes the tile's entries kChunk at a time: loads them,
+// counting-sorts them by cell into LDS records that already hold the four
+// corner weights, then sweeps the cells column by column.
 template <int D, bool kBf16Out>
 __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
     using TS = TileShape<D>;
     constexpr int TW = TS::TW, NG = TS::NG, G = TS::G, kCells = TS::kCells;
     static_assert(kTileH * kBlock <= kChunk, "the column exchange reuses the record buffer");
+    constexpr int kPer = kChunk / kBlock;   // entries per thread per chunk
+    static_assert(kPer * kBlock == kChunk, "chunk size");
     __shared__ LevelTiles lt[MSDA_MAX_LEVELS];
     __shared__ int s_tiles, s_item;
     __shared__ uint32_t wcnt[kMaxSlabs], wstart[kMaxSlabs], woff[kMaxSlabs];
-    __shared__ float4 rec[kChunk];        // (grad_out float index bits, A*(1-fy), A*fy, fx)
-    __shared__ uint16_t cell_of[kChunk];
-    __shared__ uint16_t sorted[kChunk];
+    // a chunk's entries in cell order: the four corner weights (top-left,
+    // top-right, bottom-left, bottom-right) and the byte offset of the
+    // upstream-gradient row
+    // (slot kChunk: a zero record for the sweep's slots past a range's end)
+    __shared__ float4 wrec[kChunk + 1];
+    __shared__ uint32_t grec[kChunk + 1];
     __shared__ uint32_t cstart[kCells + 1];
     __shared__ uint32_t ccount[kCells + 1];
     __shared__ uint32_t scratch[kWavesPerBlock];
+    if (threadIdx.x == 0) {
+        wrec[kChunk] = make_float4(0.f, 0.f, 0.f, 0.f);
+        grec[kChunk] = kOutside;   // out of the buffer's range: loads zeros
+    }
     setup_tiles<TW>(p, lt, &s_tiles);
-    const int T = min(s_tiles, p.t_stride);
+    const int T = block_uniform(min(s_tiles, p.t_stride));
     const int tid = threadIdx.x;
     const int BM = p.B * p.M;
     const int col = tid / G, r = tid % G;
@@ -1024,19 +1043,20 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
     const int xcd = blockIdx.x % 8;
     const int nbm_x = BM >= 8 ? (BM - xcd + 7) / 8 : 0;
     const int items = BM >= 8 ? nbm_x * T : (BM * T - xcd + 7) / 8;
+    uint32_t* const counter = p.counters + xcd * kCounterStride;
     for (;;) {
-        if (tid == 0) s_item = (int)atomicAdd(p.counters + xcd, 1u);
+        if (tid == 0) s_item = (int)atomicAdd(counter, 1u);
         __syncthreads();
-        const int k = s_item;
+        const int k = block_uniform(s_item);
         if (k >= items) break;
         int bm, tl;
         if (BM >= 8) {
             bm = xcd + 8 * (k % nbm_x);
             tl = T - 1 - k / nbm_x;
         } else {
-            const int it = xcd + 8 * k;
-            bm = it % BM;
-            tl = T - 1 - it / BM;
+            const int i = xcd + 8 * k;
+            bm = i % BM;
+            tl = T - 1 - i / BM;
         }
         int l = 0;
         while (l + 1 < p.L && lt[l + 1].tile_base <= tl) ++l;
@@ -1052,7 +1072,7 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
             woff[w] = e.y;
         }
         __syncthreads();
-        const uint32_t E = block_exclusive_scan(wcnt, wstart, p.nW, scratch);
+        const uint32_t E = (uint32_t)block_uniform((int)block_exclusive_scan(wcnt, wstart, p.nW, scratch));
 
         float4 own[kTileH], prev[kTileH];
 #pragma unroll
@@ -1065,101 +1085,96 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
             const int n = (int)min((uint32_t)kChunk, E - c0);
             for (int i = tid; i <= kCells; i += kBlock) ccount[i] = 0;
             __syncthreads();
-            // records of this chunk, histogram by cell; kRecUnroll entries per
-            // thread in flight
-            for (int e0 = tid; e0 < n; e0 += kRecUnroll * kBlock) {
-                float4 ent[kRecUnroll];
+            // every thread takes entries tid + j * kBlock of the chunk, all
+            // kPer loads in flight (indices past the end re-read the last entry)
+            float4 ent[kPer];
 #pragma unroll
-                for (int u = 0; u < kRecUnroll; ++u) {
-                    const uint32_t ge = c0 + min(e0 + u * kBlock, n - 1);
-                    int lo = 0;   // last slab whose start <= ge (nW <= kMaxSlabs)
+            for (int j = 0; j < kPer; ++j) {
+                const uint32_t ge = c0 + min(tid + j * kBlock, n - 1);
+                int lo = 0;   // last slab whose start <= ge (nW <= kMaxSlabs)
 #pragma unroll
-                    for (int step = kMaxSlabs / 2; step > 0; step >>= 1) {
-                        const int probe = min(lo + step, p.nW - 1);
-                        lo = wstart[probe] <= ge ? probe : lo;
-                    }
-                    ent[u] = load_streaming(p.slab + ((size_t)bm * p.nW + lo) * p.slab_per_block +
-                                            woff[lo] + (ge - wstart[lo]));
+                for (int step = kMaxSlabs / 2; step > 0; step >>= 1) {
+                    const int probe = min(lo + step, p.nW - 1);
+                    lo = wstart[probe] <= ge ? probe : lo;
                 }
+                ent[j] = load_streaming(p.slab + ((size_t)bm * p.nW + lo) * p.slab_per_block +
+                                        woff[lo] + (ge - wstart[lo]));
+            }
+            // cell of each entry; histogram
+            int cell[kPer];
 #pragma unroll
-                for (int u = 0; u < kRecUnroll; ++u) {
-                    const int e = e0 + u * kBlock;
-                    if (e >= n) continue;
-                    const float x = ent[u].y, y = ent[u].z, a = ent[u].w;
-                    const float x0f = floorf(x), y0f = floorf(y);
-                    const float fx = x - x0f, fy = y - y0f;
-                    // an entry has a corner in this tile, so its cell is within
-                    // one pixel of it; clamp anyway to stay in bounds
-                    const int cy = min(max((int)y0f - y_base, -1), kTileH - 1);
-                    const int cx = min(max((int)x0f - x_base, -1), TW - 1);
-                    const int cell = (cy + 1) * NG + (cx + 1);
-                    rec[e] = make_float4(as_float(as_uint(ent[u].x) * (uint32_t)D), a * (1.0f - fy),
-                                         a * fy, fx);
-                    cell_of[e] = (uint16_t)cell;
-                    atomicAdd(&ccount[cell], 1u);
-                }
+            for (int j = 0; j < kPer; ++j) {
+                // an entry has a corner in this tile, so its cell is within
+                // one pixel of it; clamp anyway to stay in bounds
+                const int cy = min(max((int)floorf(ent[j].z) - y_base, -1), kTileH - 1);
+                const int cx = min(max((int)floorf(ent[j].y) - x_base, -1), TW - 1);
+                cell[j] = (cy + 1) * NG + (cx + 1);
+                if (tid + j * kBlock < n) atomicAdd(&ccount[cell[j]], 1u);
             }
             __syncthreads();
             block_exclusive_scan(ccount, cstart, kCells + 1, scratch);
             for (int i = tid; i <= kCells; i += kBlock) ccount[i] = 0;
             __syncthreads();
-            for (int e = tid; e < n; e += kBlock) {
-                const int c = cell_of[e];
-                sorted[cstart[c] + atomicAdd(&ccount[c], 1u)] = (uint16_t)e;
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                if (tid + j * kBlock < n) {
+                    const uint32_t slot = cstart[cell[j]] + atomicAdd(&ccount[cell[j]], 1u);
+                    const float x = ent[j].y, y = ent[j].z, a = ent[j].w;
+                    const float fx = x - floorf(x), fy = y - floorf(y);
+                    const float at = a * (1.0f - fy), ab = a * fy;
+                    wrec[slot] = make_float4(at * (1.0f - fx), at * fx, ab * (1.0f - fx), ab * fx);
+                    grec[slot] = as_uint(ent[j].x) * (uint32_t)(D * sizeof(float));
+                }
             }
             __syncthreads();
             // cell-column sweep: lane group col takes the cells of cell column
-            // col - 1 (one sorted range per cell row) and adds each entry's
+            // col - 1 (one contiguous range per cell row) and adds each entry's
             // right corners to pixel column col (own) and its left corners to
             // pixel column col - 1 (prev), one upstream-gradient row per entry.
-            // kUnroll entries are in flight at once (indices past the end are
-            // clamped to the last entry and weighted 0).
+            // kUnroll entries are in flight at once; slots past the end of the
+            // group's range read the zero record.
+            const uint32_t lane_off = (uint32_t)r * 16u;
 #pragma unroll
             for (int cr = 0; cr <= kTileH; ++cr) {   // cell row cy = cr - 1
                 const int lc = cr * NG + col;
                 const uint32_t s0 = cstart[lc], e = cstart[lc + 1];
                 for (uint32_t k = s0; k < e; k += kUnroll) {
-                    float4 gv[kUnroll];
-                    float wtr[kUnroll], wbr[kUnroll], wtl[kUnroll], wbl[kUnroll];
+                    const uint32_t rem = e - k;
+                    float4 gv[kUnroll], wv[kUnroll];
 #pragma unroll
                     for (int u = 0; u < kUnroll; ++u) {
-                        const uint32_t i = min(k + u, e - 1);
-                        const float4 rv = rec[sorted[i]];
+                        const uint32_t si = (uint32_t)u < rem ? k + u : (uint32_t)kChunk;
+                        wv[u] = wrec[si];
                         const u32x4 graw = __builtin_amdgcn_raw_buffer_load_b128(
-                            grsrc, (as_uint(rv.x) + (uint32_t)r * 4u) * 4u, 0, 0);
-                        gv[u] = make_float4(as_float(graw[0]), as_float(graw[1]), as_float(graw[2]),
-                                            as_float(graw[3]));
-                        const bool live = k + u < e;
-                        const float at = live ? rv.y : 0.0f, ab = live ? rv.z : 0.0f;
-                        const float fx = rv.w, gx = 1.0f - rv.w;
-                        wtr[u] = at * fx;
-                        wbr[u] = ab * fx;
-                        wtl[u] = at * gx;
-                        wbl[u] = ab * gx;
+                            grsrc, grec[si] + lane_off, 0, 0);
+                        gv[u] = make_float4(as_float(graw[0]), as_float(graw[1]),
+                                            as_float(graw[2]), as_float(graw[3]));
                     }
 #pragma unroll
                     for (int u = 0; u < kUnroll; ++u) {
-                        // a cell in cell row cr has its top corners on pixel row
-                        // cr - 1 and its bottom corners on pixel row cr
-                        if (cr >= 1) {
-                            own[cr - 1].x = fmaf(wtr[u], gv[u].x, own[cr - 1].x);
-                            own[cr - 1].y = fmaf(wtr[u], gv[u].y, own[cr - 1].y);
-                            own[cr - 1].z = fmaf(wtr[u], gv[u].z, own[cr - 1].z);
-                            own[cr - 1].w = fmaf(wtr[u], gv[u].w, own[cr - 1].w);
-                            prev[cr - 1].x = fmaf(wtl[u], gv[u].x, prev[cr - 1].x);
-                            prev[cr - 1].y = fmaf(wtl[u], gv[u].y, prev[cr - 1].y);
-                            prev[cr - 1].z = fmaf(wtl[u], gv[u].z, prev[cr - 1].z);
-                            prev[cr - 1].w = fmaf(wtl[u], gv[u].w, prev[cr - 1].w);
-                        }
-                        if (cr < kTileH) {
-                            own[cr].x = fmaf(wbr[u], gv[u].x, own[cr].x);
-                            own[cr].y = fmaf(wbr[u], gv[u].y, own[cr].y);
-                            own[cr].z = fmaf(wbr[u], gv[u].z, own[cr].z);
-                            own[cr].w = fmaf(wbr[u], gv[u].w, own[cr].w);
-                            prev[cr].x = fmaf(wbl[u], gv[u].x, prev[cr].x);
-                            prev[cr].y = fmaf(wbl[u], gv[u].y, prev[cr].y);
-                            prev[cr].z = fmaf(wbl[u], gv[u].z, prev[cr].z);
-                            prev[cr].w = fmaf(wbl[u], gv[u].w, prev[cr].w);
+                        {
+                            // a cell in cell row cr has its top corners on pixel
+                            // row cr - 1 and its bottom corners on pixel row cr
+                            if (cr >= 1) {
+                                prev[cr - 1].x = fmaf(wv[u].x, gv[u].x, prev[cr - 1].x);
+                                prev[cr - 1].y = fmaf(wv[u].x, gv[u].y, prev[cr - 1].y);
+                                prev[cr - 1].z = fmaf(wv[u].x, gv[u].z, prev[cr - 1].z);
+                                prev[cr - 1].w = fmaf(wv[u].x, gv[u].w, prev[cr - 1].w);
+                                own[cr - 1].x = fmaf(wv[u].y, gv[u].x, own[cr - 1].x);
+                                own[cr - 1].y = fmaf(wv[u].y, gv[u].y, own[cr - 1].y);
+                                own[cr - 1].z = fmaf(wv[u].y, gv[u].z, own[cr - 1].z);
+                                own[cr - 1].w = fmaf(wv[u].y, gv[u].w, own[cr - 1].w);
+                            }
+                            if (cr < kTileH) {
+                                prev[cr].x = fmaf(wv[u].z, gv[u].x, prev[cr].x);
+                                prev[cr].y = fmaf(wv[u].z, gv[u].y, prev[cr].y);
+                                prev[cr].z = fmaf(wv[u].z, gv[u].z, prev[cr].z);
+                                prev[cr].w = fmaf(wv[u].z, gv[u].w, prev[cr].w);
+                                own[cr].x = fmaf(wv[u].w, gv[u].x, own[cr].x);
+                                own[cr].y = fmaf(wv[u].w, gv[u].y, own[cr].y);
+                                own[cr].z = fmaf(wv[u].w, gv[u].z, own[cr].z);
+                                own[cr].w = fmaf(wv[u].w, gv[u].w, own[cr].w);
+                            }
                         }
                     }
                 }
@@ -1169,7 +1184,7 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
         // pixel column col = own (cell column col - 1) + the prev sums of lane
         // group col + 1 (cell column col), passed through the record buffer,
         // which no thread reads any more
-        float4* xch = rec;
+        float4* xch = wrec;
 #pragma unroll
         for (int yy = 0; yy < kTileH; ++yy) xch[yy * kBlock + tid] = prev[yy];
         __syncthreads();
@@ -1305,7 +1320,7 @@ msda_status_t check_dims(const msda_dims_t* d, msda_dtype_t dt, bool backward) {
 }
 
 // Workspace of the grad_value path (bin + tile kernels): 8 work counters of
-// the tile kernel, then per (b, m), nW bin blocks each own Qc queries, a row of
+// the tile kernel (kCounterStride words apart), then per (b, m), nW bin blocks each own Qc queries, a row of
 // (count, offset) per tile and a slab of 16-byte entries (at most 4 per point:
 // one per corner tile). The
 // tile count of one (b, m) is bounded from Nv and L alone: a level of H x W
@@ -1339,7 +1354,7 @@ BwdPlan plan_backward(const msda_dims_t* d) {
     const size_t table_bytes = (size_t)(BM * pl.nW * pl.t_stride) * sizeof(uint2);
     const size_t slab_bytes = (size_t)(BM * pl.nW * pl.slab_per_block) * sizeof(float4);
     pl.counters_off = 0;
-    pl.table_off = kWorkspaceAlign;   // after the 8 work counters
+    pl.table_off = round_up(8 * kCounterStride * sizeof(uint32_t), kWorkspaceAlign);   // after the 8 work counters
     pl.slab_off = pl.table_off + round_up(table_bytes, kWorkspaceAlign);
     pl.bytes = pl.slab_off + round_up(slab_bytes, kWorkspaceAlign);
     return pl;
