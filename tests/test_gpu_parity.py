@@ -137,6 +137,35 @@ def test_many_points_and_levels():
     parity(w)
 
 
+@pytest.mark.parametrize("D", [8, 16, 32, 64])
+def test_points_straddling_tile_edges(D):
+    # The value gradient is built per tile of 4 pixel rows x TW columns, with
+    # TW = 256 / (D / 4) - 1 here: put most points on cells whose corners fall
+    # on both sides of a tile edge (and on integer coordinates, and just left
+    # of the level), on levels TW wide, 2 TW + 1 wide and TW - 1 wide.
+    tw = 256 // (D // 4) - 1
+    shapes = ((9, tw), (6, 2 * tw + 1), (5, tw - 1))
+    w = wl.Workload(f"tile_edges_D{D}", B=2, M=3, D=D, K=4, shapes=shapes, ref="uniform",
+                    sigma_px=2.0, Nq=61, seed=90 + D)
+    x = wl.generate(w)
+    rng = np.random.default_rng(190 + D)
+    loc = x["sampling_locations"]          # [B, Nq, M, L, K, 2]
+    for l, (H, W) in enumerate(shapes):
+        n = loc[..., l, :, 0].size
+        xcol = tw * rng.integers(0, W // tw + 1, n) - 1 + rng.random(n)
+        yrow = 4 * rng.integers(0, H // 4 + 1, n) - 1 + rng.random(n)
+        pick = rng.random(n)
+        xcol = np.where(pick < 0.15, np.round(xcol), xcol)          # integer coordinates
+        xcol = np.where((pick >= 0.15) & (pick < 0.25), -rng.random(n), xcol)  # x in (-1, 0]
+        keep = rng.random(n) < 0.2                                   # a fifth left as drawn
+        u = ((xcol + 0.5) / W).astype(np.float32).reshape(loc[..., l, :, 0].shape)
+        v = ((yrow + 0.5) / H).astype(np.float32).reshape(loc[..., l, :, 1].shape)
+        keep = keep.reshape(u.shape)
+        loc[..., l, :, 0] = np.where(keep, loc[..., l, :, 0], u)
+        loc[..., l, :, 1] = np.where(keep, loc[..., l, :, 1], v)
+    parity(w, x=x)
+
+
 def test_far_outside_and_non_finite_locations():
     w = wl.Workload("far", B=2, M=4, D=32, K=4, shapes=SMALL_PYRAMID, ref="uniform",
                     sigma_px=40.0, Nq=50, seed=81)
