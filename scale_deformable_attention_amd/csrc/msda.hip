@@ -713,7 +713,7 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
 constexpr int kTileH = 4;           // pixel rows per tile
 constexpr int kBinRange = 1024;     // tile counters a bin block keeps in LDS at once
 constexpr int kBinUnroll = 8;       // points per thread in flight in the bin kernel
-constexpr int kChunk = 2048;        // entries a tile block sorts in LDS at once
+constexpr int kChunk = 1024;        // entries a tile block sorts in LDS at once
 constexpr int kMinQueries = 64;     // queries per bin block at least (when there are enough)
 constexpr int kMaxSlabs = 64;       // bin blocks per (b, m) at most (a power of two)
 constexpr int kUnroll = 8;          // entries in flight per lane group in the sweep
