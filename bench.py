@@ -9,8 +9,10 @@ fp32). Inputs are synthetic (seeded), resident in HBM before timing starts.
 
 Prints ONE JSON line: points/s over the K timed steps (points =
 B*Nq*M*L*K per step), the roofline of the dominant kernel measured live with HIP
-events on the launch stream, and
-the CPU oracle's rate on the host (a bounded sample of the same workload).
+events on the launch stream, the forward and the backward timed one call at a
+time warm and cold (inputs evicted from the caches by a 512 MiB write before
+each call; median, p10, p90), and the CPU oracle's rate on the host (a bounded
+sample of the same workload).
 
 With --frontend fused the step is msda_forward_fused + msda_backward_fused on
 the same workload: the kernels take the raw reference points, pixel offsets
@@ -593,6 +595,33 @@ def main():
         step()   # leave a full set of gradients in place
         torch.cuda.synchronize()
 
+    # forward and backward one call at a time, warm (back to back) and cold (a
+    # 512 MiB buffer written before each call, more than the L2s and the
+    # 256 MB MALL hold, so that the inputs start in HBM): median, p10, p90
+    def spread(fn, n, scrub=None):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for a, b in evs:
+            if scrub is not None:
+                scrub.fill_(1.0)
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in evs])
+        return {"median": float(np.median(ms)), "p10": float(np.percentile(ms, 10)),
+                "p90": float(np.percentile(ms, 90))}
+
+    scrub = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+    directions = {"calls": args.steps,
+                  "warm": {"forward_ms": spread(fwd, args.steps)},
+                  "cold": {"forward_ms": spread(fwd, args.steps, scrub)}}
+    if backward:
+        directions["warm"]["backward_ms"] = spread(bwd, args.steps)
+        directions["cold"]["backward_ms"] = spread(bwd, args.steps, scrub)
+    del scrub
+    torch.cuda.synchronize()
+
     ms_per_step = total_ms / args.steps
     pts_per_s = w.points / (ms_per_step * 1e-3)
     ab = algorithmic_bytes(w, 4 if w.value_dtype == "f32" else 2, fused,
@@ -640,6 +669,7 @@ def main():
         "kernels_ms": kernels,
         "kernels_frac": {k: kernel_bytes[k] / (v * 1e-3) / 1e9 / HBM_PEAK_GBS
                          for k, v in kernels.items()},
+        "directions": directions,
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:
