@@ -32,6 +32,7 @@ pixels, 8 groups of 16 channels, 3x3 grid).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--workload NAME] [--frontend core|fused|layer|dcn]
+                       [--no-directions]
        python bench.py --calibrate-copy MIB   (a plain copy-like kernel of known size,
                                                run under the counter profiler to scale
                                                its byte counters)
@@ -462,6 +463,8 @@ def main():
     ap.add_argument("--grad-dtype", choices=("f32", "bf16"), default="f32",
                     help="storage of grad_value (core front-end)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-directions", action="store_true",
+                    help="skip the one-call-at-a-time warm/cold timing (profiler runs)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
@@ -612,15 +615,17 @@ def main():
         return {"median": float(np.median(ms)), "p10": float(np.percentile(ms, 10)),
                 "p90": float(np.percentile(ms, 90))}
 
-    scrub = torch.empty(128 << 20, dtype=torch.float32, device=dev)
-    directions = {"calls": args.steps,
-                  "warm": {"forward_ms": spread(fwd, args.steps)},
-                  "cold": {"forward_ms": spread(fwd, args.steps, scrub)}}
-    if backward:
-        directions["warm"]["backward_ms"] = spread(bwd, args.steps)
-        directions["cold"]["backward_ms"] = spread(bwd, args.steps, scrub)
-    del scrub
-    torch.cuda.synchronize()
+    directions = None
+    if not args.no_directions:
+        scrub = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+        directions = {"calls": args.steps,
+                      "warm": {"forward_ms": spread(fwd, args.steps)},
+                      "cold": {"forward_ms": spread(fwd, args.steps, scrub)}}
+        if backward:
+            directions["warm"]["backward_ms"] = spread(bwd, args.steps)
+            directions["cold"]["backward_ms"] = spread(bwd, args.steps, scrub)
+        del scrub
+        torch.cuda.synchronize()
 
     ms_per_step = total_ms / args.steps
     pts_per_s = w.points / (ms_per_step * 1e-3)

@@ -153,7 +153,7 @@ struct Params {
     uint32_t slab_per_block;  // point-index capacity of one bin block's slab
     uint2* table;             // [B*M][t_stride][nW] (count, offset)
     float4* slab;             // [B*M*nW][slab_per_block] (tuple bits, x, y, A) entries
-    uint32_t* counters;       // [8] tile work counters, one per XCD group
+    uint32_t* counters;       // tile work counters, one per XCD group, kCounterStride apart
     // fused front-end: locations and weights formed from the model's raw
     // outputs inside the kernels
     const float* ref;         // [B, Nq, L, 2] reference points (x, y), normalized
@@ -532,11 +532,13 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
 //     block writes only its own rows.
 //  3. msda_tile_kernel: persistent blocks fetch tiles from a counter per XCD
 //     group. A block collects its tile's entries from every slab of the tile's
-//     (b, m), sorts them by cell (counting sort in LDS), and lane group c
-//     sweeps pixel column c top to bottom: the cells left of and at the column
-//     feed it, and the column's pixel sums live in registers. Every grad_value
-//     element is then written exactly once with a plain store (zeros where
-//     nothing lands), so no fill pass.
+//     (b, m), sorts them by cell (counting sort in LDS, into records holding
+//     the four corner weights), and lane group c sweeps cell column c - 1 top
+//     to bottom, adding each entry's right corners to pixel column c and its
+//     left corners to column c - 1, both in registers; the column c - 1 sums
+//     then move to group c - 1 through LDS. Every grad_value element is
+//     written exactly once with a plain store (zeros where nothing lands), so
+//     no fill pass.
 // The fused front-end adds msda_softmax_stats_kernel before these (the
 // softmax max and 1/sum per tuple) and msda_ref_grad_kernel after the point
 // kernel (the reference-point gradient, a sum over heads and points).
