@@ -166,6 +166,15 @@ def test_points_straddling_tile_edges(D):
     parity(w, x=x)
 
 
+@pytest.mark.parametrize("D", [8, 32])
+def test_dense_tiles_split_across_blocks(D):
+    # Many queries on small levels: thousands of entries per grad_value tile,
+    # swept in many chunks by one block.
+    w = wl.Workload(f"dense_D{D}", B=2, M=2, D=D, K=4, shapes=((6, 40), (3, 9)), ref="uniform",
+                    sigma_px=1.5, Nq=5000, seed=95 + D)
+    parity(w)
+
+
 def test_far_outside_and_non_finite_locations():
     w = wl.Workload("far", B=2, M=4, D=32, K=4, shapes=SMALL_PYRAMID, ref="uniform",
                     sigma_px=40.0, Nq=50, seed=81)
