@@ -167,11 +167,20 @@ def test_points_straddling_tile_edges(D):
 
 
 @pytest.mark.parametrize("D", [8, 32])
-def test_dense_tiles_split_across_blocks(D):
+def test_dense_tiles_many_chunks(D):
     # Many queries on small levels: thousands of entries per grad_value tile,
     # swept in many chunks by one block.
     w = wl.Workload(f"dense_D{D}", B=2, M=2, D=D, K=4, shapes=((6, 40), (3, 9)), ref="uniform",
                     sigma_px=1.5, Nq=5000, seed=95 + D)
+    parity(w)
+
+
+@pytest.mark.parametrize("D", [8, 64])
+def test_one_pixel_levels(D):
+    # levels of one pixel, one row and one column: most corners fall outside
+    shapes = ((1, 1), (2, 1), (1, 3), (5, 2))
+    w = wl.Workload(f"thin_D{D}", B=2, M=3, D=D, K=3, shapes=shapes, ref="uniform",
+                    sigma_px=1.0, Nq=40, seed=97 + D)
     parity(w)
 
 
