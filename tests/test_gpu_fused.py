@@ -156,6 +156,20 @@ def test_many_points_and_levels():
     parity(w, x=perturb_levels(wl.generate(w), seed=5))
 
 
+@pytest.mark.parametrize("i", range(6))
+def test_random_configurations(i):
+    # seeded draws of every size parameter, each level with its own
+    # reference point
+    rng = np.random.default_rng(8000 + i)
+    L = int(rng.integers(1, 6))
+    shapes = tuple((int(rng.integers(1, 41)), int(rng.integers(1, 71))) for _ in range(L))
+    w = wl.Workload(f"fused_random_{i}", B=int(rng.integers(1, 3)), M=int(rng.integers(1, 5)),
+                    D=int(rng.choice([8, 16, 32, 64])), K=int(rng.integers(1, 6)), shapes=shapes,
+                    ref="uniform", sigma_px=float(rng.uniform(0.5, 12.0)),
+                    Nq=int(rng.integers(1, 400)), seed=8100 + i)
+    parity(w, x=perturb_levels(wl.generate(w), seed=8200 + i))
+
+
 def test_extreme_logits_and_far_offsets():
     w = wl.Workload("fused_extreme", B=2, M=4, D=32, K=4, shapes=SMALL_PYRAMID, ref="uniform",
                     sigma_px=30.0, Nq=50, seed=181)

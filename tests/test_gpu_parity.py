@@ -184,6 +184,23 @@ def test_one_pixel_levels(D):
     parity(w)
 
 
+def random_workload(i):
+    rng = np.random.default_rng(7000 + i)
+    L = int(rng.integers(1, 6))
+    shapes = tuple((int(rng.integers(1, 41)), int(rng.integers(1, 71))) for _ in range(L))
+    return wl.Workload(f"random_{i}", B=int(rng.integers(1, 3)), M=int(rng.integers(1, 5)),
+                       D=int(rng.choice([8, 16, 32, 64])), K=int(rng.integers(1, 6)),
+                       shapes=shapes, ref="uniform", sigma_px=float(rng.uniform(0.5, 12.0)),
+                       Nq=int(rng.integers(1, 400)), seed=7100 + i)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_configurations(i):
+    # seeded draws of every size parameter: head width, levels and their
+    # shapes, points, heads, batch, queries and offset spread
+    parity(random_workload(i))
+
+
 def test_far_outside_and_non_finite_locations():
     w = wl.Workload("far", B=2, M=4, D=32, K=4, shapes=SMALL_PYRAMID, ref="uniform",
                     sigma_px=40.0, Nq=50, seed=81)
