@@ -110,6 +110,27 @@ def test_grid_geometries(kernel, stride, pad, dilation):
     parity(w)
 
 
+def random_dcn(i):
+    rng = np.random.default_rng(9000 + i)
+    while True:
+        k = (int(rng.integers(1, 6)), int(rng.integers(1, 6)))
+        w = wl.DcnWorkload(f"dcn_random_{i}", B=int(rng.integers(1, 3)),
+                           H=int(rng.integers(1, 30)), W=int(rng.integers(1, 40)),
+                           G=int(rng.integers(1, 5)), D=int(rng.choice([8, 16, 32, 64])),
+                           kernel=k, stride=(int(rng.integers(1, 4)), int(rng.integers(1, 4))),
+                           pad=(int(rng.integers(0, 4)), int(rng.integers(0, 4))),
+                           dilation=(int(rng.integers(1, 4)), int(rng.integers(1, 4))),
+                           sigma_px=float(rng.uniform(0.3, 4.0)), seed=9100 + i)
+        if min(w.out_size) >= 1:
+            return w
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_random_configurations(i):
+    # seeded draws of the sizes and of the grid geometry
+    parity(random_dcn(i))
+
+
 def test_far_and_non_finite_offsets():
     w = wl.DcnWorkload("dcn_far", B=1, H=12, W=15, G=4, D=16, sigma_px=25.0, seed=420)
     x = wl.generate_dcn(w)
