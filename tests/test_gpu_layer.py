@@ -99,7 +99,7 @@ def test_linear_without_bias_and_repeatable():
 
 # ---------------------------------------------------------------- the layer
 def _layer_inputs(x, dev):
-    t = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in x.items()}
+    t = {k: torch.from_numpy(np.array(v, copy=True)).to(dev) for k, v in x.items()}
     params = {k: t[k] for k in NAMES}
     return t, params
 
@@ -152,6 +152,20 @@ def test_layer_odd_head_sizes():
     # products (offset features not a multiple of 16)
     w = wl.Workload("layer_odd", B=2, M=1, D=16, K=3, shapes=((7, 9),), ref="uniform",
                     sigma_px=2.0, Nq=21, seed=320)
+    layer_parity(w)
+
+
+@pytest.mark.parametrize("i", range(3))
+def test_layer_random_configurations(i):
+    # seeded draws of heads, head width, levels and their shapes, points,
+    # batch and queries (dyadic activations and weights)
+    rng = np.random.default_rng(9500 + i)
+    L = int(rng.integers(1, 5))
+    shapes = tuple((int(rng.integers(1, 25)), int(rng.integers(1, 40))) for _ in range(L))
+    w = wl.Workload(f"layer_random_{i}", B=int(rng.integers(1, 3)), M=int(rng.integers(1, 5)),
+                    D=int(rng.choice([8, 16, 32])), K=int(rng.integers(1, 5)), shapes=shapes,
+                    ref="uniform", sigma_px=float(rng.uniform(0.5, 6.0)),
+                    Nq=int(rng.integers(1, 200)), seed=9600 + i)
     layer_parity(w)
 
 
