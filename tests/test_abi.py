@@ -300,3 +300,14 @@ def test_precision_checks():
         ctypes.byref(dims()), ctypes.byref(pr), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, gv, FAKE,
         FAKE, FAKE, ctypes.c_size_t(1 << 40), None)
     assert bwd(P(0, 0, 1), ctypes.c_void_p(0x10008)) == INVALID   # bf16 grad_value 16-byte
+
+
+def test_c_client_builds_and_reports_version():
+    # include/msda.h compiles as C99 with gcc, and a C program linked to the
+    # library reads its version (no GPU call)
+    import subprocess
+    import abi_client
+    binary = abi_client.BINARY if os.path.exists(abi_client.BINARY) else abi_client.build()
+    r = subprocess.run([binary], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    assert int(r.stdout.strip()) == msda.msda_version()
