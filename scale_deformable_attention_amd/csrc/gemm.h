@@ -5,6 +5,11 @@
 
 #include "msda.h"
 
+// Blocks of the matrix-core GEMM resident at once on the whole GPU (3 per CU
+// on 256 CUs): reduction splits are chosen so that one launch offers about
+// this many work items.
+constexpr int64_t kGemmResidentBlocks = 768;
+
 // C[m, n] = sum_k A(m, k) B(k, n) (+ bias[n]) (+ C[m, n] if accumulate), fp32.
 //   a_kmajor: A(m, k) = A[m * lda + k], else A[k * lda + m]
 //   b_kmajor: B(k, n) = B[n * ldb + k], else B[k * ldb + n]
@@ -54,5 +59,5 @@ msda_status_t msda_colsum(int R, int N, const float* g, int64_t ldg, float* out,
 
 // Reduction splits used for a weight gradient over `rows` rows, and the
 // workspace floats a linear backward needs.
-int msda_linear_splits(int64_t rows);
+int msda_linear_splits(int64_t rows, int64_t in_features, int64_t out_features);
 size_t msda_linear_workspace_floats(int64_t rows, int64_t in_features, int64_t out_features);

@@ -63,9 +63,9 @@ SavedPlan saved_plan(const msda_dims_t* d) {
     return p;
 }
 
-// Work items one matrix-core launch should offer: 4 resident 128 x 128
-// blocks on each of the 256 CUs.
-constexpr int64_t kGemmSlots = 1024;
+// Work items one matrix-core launch should offer: the resident 128 x 128
+// blocks of the whole GPU.
+constexpr int64_t kGemmSlots = kGemmResidentBlocks;
 
 int64_t tiles_of(int64_t rows, int64_t cols) { return ((rows + 127) / 128) * ((cols + 127) / 128); }
 
@@ -266,7 +266,7 @@ msda_status_t msda_layer_backward(const msda_dims_t* dims, const float* query,
     float* part = at<float>(workspace, wp.partials);
     const int C = (int)s.C, P = (int)s.P, A = (int)s.A;
     const int Rq = (int)s.rows_q, Rv = (int)s.rows_v;
-    const int sq = msda_linear_splits(Rq);
+    const int sq = msda_linear_splits(Rq, C, C);
     msda_status_t r;
 
     // output projection: dcore = dy W_out; dW_out = dy^T core; db_out = sum dy

@@ -11,9 +11,11 @@
 //   weight grad  dW[o, i] = sum_r dy[r, o] x[r, i]      (reduction over the rows,
 //                                                         split over blocks)
 // Block tile 128 x 128, four waves of 64 x 64, each a 2 x 2 grid of
-// v_mfma_f32_32x32x2_f32 (fp32 in, fp32 accumulate). A 16-deep slice of both
-// operands is staged in LDS, k-major, double buffered; the next slice's
-// global loads are in flight while the current one feeds the matrix cores.
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation, fed with three-term bf16
+// splits of the fp32 operands (six products per fp32 product, fp32 accuracy;
+// see msda_gemm_kernel). A 16-deep slice of both operands is staged in LDS,
+// split on the way, double buffered; the next slice's global loads are in
+// flight while the current one feeds the matrix cores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,22 +30,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;          // 4 waves
 constexpr int kTile = 128;             // block tile, rows and columns
-#ifndef MSDA_GEMM_BK
-#define MSDA_GEMM_BK 16
-#endif
-constexpr int kBK = MSDA_GEMM_BK;      // reduction slice per iteration
+constexpr int kBK = 16;                // reduction slice per iteration (one MFMA step)
 constexpr int kPerThread = kTile * kBK / 256;   // staged elements of an operand per thread
-constexpr int kHalf = kBK / 2;         // reduction steps of one MFMA lane half per slice
-constexpr int kRowK = kBK + 4;         // padded LDS row of the [row][k] layout (floats)
-#ifndef MSDA_GEMM_FRAG
-#define MSDA_GEMM_FRAG 8
-#endif
-#ifndef MSDA_GEMM_KLAYOUT
-#define MSDA_GEMM_KLAYOUT 1
-#endif
-constexpr int kLdsRow = kTile + 4;     // padded LDS row (floats)
 constexpr int kSplitMax = 256;         // reduction splits of a weight gradient at most
-constexpr int kLdsFloats = (kTile * kRowK > kBK * kLdsRow) ? kTile * kRowK : kBK * kLdsRow;
 
 // C = A B (+ bias) (+ C) with A(m, k), B(k, n) read through strides:
 //   kAK: A(m, k) = A[m * lda + k]   else A[k * lda + m]
@@ -87,18 +76,43 @@ __device__ inline int xcd_work_item() {
     return x * per + (x < rem ? x : rem) + i;
 }
 
-#ifndef MSDA_GEMM_WAVES_PER_EU
-#define MSDA_GEMM_WAVES_PER_EU 4
-#endif
+// The products on the bf16 matrix cores, to fp32 accuracy: every fp32
+// operand element x is split into three bf16 terms, x1 = bf16(x),
+// x2 = bf16(x - x1), x3 = bf16(x - x1 - x2) (round to nearest even; the
+// differences are exact in fp32), which carry x's 24 significant bits, and
+// a b is summed as the six products whose terms' orders add to at most 4:
+//   a1 b1 + a1 b2 + a2 b1 + a1 b3 + a2 b2 + a3 b1.
+// Each term keeps the remainder of the previous ones to within 2^-8 of it,
+// so |a - a1 - a2 - a3| <= 2^-24 |a|; the three dropped products and the two
+// remainders add up to less than 2^-22 |a b| (four fp32 unit roundings), and
+// every bf16 x bf16 product is exact in the fp32 accumulator, so the result
+// carries the error of an fp32 product sum, within a small factor. v_mfma_f32_32x32x16_bf16 runs at 16 times the fp32
+// rate, so the six products cost 3/8 of one fp32 product. A non-finite
+// operand element yields NaN in the rows and columns it feeds.
+//
+// LDS: per operand and buffer, three planes of kTile rows x 16 k (bf16,
+// 32 bytes a row); the two 16-byte halves of a row swap places on every
+// second group of 8 rows, so that the fragment reads (one half-row per lane,
+// rows 0..31 of a tile) hit distinct banks.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+constexpr int kSplitBK = kBK;                      // reduction slice (one MFMA step)
+constexpr int kPlane = kTile * kSplitBK;           // bf16 elements of one plane
+
+__device__ inline int swz(int row, int k) {      // element offset of (row, k) in a plane
+    return row * kSplitBK + ((((k >> 3) ^ (row >> 3)) & 1) << 3) + (k & 7);
+}
+
+__device__ inline void split3(float x, __bf16& h, __bf16& m, __bf16& l) {
+    h = (__bf16)x;
+    const float r1 = x - (float)h;
+    m = (__bf16)r1;
+    l = (__bf16)(r1 - (float)m);
+}
+
 template <bool kAK, bool kBKm, bool kVec>
-__global__ __launch_bounds__(kThreads, MSDA_GEMM_WAVES_PER_EU) void msda_gemm_kernel(GemmGroup grp) {
-    // LDS layout of a staged operand: [row][k] (k contiguous) when its global
-    // rows are k-contiguous and loaded as float4s -- stored as loaded, read
-    // back as float4s; otherwise [k][row]
-    constexpr bool kAmk = MSDA_GEMM_KLAYOUT && kAK && kVec;
-    constexpr bool kBmk = MSDA_GEMM_KLAYOUT && kBKm && kVec;
-    __shared__ float As[2][kLdsFloats];
-    __shared__ float Bs[2][kLdsFloats];
+__global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmGroup grp) {
+    __shared__ __attribute__((aligned(16))) __bf16 As[2][3 * kPlane];
+    __shared__ __attribute__((aligned(16))) __bf16 Bs[2][3 * kPlane];
     const int tid = threadIdx.x;
     const int work = xcd_work_item();
     int pi = 0;
@@ -112,41 +126,53 @@ __global__ __launch_bounds__(kThreads, MSDA_GEMM_WAVES_PER_EU) void msda_gemm_ke
     const int kbeg = z * g.k_split;
     const int kend = min(g.K + g.K2, kbeg + g.k_split);
 
-    // ---- staging: kTile * kBK elements of each operand per slice
+    // ---- staging: kTile * kSplitBK elements of each operand per slice; each
+    // thread takes groups of four consecutive k of one row (a float4 when the
+    // operand is k-contiguous, else four loads that the wave's lanes, on
+    // consecutive rows, read coalesced) and writes each group split into the
+    // three planes, 8 bytes per plane
     float ra[kPerThread], rb[kPerThread];
-    // k0 and kend relative to the operand's own segment
+    auto group = [&](bool kmajor, int i, int& mn, int& k) {
+        const int idx = tid + kThreads * i;
+        if (kmajor) {
+            mn = idx / (kSplitBK / 4);
+            k = (idx % (kSplitBK / 4)) * 4;
+        } else {
+            mn = idx % kTile;
+            k = (idx / kTile) * 4;
+        }
+    };
     auto load = [&](const float* P, int64_t ld, bool kmajor, int lim_mn, int base_mn, int k0,
                     int kend, float* r) {
         if constexpr (kVec) {
 #pragma unroll
             for (int i = 0; i < kPerThread / 4; ++i) {
-                const int idx = tid + kThreads * i;
                 int mn, k;
+                group(kmajor, i, mn, k);
+                const bool row_ok = base_mn + mn < lim_mn;
                 if (kmajor) {
-                    mn = idx / (kBK / 4);
-                    k = (idx % (kBK / 4)) * 4;
+                    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (row_ok && k0 + k < kend)
+                        v = *reinterpret_cast<const float4*>(P + (int64_t)(base_mn + mn) * ld +
+                                                             (k0 + k));
+                    r[4 * i] = v.x;
+                    r[4 * i + 1] = v.y;
+                    r[4 * i + 2] = v.z;
+                    r[4 * i + 3] = v.w;
                 } else {
-                    k = idx / (kTile / 4);
-                    mn = (idx % (kTile / 4)) * 4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        r[4 * i + e] = row_ok && k0 + k + e < kend
+                                           ? P[(int64_t)(k0 + k + e) * ld + (base_mn + mn)]
+                                           : 0.0f;
                 }
-                const bool ok = base_mn + mn < lim_mn && k0 + k < kend;
-                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (ok) {
-                    const float* src = kmajor ? P + (int64_t)(base_mn + mn) * ld + (k0 + k)
-                                              : P + (int64_t)(k0 + k) * ld + (base_mn + mn);
-                    v = *reinterpret_cast<const float4*>(src);
-                }
-                r[4 * i] = v.x;
-                r[4 * i + 1] = v.y;
-                r[4 * i + 2] = v.z;
-                r[4 * i + 3] = v.w;
             }
         } else {
 #pragma unroll
             for (int i = 0; i < kPerThread; ++i) {
                 const int idx = tid + kThreads * i;
-                const int mn = kmajor ? idx / kBK : idx % kTile;
-                const int k = kmajor ? idx % kBK : idx / kTile;
+                const int mn = kmajor ? idx / kSplitBK : idx % kTile;
+                const int k = kmajor ? idx % kSplitBK : idx / kTile;
                 const bool ok = base_mn + mn < lim_mn && k0 + k < kend;
                 r[i] = ok ? (kmajor ? P[(int64_t)(base_mn + mn) * ld + (k0 + k)]
                                     : P[(int64_t)(k0 + k) * ld + (base_mn + mn)])
@@ -154,38 +180,39 @@ __global__ __launch_bounds__(kThreads, MSDA_GEMM_WAVES_PER_EU) void msda_gemm_ke
             }
         }
     };
-    auto store = [&](float* S, bool kmajor, bool mk, const float* r) {
+    auto store = [&](__bf16* S, bool kmajor, const float* r) {
         if constexpr (kVec) {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
             for (int i = 0; i < kPerThread / 4; ++i) {
-                const int idx = tid + kThreads * i;
-                if (kmajor) {
-                    const int mn = idx / (kBK / 4), k = (idx % (kBK / 4)) * 4;
-                    if (mk) {
-                        *reinterpret_cast<float4*>(&S[mn * kRowK + k]) =
-                            make_float4(r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]);
-                    } else {
+                int mn, k;
+                group(kmajor, i, mn, k);
+                __bf16 h[4], m[4], l[4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) S[(k + e) * kLdsRow + mn] = r[4 * i + e];
-                    }
-                } else {
-                    const int k = idx / (kTile / 4), mn = (idx % (kTile / 4)) * 4;
-                    *reinterpret_cast<float4*>(&S[k * kLdsRow + mn]) =
-                        make_float4(r[4 * i], r[4 * i + 1], r[4 * i + 2], r[4 * i + 3]);
-                }
+                for (int e = 0; e < 4; ++e) split3(r[4 * i + e], h[e], m[e], l[e]);
+                const int o = swz(mn, k);
+                *reinterpret_cast<bf16x4*>(&S[o]) = bf16x4{h[0], h[1], h[2], h[3]};
+                *reinterpret_cast<bf16x4*>(&S[kPlane + o]) = bf16x4{m[0], m[1], m[2], m[3]};
+                *reinterpret_cast<bf16x4*>(&S[2 * kPlane + o]) = bf16x4{l[0], l[1], l[2], l[3]};
             }
         } else {
 #pragma unroll
             for (int i = 0; i < kPerThread; ++i) {
                 const int idx = tid + kThreads * i;
-                const int mn = kmajor ? idx / kBK : idx % kTile;
-                const int k = kmajor ? idx % kBK : idx / kTile;
-                S[k * kLdsRow + mn] = r[i];
+                const int mn = kmajor ? idx / kSplitBK : idx % kTile;
+                const int k = kmajor ? idx % kSplitBK : idx / kTile;
+                __bf16 h, m, l;
+                split3(r[i], h, m, l);
+                const int o = swz(mn, k);
+                S[o] = h;
+                S[kPlane + o] = m;
+                S[2 * kPlane + o] = l;
             }
         }
     };
 
-    // ---- wave tile 64 x 64 at (wm, wn); lane (li, lk) feeds row/column li, k-offset lk
+    // ---- wave tile 64 x 64 at (wm, wn); lane (li, lk) feeds row/column li
+    // with k = 8 lk .. 8 lk + 7 of the slice
     const int lane = tid & 63, w = tid >> 6;
     const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
     const int li = lane & 31, lk = lane >> 5;
@@ -197,12 +224,14 @@ __global__ __launch_bounds__(kThreads, MSDA_GEMM_WAVES_PER_EU) void msda_gemm_ke
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-    // column sums of A (a bias gradient rides along with its weight gradient):
-    // the blocks of column tile 0, one thread per row of the tile
-    const bool do_asum = g.asum != nullptr && n0 == 0 && tid < kTile;
+    // column sums of A (a bias gradient rides along with its weight
+    // gradient): with A not k-contiguous (the weight gradient's dy^T) the
+    // fp32 values are summed as staged -- rows tid % kTile, two threads per
+    // row, combined at the end; otherwise from the planes, one thread per row
+    constexpr bool kAsumStaged = kVec && !kAK;
+    const bool do_asum = g.asum != nullptr && n0 == 0 && (kAsumStaged || tid < kTile);
     float asum = 0.0f;
 
-    // slice k0 of the combined reduction, from its segment
     auto fetch = [&](int k0) {
         if (k0 >= g.K) {
             load(g.A2, g.lda2, kAK, g.M, m0, k0 - g.K, kend - g.K, ra);
@@ -213,68 +242,82 @@ __global__ __launch_bounds__(kThreads, MSDA_GEMM_WAVES_PER_EU) void msda_gemm_ke
         }
     };
 
+    auto asum_staged = [&]() {
+        if constexpr (kAsumStaged) {
+            if (do_asum) {
+#pragma unroll
+                for (int i = 0; i < kPerThread; ++i) asum += ra[i];
+            }
+        }
+    };
     int buf = 0;
     if (kbeg < kend) {
         fetch(kbeg);
-        store(As[0], kAK, kAmk, ra);
-        store(Bs[0], kBKm, kBmk, rb);
+        asum_staged();
+        store(As[0], kAK, ra);
+        store(Bs[0], kBKm, rb);
     }
     __syncthreads();
-    for (int k0 = kbeg; k0 < kend; k0 += kBK) {
-        const bool more = k0 + kBK < kend;
-        if (more) fetch(k0 + kBK);
-        const float* Ab = As[buf];
-        const float* Bb = Bs[buf];
-        // MFMA step s sums over k = lk * kHalf + s (the lane halves take the
-        // slice's two halves): a lane's operands of a slice are then kHalf
-        // consecutive k of one row
-        // fragments read kFrag k's at a time (fewer live registers)
-        constexpr int kFrag = MSDA_GEMM_FRAG;
-        auto frag = [&](const float* S, bool mk, int row, int q0, float* v) {
-            if (mk) {
+    for (int k0 = kbeg; k0 < kend; k0 += kSplitBK) {
+        const bool more = k0 + kSplitBK < kend;
+        if (more) {
+            fetch(k0 + kSplitBK);
+            asum_staged();
+        }
+        const __bf16* Ab = As[buf];
+        const __bf16* Bb = Bs[buf];
+        bf16x8 fa[2][3], fb[2][3];
 #pragma unroll
-                for (int q = 0; q < kFrag; q += 4) {
-                    const float4 f =
-                        *reinterpret_cast<const float4*>(&S[row * kRowK + lk * kHalf + q0 + q]);
-                    v[q] = f.x;
-                    v[q + 1] = f.y;
-                    v[q + 2] = f.z;
-                    v[q + 3] = f.w;
-                }
-            } else {
+        for (int t2 = 0; t2 < 2; ++t2) {
+            const int ar = wm + 32 * t2 + li, br = wn + 32 * t2 + li;
 #pragma unroll
-                for (int q = 0; q < kFrag; ++q) v[q] = S[(lk * kHalf + q0 + q) * kLdsRow + row];
-            }
-        };
-#pragma unroll
-        for (int q0 = 0; q0 < kHalf; q0 += kFrag) {
-            float a0v[kFrag], a1v[kFrag], b0v[kFrag], b1v[kFrag];
-            frag(Ab, kAmk, wm + li, q0, a0v);
-            frag(Ab, kAmk, wm + 32 + li, q0, a1v);
-            frag(Bb, kBmk, wn + li, q0, b0v);
-            frag(Bb, kBmk, wn + 32 + li, q0, b1v);
-#pragma unroll
-            for (int q = 0; q < kFrag; ++q) {
-                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0v[q], b0v[q], acc[0][0], 0, 0, 0);
-                acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0v[q], b1v[q], acc[0][1], 0, 0, 0);
-                acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1v[q], b0v[q], acc[1][0], 0, 0, 0);
-                acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1v[q], b1v[q], acc[1][1], 0, 0, 0);
+            for (int q = 0; q < 3; ++q) {
+                fa[t2][q] = *reinterpret_cast<const bf16x8*>(&Ab[q * kPlane + swz(ar, 8 * lk)]);
+                fb[t2][q] = *reinterpret_cast<const bf16x8*>(&Bb[q * kPlane + swz(br, 8 * lk)]);
             }
         }
-        if (do_asum) {
+        // the six products, each over the four tiles in turn (independent
+        // accumulators between dependent steps)
+        constexpr int kPa[6] = {0, 0, 1, 0, 1, 2};
+        constexpr int kPb[6] = {0, 1, 0, 2, 1, 0};
 #pragma unroll
-            for (int q = 0; q < kBK; ++q)
-                asum += kAmk ? Ab[tid * kRowK + q] : Ab[q * kLdsRow + tid];
+        for (int pr = 0; pr < 6; ++pr) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a][kPa[pr]],
+                                                                         fb[b][kPb[pr]],
+                                                                         acc[a][b], 0, 0, 0);
+        }
+        if constexpr (!kAsumStaged) {
+            if (do_asum) {
+#pragma unroll
+                for (int q = 0; q < kSplitBK; ++q) {
+                    const int o = swz(tid, q);
+                    asum += ((float)Ab[o] + (float)Ab[kPlane + o]) + (float)Ab[2 * kPlane + o];
+                }
+            }
         }
         if (more) {
-            store(As[buf ^ 1], kAK, kAmk, ra);
-            store(Bs[buf ^ 1], kBKm, kBmk, rb);
+            store(As[buf ^ 1], kAK, ra);
+            store(Bs[buf ^ 1], kBKm, rb);
         }
         __syncthreads();
         buf ^= 1;
     }
 
-    if (do_asum && m0 + tid < g.M) g.asum[(int64_t)z * g.M + m0 + tid] = asum;
+    if constexpr (kAsumStaged) {
+        if (g.asum != nullptr && n0 == 0) {   // block-uniform
+            float* red = reinterpret_cast<float*>(As[0]);   // free after the last barrier
+            red[tid] = asum;
+            __syncthreads();
+            if (tid < kTile && m0 + tid < g.M)
+                g.asum[(int64_t)z * g.M + m0 + tid] = red[tid] + red[tid + kTile];
+        }
+    } else {
+        if (do_asum && m0 + tid < g.M) g.asum[(int64_t)z * g.M + m0 + tid] = asum;
+    }
 
     // ---- epilogue: 32x32 accumulator register r of lane (li, lk) holds
     // row 8 * (r / 4) + 4 * lk + r % 4, column li
@@ -361,9 +404,11 @@ __global__ __launch_bounds__(kThreads) void msda_colsum_kernel(const float* g, i
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int splits_for(int64_t R) {
-    // about 2 blocks per CU for the weight gradient's 128 x 128 tiles
-    const int64_t want = (R + 255) / 256;
+int splits_for(int64_t R, int64_t in_features, int64_t out_features) {
+    // the weight gradient's 128 x 128 tiles times the splits fill the GPU's
+    // resident blocks once (kGemmResidentBlocks), at least 256 rows a split
+    const int64_t tiles = ((in_features + kTile - 1) / kTile) * ((out_features + kTile - 1) / kTile);
+    const int64_t want = std::min<int64_t>((R + 255) / 256, kGemmResidentBlocks / std::max<int64_t>(tiles, 1));
     return (int)std::max<int64_t>(1, std::min<int64_t>(kSplitMax, want));
 }
 
@@ -531,11 +576,13 @@ msda_status_t msda_colsum(int R, int N, const float* g, int64_t ldg, float* out,
 // Workspace of a linear backward: the weight gradient's split partials and
 // the bias gradient's.
 size_t msda_linear_workspace_floats(int64_t rows, int64_t in_features, int64_t out_features) {
-    const int s = splits_for(rows);
+    const int s = splits_for(rows, in_features, out_features);
     return (size_t)s * (size_t)in_features * (size_t)out_features + (size_t)s * (size_t)out_features;
 }
 
-int msda_linear_splits(int64_t rows) { return splits_for(rows); }
+int msda_linear_splits(int64_t rows, int64_t in_features, int64_t out_features) {
+    return splits_for(rows, in_features, out_features);
+}
 
 namespace {
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
@@ -590,7 +637,7 @@ msda_status_t msda_linear_backward(int64_t rows, int64_t in_features, int64_t ou
         if (!workspace || workspace_bytes < need) return MSDA_ERROR_INVALID_VALUE;
     }
     const int R = (int)rows, I = (int)in_features, O = (int)out_features;
-    const int splits = splits_for(rows);
+    const int splits = splits_for(rows, in_features, out_features);
     float* part_w = static_cast<float*>(workspace);
     float* part_b = part_w ? part_w + (size_t)splits * I * O : nullptr;
     msda_status_t s = MSDA_SUCCESS;
