@@ -712,25 +712,31 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
 }
 
 // ---- grad_value tiles
-constexpr int kTileH = 4;           // pixel rows per tile
+// Pixel rows per tile: kTileH, or kTileHTall where the points are sparse
+// (fewer than one per pixel): a tall tile gathers twice the pixels' entries
+// per work item, and with few entries per tile the per-item latency (work
+// counter, table row, entry loads) is what costs.
+constexpr int kTileH = 4;
+constexpr int kTileHTall = 8;
 constexpr int kBinRange = 1024;     // tile counters a bin block keeps in LDS at once
 constexpr int kBinUnroll = 8;       // points per thread in flight in the bin kernel
 constexpr int kChunk = 1024;        // entries a tile block sorts in LDS at once
 constexpr int kMinQueries = 64;     // queries per bin block at least (when there are enough)
 constexpr int kMaxSlabs = 64;       // bin blocks per (b, m) at most (a power of two)
 constexpr int kUnroll = 8;          // entries in flight per lane group in the sweep
+constexpr int kUnrollTall = 2;      // the same for tall tiles (few entries per cell column)
 
-// A tile is kTileH x TW pixels. Its pixels are fed by the cells (top-left
-// corners) in cell rows -1 .. kTileH-1 and cell columns -1 .. TW-1 relative to
+// A tile is TH x TW pixels. Its pixels are fed by the cells (top-left
+// corners) in cell rows -1 .. TH-1 and cell columns -1 .. TW-1 relative to
 // it: NG = TW + 1 cell columns, one per lane group of a tile block (4 fp32
 // channels per lane).
-template <int D>
+template <int D, int TH>
 struct TileShape {
     static constexpr int PL = 4;
     static constexpr int G = D / PL;
     static constexpr int NG = kBlock / G;   // lane groups
     static constexpr int TW = NG - 1;       // pixel columns per tile
-    static constexpr int kCells = (kTileH + 1) * NG;
+    static constexpr int kCells = (TH + 1) * NG;
     static_assert(TW >= 15, "tile width");
 };
 
@@ -739,7 +745,7 @@ struct LevelTiles {
 };
 
 // Per-level tile grid of one (b, m): thread 0 fills the table, everyone waits.
-template <int TW>
+template <int TW, int TH>
 __device__ inline void setup_tiles(const Params& p, LevelTiles* lt, int* total) {
     if (threadIdx.x == 0) {
         int base = 0;
@@ -752,7 +758,7 @@ __device__ inline void setup_tiles(const Params& p, LevelTiles* lt, int* total) 
             t.ntx = (t.W + TW - 1) / TW;
             t.pad0 = t.pad1 = t.pad2 = 0;
             lt[l] = t;
-            base += ((t.H + kTileH - 1) / kTileH) * t.ntx;
+            base += ((t.H + TH - 1) / TH) * t.ntx;
         }
         *total = base;
     }
@@ -816,7 +822,7 @@ __device__ inline uint32_t block_exclusive_scan(const uint32_t* a, uint32_t* o, 
 // and emit[c] says whether corner c is inside the level and is the first
 // corner of its tile.
 // (u, v) normalized, or with kPixel already the pixel coordinates (x, y).
-template <int TW, bool kPixel>
+template <int TW, int TH, bool kPixel>
 __device__ inline void point_tiles(float u, float v, const LevelTiles& lt, int* tile, bool* emit) {
     const float Hf = (float)lt.H, Wf = (float)lt.W;
     const float x = kPixel ? u : fmaf(u, Wf, -0.5f);
@@ -832,7 +838,7 @@ __device__ inline void point_tiles(float u, float v, const LevelTiles& lt, int* 
     // i.e. where the pixel coordinate is >= 0)
     const int tx0 = (int)((uint32_t)max(x0, 0) / (uint32_t)TW);
     const int tx1 = (int)((uint32_t)(x0 + 1) / (uint32_t)TW);
-    const int ty0 = max(y0, 0) / kTileH, ty1 = (y0 + 1) / kTileH;
+    const int ty0 = max(y0, 0) / TH, ty1 = (y0 + 1) / TH;
     const bool v00 = vx0 && vy0, v01 = vx1 && vy0, v10 = vx0 && vy1, v11 = vx1 && vy1;
     const bool same_x = tx0 == tx1, same_y = ty0 == ty1;
     emit[0] = v00;
@@ -887,15 +893,15 @@ struct PointWalk {
     }
 };
 
-template <int D, int FE>
+template <int D, int FE, int TH>
 __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
-    using TS = TileShape<D>;
+    using TS = TileShape<D, TH>;
     __shared__ LevelTiles lt[MSDA_MAX_LEVELS];
     __shared__ int s_tiles;
     __shared__ uint32_t cnt[kBinRange];
     __shared__ uint32_t off[kBinRange];
     __shared__ uint32_t scratch[kWavesPerBlock];
-    setup_tiles<TS::TW>(p, lt, &s_tiles);
+    setup_tiles<TS::TW, TH>(p, lt, &s_tiles);
     // tables inconsistent with Nv could exceed the row: drop those tiles
     // rather than write past the workspace
     const int T = block_uniform(min(s_tiles, p.t_stride));
@@ -949,7 +955,7 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
             for (int u = 0; u < kBinUnroll; ++u) {
                 int tile[4];
                 bool emit[4];
-                point_tiles<TS::TW, FE == kFeDcn>(uv[u].x, uv[u].y, lt[lvl[u]], tile, emit);
+                point_tiles<TS::TW, TH, FE == kFeDcn>(uv[u].x, uv[u].y, lt[lvl[u]], tile, emit);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     if (ok[u] && emit[c] && tile[c] >= r0 && tile[c] < r0 + rn)
@@ -982,7 +988,7 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
                 int tile[4];
                 bool emit[4];
                 const LevelTiles& L_ = lt[lvl[u]];
-                point_tiles<TS::TW, FE == kFeDcn>(uv[u].x, uv[u].y, L_, tile, emit);
+                point_tiles<TS::TW, TH, FE == kFeDcn>(uv[u].x, uv[u].y, L_, tile, emit);
                 // the entry carries all the tile kernel needs: the tuple (its
                 // upstream-gradient row), the fp32 pixel coordinates (cell and
                 // fractions follow from them exactly as here) and the weight
@@ -1010,11 +1016,24 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
 // start first. A block takes the tile's entries kChunk at a time: loads them,
 // counting-sorts them by cell into LDS records that already hold the four
 // corner weights, then sweeps the cells column by column.
-template <int D, bool kBf16Out>
-__global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
-    using TS = TileShape<D>;
+template <int D, bool kBf16Out, int TH>
+// (tall tiles: at most 128 VGPRs, so that 4 blocks fit per CU)
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TH == kTileHTall ? 4 : 1)))
+void msda_tile_kernel(Params p) {
+    using TS = TileShape<D, TH>;
     constexpr int TW = TS::TW, NG = TS::NG, G = TS::G, kCells = TS::kCells;
-    static_assert(kTileH * kBlock <= kChunk, "the column exchange reuses the record buffer");
+    // the column exchange reuses the record buffer, kXch pixel rows at a
+    // time; the zero record sits after the chunk's records
+    constexpr int kXch = kChunk / kBlock < TH ? kChunk / kBlock : TH;
+    static_assert(TH % kXch == 0, "exchange rows");
+    constexpr int kZero = kChunk;
+    // Tall tiles (sparse points) order the cells column by column, so that a
+    // lane group's entries form one range and all its loads go out together
+    // (a cell-row-by-row sweep waits for one load round trip per non-empty
+    // cell row of the wave's columns); each record then carries its cell row
+    // in the low bits of the row offset (a multiple of 4 D >= 32).
+    constexpr bool kColMajor = TH == kTileHTall;
+    static_assert(!kColMajor || (TH < 16 && D * sizeof(float) >= 16), "cell row in the offset's low bits");
     constexpr int kPer = kChunk / kBlock;   // entries per thread per chunk
     static_assert(kPer * kBlock == kChunk, "chunk size");
     __shared__ LevelTiles lt[MSDA_MAX_LEVELS];
@@ -1023,17 +1042,17 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
     // a chunk's entries in cell order: the four corner weights (top-left,
     // top-right, bottom-left, bottom-right) and the byte offset of the
     // upstream-gradient row
-    // (slot kChunk: a zero record for the sweep's slots past a range's end)
-    __shared__ float4 wrec[kChunk + 1];
-    __shared__ uint32_t grec[kChunk + 1];
+    // (slot kZero: a zero record for the sweep's slots past a range's end)
+    __shared__ float4 wrec[kZero + 1];
+    __shared__ uint32_t grec[kZero + 1];
     __shared__ uint32_t cstart[kCells + 1];
     __shared__ uint32_t ccount[kCells + 1];
     __shared__ uint32_t scratch[kWavesPerBlock];
     if (threadIdx.x == 0) {
-        wrec[kChunk] = make_float4(0.f, 0.f, 0.f, 0.f);
-        grec[kChunk] = kOutside;   // out of the buffer's range: loads zeros
+        wrec[kZero] = make_float4(0.f, 0.f, 0.f, 0.f);
+        grec[kZero] = kOutside;   // out of the buffer's range: loads zeros
     }
-    setup_tiles<TW>(p, lt, &s_tiles);
+    setup_tiles<TW, TH>(p, lt, &s_tiles);
     const int T = block_uniform(min(s_tiles, p.t_stride));
     const int tid = threadIdx.x;
     const int BM = p.B * p.M;
@@ -1064,7 +1083,7 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
         while (l + 1 < p.L && lt[l + 1].tile_base <= tl) ++l;
         const LevelTiles L_ = lt[l];
         const int ty = (tl - L_.tile_base) / L_.ntx, tx = (tl - L_.tile_base) - ty * L_.ntx;
-        const int y_base = ty * kTileH, x_base = tx * TW;
+        const int y_base = ty * TH, x_base = tx * TW;
         const int b = bm / p.M, m = bm - b * p.M;
 
         // this tile's entries in every slab of (b, m)
@@ -1076,9 +1095,9 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
         __syncthreads();
         const uint32_t E = (uint32_t)block_uniform((int)block_exclusive_scan(wcnt, wstart, p.nW, scratch));
 
-        float4 own[kTileH], prev[kTileH];
+        float4 own[TH], prev[TH];
 #pragma unroll
-        for (int y = 0; y < kTileH; ++y) {
+        for (int y = 0; y < TH; ++y) {
             own[y] = make_float4(0.f, 0.f, 0.f, 0.f);
             prev[y] = own[y];
         }
@@ -1108,9 +1127,9 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
             for (int j = 0; j < kPer; ++j) {
                 // an entry has a corner in this tile, so its cell is within
                 // one pixel of it; clamp anyway to stay in bounds
-                const int cy = min(max((int)floorf(ent[j].z) - y_base, -1), kTileH - 1);
+                const int cy = min(max((int)floorf(ent[j].z) - y_base, -1), TH - 1);
                 const int cx = min(max((int)floorf(ent[j].y) - x_base, -1), TW - 1);
-                cell[j] = (cy + 1) * NG + (cx + 1);
+                cell[j] = kColMajor ? (cx + 1) * (TH + 1) + (cy + 1) : (cy + 1) * NG + (cx + 1);
                 if (tid + j * kBlock < n) atomicAdd(&ccount[cell[j]], 1u);
             }
             __syncthreads();
@@ -1125,57 +1144,101 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
                     const float fx = x - floorf(x), fy = y - floorf(y);
                     const float at = a * (1.0f - fy), ab = a * fy;
                     wrec[slot] = make_float4(at * (1.0f - fx), at * fx, ab * (1.0f - fx), ab * fx);
-                    grec[slot] = as_uint(ent[j].x) * (uint32_t)(D * sizeof(float));
+                    grec[slot] = as_uint(ent[j].x) * (uint32_t)(D * sizeof(float)) +
+                                 (kColMajor ? (uint32_t)(cell[j] % (TH + 1)) : 0u);
                 }
             }
             __syncthreads();
             // cell-column sweep: lane group col takes the cells of cell column
-            // col - 1 (one contiguous range per cell row) and adds each entry's
-            // right corners to pixel column col (own) and its left corners to
-            // pixel column col - 1 (prev), one upstream-gradient row per entry.
-            // kUnroll entries are in flight at once; slots past the end of the
-            // group's range read the zero record.
+            // col - 1 and adds each entry's right corners to pixel column col
+            // (own) and its left corners to pixel column col - 1 (prev), one
+            // upstream-gradient row per entry. kUnroll entries are in flight
+            // at once; slots past the end of the group's range read the zero
+            // record.
             const uint32_t lane_off = (uint32_t)r * 16u;
-#pragma unroll
-            for (int cr = 0; cr <= kTileH; ++cr) {   // cell row cy = cr - 1
-                const int lc = cr * NG + col;
-                const uint32_t s0 = cstart[lc], e = cstart[lc + 1];
-                for (uint32_t k = s0; k < e; k += kUnroll) {
+            if constexpr (kColMajor) {
+                // the column's cells in one range; a cell in cell row cr has
+                // its top corners on pixel row cr - 1 and its bottom corners
+                // on pixel row cr, picked per entry (a product is added only
+                // to its own rows, so a non-finite gradient stays there)
+                const uint32_t s0 = cstart[col * (TH + 1)], e = cstart[(col + 1) * (TH + 1)];
+                for (uint32_t k = s0; k < e; k += kUnrollTall) {
                     const uint32_t rem = e - k;
-                    float4 gv[kUnroll], wv[kUnroll];
+                    float4 gv[kUnrollTall], wv[kUnrollTall];
+                    int crow[kUnrollTall];
 #pragma unroll
-                    for (int u = 0; u < kUnroll; ++u) {
-                        const uint32_t si = (uint32_t)u < rem ? k + u : (uint32_t)kChunk;
+                    for (int u = 0; u < kUnrollTall; ++u) {
+                        const uint32_t si = (uint32_t)u < rem ? k + u : (uint32_t)kZero;
                         wv[u] = wrec[si];
+                        const uint32_t gr = grec[si];
+                        crow[u] = (int)(gr & 15u);
                         const u32x4 graw = __builtin_amdgcn_raw_buffer_load_b128(
-                            grsrc, grec[si] + lane_off, 0, 0);
+                            grsrc, (gr & ~15u) + lane_off, 0, 0);
                         gv[u] = make_float4(as_float(graw[0]), as_float(graw[1]),
                                             as_float(graw[2]), as_float(graw[3]));
                     }
 #pragma unroll
-                    for (int u = 0; u < kUnroll; ++u) {
-                        {
-                            // a cell in cell row cr has its top corners on pixel
-                            // row cr - 1 and its bottom corners on pixel row cr
-                            if (cr >= 1) {
-                                prev[cr - 1].x = fmaf(wv[u].x, gv[u].x, prev[cr - 1].x);
-                                prev[cr - 1].y = fmaf(wv[u].x, gv[u].y, prev[cr - 1].y);
-                                prev[cr - 1].z = fmaf(wv[u].x, gv[u].z, prev[cr - 1].z);
-                                prev[cr - 1].w = fmaf(wv[u].x, gv[u].w, prev[cr - 1].w);
-                                own[cr - 1].x = fmaf(wv[u].y, gv[u].x, own[cr - 1].x);
-                                own[cr - 1].y = fmaf(wv[u].y, gv[u].y, own[cr - 1].y);
-                                own[cr - 1].z = fmaf(wv[u].y, gv[u].z, own[cr - 1].z);
-                                own[cr - 1].w = fmaf(wv[u].y, gv[u].w, own[cr - 1].w);
+                    for (int u = 0; u < kUnrollTall; ++u) {
+#pragma unroll
+                        for (int y = 0; y < TH; ++y) {
+                            const bool top = y == crow[u] - 1, bot = y == crow[u];
+                            const float wl = top ? wv[u].x : wv[u].z;
+                            const float wr = top ? wv[u].y : wv[u].w;
+                            if (top || bot) {
+                                prev[y].x = fmaf(wl, gv[u].x, prev[y].x);
+                                prev[y].y = fmaf(wl, gv[u].y, prev[y].y);
+                                prev[y].z = fmaf(wl, gv[u].z, prev[y].z);
+                                prev[y].w = fmaf(wl, gv[u].w, prev[y].w);
+                                own[y].x = fmaf(wr, gv[u].x, own[y].x);
+                                own[y].y = fmaf(wr, gv[u].y, own[y].y);
+                                own[y].z = fmaf(wr, gv[u].z, own[y].z);
+                                own[y].w = fmaf(wr, gv[u].w, own[y].w);
                             }
-                            if (cr < kTileH) {
-                                prev[cr].x = fmaf(wv[u].z, gv[u].x, prev[cr].x);
-                                prev[cr].y = fmaf(wv[u].z, gv[u].y, prev[cr].y);
-                                prev[cr].z = fmaf(wv[u].z, gv[u].z, prev[cr].z);
-                                prev[cr].w = fmaf(wv[u].z, gv[u].w, prev[cr].w);
-                                own[cr].x = fmaf(wv[u].w, gv[u].x, own[cr].x);
-                                own[cr].y = fmaf(wv[u].w, gv[u].y, own[cr].y);
-                                own[cr].z = fmaf(wv[u].w, gv[u].z, own[cr].z);
-                                own[cr].w = fmaf(wv[u].w, gv[u].w, own[cr].w);
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int cr = 0; cr <= TH; ++cr) {   // cell row cy = cr - 1
+                    const int lc = cr * NG + col;
+                    const uint32_t s0 = cstart[lc], e = cstart[lc + 1];
+                    for (uint32_t k = s0; k < e; k += kUnroll) {
+                        const uint32_t rem = e - k;
+                        float4 gv[kUnroll], wv[kUnroll];
+#pragma unroll
+                        for (int u = 0; u < kUnroll; ++u) {
+                            const uint32_t si = (uint32_t)u < rem ? k + u : (uint32_t)kZero;
+                            wv[u] = wrec[si];
+                            const u32x4 graw = __builtin_amdgcn_raw_buffer_load_b128(
+                                grsrc, grec[si] + lane_off, 0, 0);
+                            gv[u] = make_float4(as_float(graw[0]), as_float(graw[1]),
+                                                as_float(graw[2]), as_float(graw[3]));
+                        }
+#pragma unroll
+                        for (int u = 0; u < kUnroll; ++u) {
+                            {
+                                // a cell in cell row cr has its top corners on pixel
+                                // row cr - 1 and its bottom corners on pixel row cr
+                                if (cr >= 1) {
+                                    prev[cr - 1].x = fmaf(wv[u].x, gv[u].x, prev[cr - 1].x);
+                                    prev[cr - 1].y = fmaf(wv[u].x, gv[u].y, prev[cr - 1].y);
+                                    prev[cr - 1].z = fmaf(wv[u].x, gv[u].z, prev[cr - 1].z);
+                                    prev[cr - 1].w = fmaf(wv[u].x, gv[u].w, prev[cr - 1].w);
+                                    own[cr - 1].x = fmaf(wv[u].y, gv[u].x, own[cr - 1].x);
+                                    own[cr - 1].y = fmaf(wv[u].y, gv[u].y, own[cr - 1].y);
+                                    own[cr - 1].z = fmaf(wv[u].y, gv[u].z, own[cr - 1].z);
+                                    own[cr - 1].w = fmaf(wv[u].y, gv[u].w, own[cr - 1].w);
+                                }
+                                if (cr < TH) {
+                                    prev[cr].x = fmaf(wv[u].z, gv[u].x, prev[cr].x);
+                                    prev[cr].y = fmaf(wv[u].z, gv[u].y, prev[cr].y);
+                                    prev[cr].z = fmaf(wv[u].z, gv[u].z, prev[cr].z);
+                                    prev[cr].w = fmaf(wv[u].z, gv[u].w, prev[cr].w);
+                                    own[cr].x = fmaf(wv[u].w, gv[u].x, own[cr].x);
+                                    own[cr].y = fmaf(wv[u].w, gv[u].y, own[cr].y);
+                                    own[cr].z = fmaf(wv[u].w, gv[u].z, own[cr].z);
+                                    own[cr].w = fmaf(wv[u].w, gv[u].w, own[cr].w);
+                                }
                             }
                         }
                     }
@@ -1188,23 +1251,27 @@ __global__ __launch_bounds__(kBlock) void msda_tile_kernel(Params p) {
         // which no thread reads any more
         float4* xch = wrec;
 #pragma unroll
-        for (int yy = 0; yy < kTileH; ++yy) xch[yy * kBlock + tid] = prev[yy];
-        __syncthreads();
-        if (col < TW) {
+        for (int h = 0; h < TH; h += kXch) {
+            if (h > 0) __syncthreads();   // the previous rows have been read
 #pragma unroll
-            for (int yy = 0; yy < kTileH; ++yy) {
-                const float4 nb = xch[yy * kBlock + tid + G];
-                own[yy].x += nb.x;
-                own[yy].y += nb.y;
-                own[yy].z += nb.z;
-                own[yy].w += nb.w;
+            for (int yy = 0; yy < kXch; ++yy) xch[yy * kBlock + tid] = prev[h + yy];
+            __syncthreads();
+            if (col < TW) {
+#pragma unroll
+                for (int yy = 0; yy < kXch; ++yy) {
+                    const float4 nb = xch[yy * kBlock + tid + G];
+                    own[h + yy].x += nb.x;
+                    own[h + yy].y += nb.y;
+                    own[h + yy].z += nb.z;
+                    own[h + yy].w += nb.w;
+                }
             }
         }
         // every pixel of the tile that is inside the level, written once
         const int x = x_base + col;
         if (col < TW && x < L_.W) {
 #pragma unroll
-            for (int yy = 0; yy < kTileH; ++yy) {
+            for (int yy = 0; yy < TH; ++yy) {
                 const int y = y_base + yy;
                 if (y < L_.H) {
                     const size_t rowi = (size_t)b * p.Nv + L_.start + (size_t)y * L_.W + x;
@@ -1331,6 +1398,7 @@ msda_status_t check_dims(const msda_dims_t* d, msda_dtype_t dt, bool backward) {
 // so sum_l <= Nv/4 + L.
 struct BwdPlan {
     int64_t nW = 0, Qc = 0, t_stride = 0, slab_per_block = 0;
+    int tall = 0;   // tiles of kTileHTall rows (1) or kTileH rows (0)
     size_t counters_off = 0, table_off = 0, slab_off = 0, bytes = 0;
 };
 
@@ -1351,7 +1419,9 @@ BwdPlan plan_backward(const msda_dims_t* d) {
     pl.nW = Qc > 0 ? (d->Nq + Qc - 1) / Qc : 1;
     pl.Qc = Qc;
     pl.t_stride = (d->Nv + 3) / 4 + d->L;
-    static_assert(kTileH == 4, "the tile-count bound above assumes 4-row tiles");
+    static_assert(kTileH >= 4 && kTileHTall >= 4, "the tile-count bound above assumes tiles of 4 rows or more");
+    // tall tiles where a (b, m) has fewer points than pixels
+    pl.tall = d->Nq * d->L * d->K < d->Nv ? 1 : 0;
     pl.slab_per_block = round_up((size_t)(4 * Qc * d->L * d->K), 64);
     const size_t table_bytes = (size_t)(BM * pl.nW * pl.t_stride) * sizeof(uint2);
     const size_t slab_bytes = (size_t)(BM * pl.nW * pl.slab_per_block) * sizeof(float4);
@@ -1397,9 +1467,10 @@ Sizes sizes_of(const msda_dims_t* d) {
 
 // Blocks of the tile kernel that fit on one CU, asked of the runtime once per
 // kernel and kept.
-int tile_blocks_per_cu(int64_t D, const void* kernel, bool bf16_out) {
-    static std::atomic<int> known[8];
-    std::atomic<int>& slot = known[(D == 8 ? 0 : D == 16 ? 1 : D == 32 ? 2 : 3) + (bf16_out ? 4 : 0)];
+int tile_blocks_per_cu(int64_t D, const void* kernel, bool bf16_out, int tall) {
+    static std::atomic<int> known[16];
+    std::atomic<int>& slot =
+        known[(D == 8 ? 0 : D == 16 ? 1 : D == 32 ? 2 : 3) + (bf16_out ? 4 : 0) + (tall ? 8 : 0)];
     int n = slot.load(std::memory_order_relaxed);
     if (n > 0) return n;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kBlock, 0) != hipSuccess || n < 1) n = 1;
@@ -1418,18 +1489,19 @@ msda_status_t launch(const void* kernel, int64_t blocks, Params& p, hipStream_t 
 struct Kernels {
     const void* fwd = nullptr;
     const void* point = nullptr;
-    const void* bin = nullptr;
-    const void* tile = nullptr;
+    // bin and tile kernels: [0] tiles of kTileH rows, [1] of kTileHTall rows
+    const void* bin[2] = {};
+    const void* tile[2] = {};
     const void* fwd_fused = nullptr;
     const void* point_fused = nullptr;
-    const void* bin_fused = nullptr;
+    const void* bin_fused[2] = {};
     const void* fwd_dcn = nullptr;
     const void* point_dcn = nullptr;
-    const void* bin_dcn = nullptr;
+    const void* bin_dcn[2] = {};
     const void* fwd_half = nullptr;     // binary16 locations and weights
     const void* point_half = nullptr;
-    const void* bin_half = nullptr;
-    const void* tile_bf16 = nullptr;    // grad_value stored as bf16
+    const void* bin_half[2] = {};
+    const void* tile_bf16[2] = {};      // grad_value stored as bf16
     int tuples_per_block = 0;
 };
 
@@ -1438,18 +1510,24 @@ Kernels kernels_for() {
     Kernels k;
     k.fwd = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D, kFeCore>);
     k.point = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D, kFeCore>);
-    k.bin = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCore>);
+    k.bin[0] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCore, kTileH>);
+    k.bin[1] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCore, kTileHTall>);
     k.fwd_fused = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D, kFeFused>);
     k.point_fused = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D, kFeFused>);
-    k.bin_fused = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeFused>);
+    k.bin_fused[0] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeFused, kTileH>);
+    k.bin_fused[1] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeFused, kTileHTall>);
     k.fwd_dcn = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D, kFeDcn>);
     k.point_dcn = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D, kFeDcn>);
-    k.bin_dcn = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeDcn>);
+    k.bin_dcn[0] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeDcn, kTileH>);
+    k.bin_dcn[1] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeDcn, kTileHTall>);
     k.fwd_half = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D, kFeCoreHalf>);
     k.point_half = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D, kFeCoreHalf>);
-    k.bin_half = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCoreHalf>);
-    k.tile = reinterpret_cast<const void*>(&msda_tile_kernel<D, false>);
-    k.tile_bf16 = reinterpret_cast<const void*>(&msda_tile_kernel<D, true>);
+    k.bin_half[0] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCoreHalf, kTileH>);
+    k.bin_half[1] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCoreHalf, kTileHTall>);
+    k.tile[0] = reinterpret_cast<const void*>(&msda_tile_kernel<D, false, kTileH>);
+    k.tile[1] = reinterpret_cast<const void*>(&msda_tile_kernel<D, false, kTileHTall>);
+    k.tile_bf16[0] = reinterpret_cast<const void*>(&msda_tile_kernel<D, true, kTileH>);
+    k.tile_bf16[1] = reinterpret_cast<const void*>(&msda_tile_kernel<D, true, kTileHTall>);
     k.tuples_per_block = Shape<T, D>::TPW * kWavesPerBlock;
     return k;
 }
@@ -1468,10 +1546,13 @@ Kernels pick(msda_dtype_t dt, int64_t D) {
     return Kernels();
 }
 
-// grad_value: the bin kernel, then the tile kernel, on the workspace of `pl`.
+// grad_value: the bin kernel, then the tile kernel, on the workspace of `pl`
+// (bins and tiles hold the two tile heights' kernels; the plan picks one).
 msda_status_t launch_grad_value(Params& p, const BwdPlan& pl, const msda_dims_t* dims,
-                                const void* bin, const void* tile, void* workspace,
-                                hipStream_t stream, bool bf16_out = false) {
+                                const void* const* bins, const void* const* tiles,
+                                void* workspace, hipStream_t stream, bool bf16_out = false) {
+    const void* bin = bins[pl.tall];
+    const void* tile = tiles[pl.tall];
     p.nW = (int)pl.nW;
     p.Qc = (int)pl.Qc;
     p.t_stride = (int)pl.t_stride;
@@ -1489,7 +1570,7 @@ msda_status_t launch_grad_value(Params& p, const BwdPlan& pl, const msda_dims_t*
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return MSDA_ERROR_LAUNCH;
-    const int per_cu = tile_blocks_per_cu(dims->D, tile, bf16_out);
+    const int per_cu = tile_blocks_per_cu(dims->D, tile, bf16_out, pl.tall);
     const int64_t items = BM * pl.t_stride;
     const int64_t resident = ((int64_t)per_cu * (cus > 0 ? cus : 1) + 7) / 8 * 8;
     const int64_t grid = items < resident ? ((items + 7) / 8) * 8 : resident;

@@ -137,23 +137,30 @@ def test_many_points_and_levels():
     parity(w)
 
 
+@pytest.mark.parametrize("th", [4, 8])
 @pytest.mark.parametrize("D", [8, 16, 32, 64])
-def test_points_straddling_tile_edges(D):
-    # The value gradient is built per tile of 4 pixel rows x TW columns, with
-    # TW = 256 / (D / 4) - 1 here: put most points on cells whose corners fall
-    # on both sides of a tile edge (and on integer coordinates, and just left
-    # of the level), on levels TW wide, 2 TW + 1 wide and TW - 1 wide.
+def test_points_straddling_tile_edges(D, th):
+    # The value gradient is built per tile of th pixel rows x TW columns, with
+    # TW = 256 / (D / 4) - 1 here; the library takes 8-row tiles when a (b, m)
+    # has fewer points than pixels and 4-row tiles otherwise, so the query
+    # count picks th. Most points go on cells whose corners fall on both sides
+    # of a tile edge (and on integer coordinates, and just left of the level),
+    # on levels TW wide, 2 TW + 1 wide and TW - 1 wide.
     tw = 256 // (D // 4) - 1
     shapes = ((9, tw), (6, 2 * tw + 1), (5, tw - 1))
-    w = wl.Workload(f"tile_edges_D{D}", B=2, M=3, D=D, K=4, shapes=shapes, ref="uniform",
-                    sigma_px=2.0, Nq=61, seed=90 + D)
+    nv = sum(h * w for h, w in shapes)
+    L, K = len(shapes), 4
+    nq = nv // (L * K) - 3 if th == 8 else nv // (L * K) + 9
+    assert (nq * L * K < nv) == (th == 8)
+    w = wl.Workload(f"tile_edges_D{D}_th{th}", B=2, M=3, D=D, K=K, shapes=shapes, ref="uniform",
+                    sigma_px=2.0, Nq=nq, seed=90 + D + th)
     x = wl.generate(w)
-    rng = np.random.default_rng(190 + D)
+    rng = np.random.default_rng(190 + D + th)
     loc = x["sampling_locations"]          # [B, Nq, M, L, K, 2]
     for l, (H, W) in enumerate(shapes):
         n = loc[..., l, :, 0].size
         xcol = tw * rng.integers(0, W // tw + 1, n) - 1 + rng.random(n)
-        yrow = 4 * rng.integers(0, H // 4 + 1, n) - 1 + rng.random(n)
+        yrow = th * rng.integers(0, H // th + 1, n) - 1 + rng.random(n)
         pick = rng.random(n)
         xcol = np.where(pick < 0.15, np.round(xcol), xcol)          # integer coordinates
         xcol = np.where((pick >= 0.15) & (pick < 0.25), -rng.random(n), xcol)  # x in (-1, 0]
@@ -163,6 +170,27 @@ def test_points_straddling_tile_edges(D):
         keep = keep.reshape(u.shape)
         loc[..., l, :, 0] = np.where(keep, loc[..., l, :, 0], u)
         loc[..., l, :, 1] = np.where(keep, loc[..., l, :, 1], v)
+    parity(w, x=x)
+
+
+@pytest.mark.parametrize("D", [8, 32])
+def test_sparse_points_crowded_tall_tiles(D):
+    # Fewer points than pixels (8-row tiles), but nearly all of them within a
+    # few pixels of two spots: a few tiles get thousands of entries, swept in
+    # many chunks, while the rest of the level is empty.
+    shapes = ((96, 120), (48, 60))
+    w = wl.Workload(f"crowded_D{D}", B=2, M=2, D=D, K=4, shapes=shapes, ref="uniform",
+                    sigma_px=1.0, Nq=1500, seed=96 + D)
+    assert w.num_queries * w.L * w.K < w.Nv
+    x = wl.generate(w)
+    rng = np.random.default_rng(196 + D)
+    loc = x["sampling_locations"]
+    spot = rng.integers(0, 2, loc.shape[:-1])
+    centre = np.where(spot == 0, 0.3, 0.71)
+    jitter = rng.normal(0.0, 0.01, loc.shape)
+    crowd = rng.random(loc.shape[:-1]) < 0.9
+    for c in range(2):
+        loc[..., c] = np.where(crowd, (centre + jitter[..., c]).astype(np.float32), loc[..., c])
     parity(w, x=x)
 
 
