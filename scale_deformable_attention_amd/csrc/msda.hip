@@ -188,12 +188,12 @@ struct PointIn {
     float z;      // weight, or the logit
 };
 
+// (q: the tuple's query, t / M mod Nq, where the caller knows it)
 template <int FE>
-__device__ inline PointIn load_point(const Params& p, int t, int j, int l) {
+__device__ inline PointIn load_point_q(const Params& p, int t, int j, int l, int q) {
     PointIn in;
     const size_t pt = (size_t)t * p.LK + j;
     if constexpr (FE == kFeDcn) {
-        const int q = (t / p.M) % p.Nq;
         const int ho = q / p.out_W, wo = q - ho * p.out_W;
         const int ky = j / p.kernel_w, kx = j - ky * p.kernel_w;
         in.uv = make_float2((float)(wo * p.stride_w - p.pad_w + kx * p.dil_w),
@@ -217,6 +217,11 @@ __device__ inline PointIn load_point(const Params& p, int t, int j, int l) {
         in.z = p.attn[pt];
     }
     return in;
+}
+
+template <int FE>
+__device__ inline PointIn load_point(const Params& p, int t, int j, int l) {
+    return load_point_q<FE>(p, t, j, l, FE == kFeDcn ? (t / p.M) % p.Nq : 0);
 }
 
 // Fused front-end: the location is the reference point plus the offset over
@@ -922,9 +927,10 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
             const int t = ok ? (int)it.t : (int)it.tuple0;
             const int j = ok ? it.j : 0;
             const int l = ok ? it.l : 0;
+            const int q = ok ? q_begin + it.qo : q_begin;
             float2 st = make_float2(0.f, 0.f);
             if constexpr (FE == kFeFused) st = want_a ? p.smax[t] : st;
-            finish_point<FE>(load_point<FE>(p, t, j, l),
+            finish_point<FE>(load_point_q<FE>(p, t, j, l, q),
                              make_int4(lt[l].H, lt[l].W, lt[l].start, 0), st.x, st.y, uv, a);
         } else {
             const size_t pt = ok ? it.pt : it.pt0;
