@@ -102,7 +102,9 @@ def test_every_group_width(D, value_dtype):
 @pytest.mark.parametrize("kernel,stride,pad,dilation", [
     ((3, 3), (2, 2), (1, 1), (1, 1)), ((5, 3), (1, 2), (4, 1), (2, 1)),
     ((3, 2), (2, 1), (2, 3), (1, 3)), ((1, 1), (1, 1), (0, 0), (1, 1)),
-    ((7, 7), (1, 1), (3, 3), (1, 1))])
+    ((7, 7), (1, 1), (3, 3), (1, 1)),
+    # fewer points than input pixels: the 8-row grad_value tiles
+    ((1, 1), (2, 2), (0, 0), (1, 1))])
 def test_grid_geometries(kernel, stride, pad, dilation):
     w = wl.DcnWorkload(f"dcn_{kernel}_{stride}_{pad}_{dilation}", B=2, H=13, W=10, G=2, D=16,
                        kernel=kernel, stride=stride, pad=pad, dilation=dilation, sigma_px=1.0,
