@@ -14,8 +14,9 @@
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulation, fed with three-term bf16
 // splits of the fp32 operands (six products per fp32 product, fp32 accuracy;
 // see msda_gemm_kernel). A 16-deep slice of both operands is staged in LDS,
-// split on the way, double buffered; the next slice's global loads are in
-// flight while the current one feeds the matrix cores.
+// split on the way, double buffered; while a slice feeds the matrix cores the
+// next slice's weight-side operand and the A operand two slices ahead are in
+// flight (A streams from HBM; B is mostly small and L2-resident).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -232,15 +233,15 @@ __global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmGroup grp) {
     const bool do_asum = g.asum != nullptr && n0 == 0 && (kAsumStaged || tid < kTile);
     float asum = 0.0f;
 
-    auto fetch = [&](int k0) {
-        if (k0 >= g.K) {
-            load(g.A2, g.lda2, kAK, g.M, m0, k0 - g.K, kend - g.K, ra);
-            load(g.B2, g.ldb2, kBKm, g.N, n0, k0 - g.K, kend - g.K, rb);
-        } else {
-            load(g.A, g.lda, kAK, g.M, m0, k0, min(kend, g.K), ra);
-            load(g.B, g.ldb, kBKm, g.N, n0, k0, min(kend, g.K), rb);
-        }
+    auto fetchA = [&](int k0, float* r) {
+        if (k0 >= g.K) load(g.A2, g.lda2, kAK, g.M, m0, k0 - g.K, kend - g.K, r);
+        else load(g.A, g.lda, kAK, g.M, m0, k0, min(kend, g.K), r);
     };
+    auto fetchB = [&](int k0) {
+        if (k0 >= g.K) load(g.B2, g.ldb2, kBKm, g.N, n0, k0 - g.K, kend - g.K, rb);
+        else load(g.B, g.ldb, kBKm, g.N, n0, k0, min(kend, g.K), rb);
+    };
+    float ra2[kPerThread];   // A two slices ahead
 
     auto asum_staged = [&]() {
         if constexpr (kAsumStaged) {
@@ -252,18 +253,18 @@ __global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmGroup grp) {
     };
     int buf = 0;
     if (kbeg < kend) {
-        fetch(kbeg);
+        fetchA(kbeg, ra);
+        fetchB(kbeg);
         asum_staged();
         store(As[0], kAK, ra);
         store(Bs[0], kBKm, rb);
+        if (kbeg + kSplitBK < kend) fetchA(kbeg + kSplitBK, ra);
     }
     __syncthreads();
     for (int k0 = kbeg; k0 < kend; k0 += kSplitBK) {
         const bool more = k0 + kSplitBK < kend;
-        if (more) {
-            fetch(k0 + kSplitBK);
-            asum_staged();
-        }
+        if (more) fetchB(k0 + kSplitBK);
+        if (k0 + 2 * kSplitBK < kend) fetchA(k0 + 2 * kSplitBK, ra2);
         const __bf16* Ab = As[buf];
         const __bf16* Bb = Bs[buf];
         bf16x8 fa[2][3], fb[2][3];
@@ -300,11 +301,14 @@ __global__ __launch_bounds__(kThreads) void msda_gemm_kernel(GemmGroup grp) {
             }
         }
         if (more) {
+            asum_staged();
             store(As[buf ^ 1], kAK, ra);
             store(Bs[buf ^ 1], kBKm, rb);
         }
         __syncthreads();
         buf ^= 1;
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) ra[i] = ra2[i];
     }
 
     if constexpr (kAsumStaged) {
