@@ -727,7 +727,8 @@ constexpr int kBinRange = 1024;     // tile counters a bin block keeps in LDS at
 constexpr int kBinUnroll = 8;       // points per thread in flight in the bin kernel
 constexpr int kChunk = 1024;        // entries a tile block sorts in LDS at once
 constexpr int kMinQueries = 64;     // queries per bin block at least (when there are enough)
-constexpr int kMaxSlabs = 64;       // bin blocks per (b, m) at most (a power of two)
+constexpr int kMaxSlabs = 256;      // bin blocks per (b, m) at most (a power of two)
+constexpr int kBinSlabs = 64;       // the same unless the points then fit in registers
 constexpr int kUnroll = 8;          // entries in flight per lane group in the sweep
 constexpr int kUnrollTall = 2;      // the same for tall tiles (few entries per cell column)
 
@@ -898,7 +899,9 @@ struct PointWalk {
     }
 };
 
-template <int D, int FE, int TH>
+// kCached: the block has at most kBinUnroll points per thread, loaded once and
+// kept in registers for both passes (otherwise each pass loads them).
+template <int D, int FE, int TH, bool kCached>
 __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
     using TS = TileShape<D, TH>;
     __shared__ LevelTiles lt[MSDA_MAX_LEVELS];
@@ -939,6 +942,70 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
         }
     };
     uint32_t base = 0;
+    if constexpr (kCached) {
+        // the pixel coordinates (x, y) of a point, its level, tuple and weight
+        float px[kBinUnroll], py[kBinUnroll], pa[kBinUnroll];
+        int lvl[kBinUnroll];
+        bool ok[kBinUnroll];
+        uint32_t tup[kBinUnroll];
+        {
+            PointWalk it(p, tid, q_begin, b, m);
+            float2 uv[kBinUnroll];
+#pragma unroll
+            for (int u = 0; u < kBinUnroll; ++u) {
+                ok[u] = it.i < npts;
+                lvl[u] = it.l;
+                tup[u] = (uint32_t)it.t;
+                point_of(it, ok[u], uv[u], pa[u], true);
+                it.next();
+            }
+#pragma unroll
+            for (int u = 0; u < kBinUnroll; ++u) {
+                const LevelTiles& L_ = lt[lvl[u]];
+                px[u] = FE == kFeDcn ? uv[u].x : fmaf(uv[u].x, (float)L_.W, -0.5f);
+                py[u] = FE == kFeDcn ? uv[u].y : fmaf(uv[u].y, (float)L_.H, -0.5f);
+            }
+        }
+        for (int r0 = 0; r0 < T; r0 += kBinRange) {
+            const int rn = min(kBinRange, T - r0);
+            for (int i = tid; i < rn; i += kBlock) cnt[i] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < kBinUnroll; ++u) {
+                int tile[4];
+                bool emit[4];
+                point_tiles<TS::TW, TH, true>(px[u], py[u], lt[lvl[u]], tile, emit);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (ok[u] && emit[c] && tile[c] >= r0 && tile[c] < r0 + rn)
+                        atomicAdd(&cnt[tile[c] - r0], 1u);
+                }
+            }
+            __syncthreads();
+            const uint32_t total = block_exclusive_scan(cnt, off, rn, scratch);
+            for (int i = tid; i < rn; i += kBlock) row[(size_t)(r0 + i) * p.nW] = make_uint2(cnt[i], base + off[i]);
+            __syncthreads();
+            for (int i = tid; i < rn; i += kBlock) cnt[i] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < kBinUnroll; ++u) {
+                int tile[4];
+                bool emit[4];
+                point_tiles<TS::TW, TH, true>(px[u], py[u], lt[lvl[u]], tile, emit);
+                const float4 rec = make_float4(as_float(tup[u]), px[u], py[u], pa[u]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (ok[u] && emit[c] && tile[c] >= r0 && tile[c] < r0 + rn) {
+                        const uint32_t slot = atomicAdd(&cnt[tile[c] - r0], 1u);
+                        slab[base + off[tile[c] - r0] + slot] = rec;
+                    }
+                }
+            }
+            base += total;
+            __syncthreads();
+        }
+        return;
+    }
     // a point index that is always valid (npts > 0 whenever a loop body runs)
     // stands in for the lanes past the end, so that every load is unconditional
     for (int r0 = 0; r0 < T; r0 += kBinRange) {
@@ -1405,6 +1472,7 @@ msda_status_t check_dims(const msda_dims_t* d, msda_dtype_t dt, bool backward) {
 struct BwdPlan {
     int64_t nW = 0, Qc = 0, t_stride = 0, slab_per_block = 0;
     int tall = 0;   // tiles of kTileHTall rows (1) or kTileH rows (0)
+    int cached = 0; // bin blocks of at most kBinUnroll points per thread (1)
     size_t counters_off = 0, table_off = 0, slab_off = 0, bytes = 0;
 };
 
@@ -1414,13 +1482,25 @@ BwdPlan plan_backward(const msda_dims_t* d) {
     BwdPlan pl;
     const int64_t BM = d->B * d->M;
     if (BM == 0) return pl;
-    // about 4096 bin blocks in total, at most kMaxSlabs per (b, m) and at
+    // about 4096 bin blocks in total, at most kBinSlabs per (b, m) and at
     // least kMinQueries queries per block (fewer, fuller slabs when there are
     // few queries: every tile reads one table entry per slab)
     int64_t nW = (4096 + BM - 1) / BM;
-    nW = nW < 1 ? 1 : (nW > kMaxSlabs ? kMaxSlabs : nW);
+    nW = nW < 1 ? 1 : (nW > kBinSlabs ? kBinSlabs : nW);
     const int64_t nW_q = (d->Nq + kMinQueries - 1) / kMinQueries;
     if (nW > nW_q) nW = nW_q < 1 ? 1 : nW_q;
+    // more, smaller bin blocks where that lets every block keep its points
+    // in registers (one load per point instead of one per pass), as long as
+    // the (tile, block) table -- nW rows per tile -- grows at most threefold
+    const int64_t LK = d->L * d->K;
+    const int64_t q_fit = LK > 0 ? (int64_t)(kBinUnroll * kBlock) / LK : 0;
+    if (q_fit >= 1 && d->Nq > 0) {
+        const int64_t nW_fit = (d->Nq + q_fit - 1) / q_fit;
+        if (nW_fit <= kMaxSlabs && nW_fit <= 3 * nW) {
+            if (nW_fit > nW) nW = nW_fit;
+            pl.cached = 1;
+        }
+    }
     const int64_t Qc = d->Nq > 0 ? (d->Nq + nW - 1) / nW : 0;
     pl.nW = Qc > 0 ? (d->Nq + Qc - 1) / Qc : 1;
     pl.Qc = Qc;
@@ -1495,18 +1575,19 @@ msda_status_t launch(const void* kernel, int64_t blocks, Params& p, hipStream_t 
 struct Kernels {
     const void* fwd = nullptr;
     const void* point = nullptr;
-    // bin and tile kernels: [0] tiles of kTileH rows, [1] of kTileHTall rows
-    const void* bin[2] = {};
+    // bin kernels: [tall + 2 * cached]; tile kernels: [tall] (tall: tiles of
+    // kTileHTall rows, else kTileH; cached: points kept in registers)
+    const void* bin[4] = {};
     const void* tile[2] = {};
     const void* fwd_fused = nullptr;
     const void* point_fused = nullptr;
-    const void* bin_fused[2] = {};
+    const void* bin_fused[4] = {};
     const void* fwd_dcn = nullptr;
     const void* point_dcn = nullptr;
-    const void* bin_dcn[2] = {};
+    const void* bin_dcn[4] = {};
     const void* fwd_half = nullptr;     // binary16 locations and weights
     const void* point_half = nullptr;
-    const void* bin_half[2] = {};
+    const void* bin_half[4] = {};
     const void* tile_bf16[2] = {};      // grad_value stored as bf16
     int tuples_per_block = 0;
 };
@@ -1516,20 +1597,28 @@ Kernels kernels_for() {
     Kernels k;
     k.fwd = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D, kFeCore>);
     k.point = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D, kFeCore>);
-    k.bin[0] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCore, kTileH>);
-    k.bin[1] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCore, kTileHTall>);
+    k.bin[0] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCore, kTileH, false>);
+    k.bin[1] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCore, kTileHTall, false>);
+    k.bin[2] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCore, kTileH, true>);
+    k.bin[3] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCore, kTileHTall, true>);
     k.fwd_fused = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D, kFeFused>);
     k.point_fused = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D, kFeFused>);
-    k.bin_fused[0] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeFused, kTileH>);
-    k.bin_fused[1] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeFused, kTileHTall>);
+    k.bin_fused[0] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeFused, kTileH, false>);
+    k.bin_fused[1] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeFused, kTileHTall, false>);
+    k.bin_fused[2] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeFused, kTileH, true>);
+    k.bin_fused[3] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeFused, kTileHTall, true>);
     k.fwd_dcn = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D, kFeDcn>);
     k.point_dcn = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D, kFeDcn>);
-    k.bin_dcn[0] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeDcn, kTileH>);
-    k.bin_dcn[1] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeDcn, kTileHTall>);
+    k.bin_dcn[0] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeDcn, kTileH, false>);
+    k.bin_dcn[1] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeDcn, kTileHTall, false>);
+    k.bin_dcn[2] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeDcn, kTileH, true>);
+    k.bin_dcn[3] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeDcn, kTileHTall, true>);
     k.fwd_half = reinterpret_cast<const void*>(&msda_fwd_kernel<T, D, kFeCoreHalf>);
     k.point_half = reinterpret_cast<const void*>(&msda_bwd_point_kernel<T, D, kFeCoreHalf>);
-    k.bin_half[0] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCoreHalf, kTileH>);
-    k.bin_half[1] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCoreHalf, kTileHTall>);
+    k.bin_half[0] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCoreHalf, kTileH, false>);
+    k.bin_half[1] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCoreHalf, kTileHTall, false>);
+    k.bin_half[2] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCoreHalf, kTileH, true>);
+    k.bin_half[3] = reinterpret_cast<const void*>(&msda_bin_kernel<D, kFeCoreHalf, kTileHTall, true>);
     k.tile[0] = reinterpret_cast<const void*>(&msda_tile_kernel<D, false, kTileH>);
     k.tile[1] = reinterpret_cast<const void*>(&msda_tile_kernel<D, false, kTileHTall>);
     k.tile_bf16[0] = reinterpret_cast<const void*>(&msda_tile_kernel<D, true, kTileH>);
@@ -1553,11 +1642,11 @@ Kernels pick(msda_dtype_t dt, int64_t D) {
 }
 
 // grad_value: the bin kernel, then the tile kernel, on the workspace of `pl`
-// (bins and tiles hold the two tile heights' kernels; the plan picks one).
+// (bins and tiles hold the variants indexed as in Kernels; the plan picks).
 msda_status_t launch_grad_value(Params& p, const BwdPlan& pl, const msda_dims_t* dims,
                                 const void* const* bins, const void* const* tiles,
                                 void* workspace, hipStream_t stream, bool bf16_out = false) {
-    const void* bin = bins[pl.tall];
+    const void* bin = bins[pl.tall + 2 * pl.cached];
     const void* tile = tiles[pl.tall];
     p.nW = (int)pl.nW;
     p.Qc = (int)pl.Qc;
