@@ -529,12 +529,14 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
 //     forms the four partial dot products g . v_c, reduces them across the
 //     group with DPP, and the point's lane keeps them and finishes the point.
 //  2. msda_bin_kernel: sorts the points into buckets by the grad_value tiles
-//     (TH x TW pixels of one (b, m, level)) their inside-the-level corners land
-//     in. A block owns a range of queries of one (b, m); it counts per tile with
+//     (TH x TW pixels of one (b, m, level); TH = 4, or 8 where a (b, m) has
+//     fewer points than pixels) their inside-the-level corners land in. A
+//     block owns a range of queries of one (b, m); it counts per tile with
 //     LDS integer atomics (fast), scans, writes its per-tile (count, offset)
 //     row to the workspace and one 16-byte entry per (point, tile) -- tuple,
-//     pixel coordinates, weight -- to its own slab. No global atomics: every
-//     block writes only its own rows.
+//     pixel coordinates, weight -- to its own slab (a block of at most
+//     kBinUnroll points per thread loads them once, for both passes). No
+//     global atomics: every block writes only its own rows.
 //  3. msda_tile_kernel: persistent blocks fetch tiles from a counter per XCD
 //     group. A block collects its tile's entries from every slab of the tile's
 //     (b, m), sorts them by cell (counting sort in LDS, into records holding
@@ -1088,9 +1090,9 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
 // first: those tiles have the most points per pixel and the longest lists, and
 // start first. A block takes the tile's entries kChunk at a time: loads them,
 // counting-sorts them by cell into LDS records that already hold the four
-// corner weights, then sweeps the cells column by column.
+// corner weights, then sweeps the cells column by column. (Tall tiles: at
+// most 128 VGPRs, so that 4 blocks fit per CU.)
 template <int D, bool kBf16Out, int TH>
-// (tall tiles: at most 128 VGPRs, so that 4 blocks fit per CU)
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(TH == kTileHTall ? 4 : 1)))
 void msda_tile_kernel(Params p) {
     using TS = TileShape<D, TH>;
@@ -1646,6 +1648,9 @@ Kernels pick(msda_dtype_t dt, int64_t D) {
 msda_status_t launch_grad_value(Params& p, const BwdPlan& pl, const msda_dims_t* dims,
                                 const void* const* bins, const void* const* tiles,
                                 void* workspace, hipStream_t stream, bool bf16_out = false) {
+    // the register-cached bin kernel holds kBinUnroll points per thread
+    if (pl.cached && pl.Qc * dims->L * dims->K > (int64_t)kBinUnroll * kBlock)
+        return MSDA_ERROR_LAUNCH;
     const void* bin = bins[pl.tall + 2 * pl.cached];
     const void* tile = tiles[pl.tall];
     p.nW = (int)pl.nW;
