@@ -251,7 +251,7 @@ msda_status_t msda_backward_fused_workspace_size(const msda_dims_t *dims,
  * matrix cores (fp32 products, fp32 accumulation). MSDeformAttn wraps the
  * core in four of them: the value projection on the flattened input, the
  * sampling-offset and attention-weight heads on the query, and the output
- * projection (deformable-attention practice guide, section 3.1;
+ * projection (deformable-attention tutorial (discosf.com), section 3.1;
  * DETR-to-Deformable-DETR article, section 3.2).
  *
  *   x       [rows, in_features]
@@ -290,7 +290,7 @@ msda_status_t msda_linear_backward_workspace_size(int64_t rows, int64_t in_featu
 
 /*
  * The whole MSDeformAttn layer around the fused core (deformable-attention
- * practice guide, section 3.1: value_proj, sampling_offsets,
+ * tutorial (discosf.com), section 3.1: value_proj, sampling_offsets,
  * attention_weights and output_proj; DETR-to-Deformable-DETR article,
  * section 3.2), fp32 throughout, C = M * D channels:
  *
@@ -358,7 +358,7 @@ msda_status_t msda_layer_workspace_size(const msda_dims_t *dims, size_t *bytes);
 
 /*
  * Grouped single-level deformable aggregation (DCNv3; deformable-attention
- * practice guide, section 4.2): for every output pixel p0 = (ho, wo), group g
+ * tutorial (discosf.com), section 4.2): for every output pixel p0 = (ho, wo), group g
  * and kernel point k = ky * kernel_w + kx,
  *
  *   output[b, ho, wo, g, :] = sum_k mask[b, ho, wo, g, k] *

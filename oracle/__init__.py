@@ -24,15 +24,33 @@ _pi = ctypes.POINTER(ctypes.c_int64)
 
 
 def library(path=None):
-    """Load (building first if absent) the oracle shared library."""
+    """Load the oracle shared library, building it first when it is absent or
+    older than its source (the build leaves a digest of the source next to the
+    library)."""
     global _LIB
     if path is not None:
         return _bind(ctypes.CDLL(path))
     if _LIB is None:
-        if not os.path.exists(_build.LIBRARY):
+        if not _build.is_current():
             _build.build()
         _LIB = _bind(ctypes.CDLL(_build.LIBRARY))
+        # the library must report the version the source declares
+        want = source_version()
+        got = _LIB.msda_oracle_version()
+        if got != want:
+            raise RuntimeError(f"oracle library reports version {got}, its source {want}: "
+                               "stale build")
     return _LIB
+
+
+def source_version():
+    """The version number msda_oracle.c declares (msda_oracle_version)."""
+    import re
+    with open(_build.SOURCE) as f:
+        m = re.search(r"int msda_oracle_version\(void\) \{ return (\d+); \}", f.read())
+    if not m:
+        raise RuntimeError("msda_oracle_version not found in the oracle source")
+    return int(m.group(1))
 
 
 def _bind(lib):

@@ -3,7 +3,7 @@ infrastructure: only the tests, the smoke check and the benchmark's CPU
 baseline may import it; the product path never does).
 
 The layer is MSDeformAttn as the pages build it (deformable-attention
-practice guide, section 3.1, the module with sampling_offsets,
+tutorial (discosf.com), section 3.1, the module with sampling_offsets,
 attention_weights, value_proj and output_proj linear layers;
 DETR-to-Deformable-DETR article, section 3.2, the forward that views the
 offsets as [B, Nq, M, L, K, 2], takes the softmax of the weights over L*K and

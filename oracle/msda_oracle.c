@@ -393,10 +393,9 @@ int msda_oracle_backward_fused(int64_t B, int64_t Nv, int64_t M, int64_t D, int6
     return rc;
 }
 
-/* Version tag so a test can tell a stale build from the current source. */
 /*
  * Grouped single-level deformable aggregation (DCNv3, deformable-attention
- * practice guide section 4.2):
+ * tutorial (discosf.com) section 4.2):
  *
  *   y(p0) = sum_g sum_k w_g m_gk x_g(p0 + p_k + dp_gk)
  *
@@ -537,4 +536,6 @@ int msda_oracle_dcn_backward(int64_t B, int64_t H, int64_t W, int64_t G, int64_t
     return ORACLE_OK;
 }
 
+/* Version tag: the loader compares it with this line of the source, so a
+ * stale build cannot pass for the current one. */
 int msda_oracle_version(void) { return 3; }

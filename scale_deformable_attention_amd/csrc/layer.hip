@@ -1,5 +1,5 @@
 // layer.hip -- the whole MSDeformAttn layer: the four projections around the
-// fused core (deformable-attention practice guide, section 3.1: value_proj,
+// fused core (deformable-attention tutorial (discosf.com), section 3.1: value_proj,
 // sampling_offsets, attention_weights and output_proj linear layers;
 // DETR-to-Deformable-DETR article, section 3.2: offsets viewed per head,
 // level and point, the weights' softmax over L*K, offset / (W, H) added to the

@@ -2,7 +2,7 @@
 // attention core on the gfx950 matrix cores: y = x W^T + b and its gradients
 // (torch nn.Linear semantics). In MSDeformAttn four of them surround the core:
 // the value projection, the sampling-offset and attention-weight heads on the
-// query, and the output projection (deformable-attention practice guide,
+// query, and the output projection (deformable-attention tutorial (discosf.com),
 // section 3.1; DETR-to-Deformable-DETR article, section 3.2).
 //
 // One kernel serves the three products a linear layer needs:

@@ -1696,14 +1696,6 @@ FusedPlan plan_backward_fused(const msda_dims_t* d) {
     return f;
 }
 
-}  // namespace
-
-extern "C" {
-
-}  // extern "C"
-
-namespace {
-
 msda_status_t check_precision(const msda_precision_t* pr) {
     if (!pr) return MSDA_ERROR_INVALID_VALUE;
     if (pr->value != MSDA_DTYPE_F32 && pr->value != MSDA_DTYPE_BF16 && pr->value != MSDA_DTYPE_F16)

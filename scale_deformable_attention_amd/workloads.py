@@ -302,7 +302,7 @@ class DcnWorkload:
 
 # InternImage-style stages on the 800x1333 detection input: 16 channels per
 # group at every stage (64 channels in 4 groups at stride 4, 128 in 8 at
-# stride 8), 3x3 grids (deformable-attention practice guide, sections 4.2 and
+# stride 8), 3x3 grids (deformable-attention tutorial (discosf.com), sections 4.2 and
 # 5.2: G between 4 and 16, G=8 with K=9 as the typical pairing).
 DCN_WORKLOADS = {
     "dcn_tiny": DcnWorkload("dcn_tiny", B=1, H=6, W=7, G=2, D=8, sigma_px=1.0, seed=2001,

@@ -439,6 +439,116 @@ def pin_permutation(lib=None):
     assert np.array_equal(fwd(lib, value[pb], shapes, lsi, loc[pb], attn[pb]), o[pb])
 
 
+# ----------------------------------------------------------------------------- term sums S
+# Every GPU parity gate is |gpu - r| <= rho |r| + 1e-5 S, where S is the sum of
+# the absolute values of the terms the oracle adds up for that element. These
+# pins fix S without reading the oracle's own S code: where every term of an
+# element is non-negative (the bilinear weights are), S is that element's
+# result on inputs replaced by their absolute values; the location terms
+# carry signed weight derivatives, so their S is summed from the dense tent
+# form; and |r| <= S everywhere.
+
+def _le_abs_sum(r, s, what):
+    r, s = np.asarray(r, np.float64), np.asarray(s, np.float64)
+    assert np.all(np.isfinite(s)), f"{what}: non-finite term sum"
+    assert np.all(np.abs(r) <= s * (1.0 + 1e-12) + 1e-300), f"{what}: |result| exceeds its term sum"
+
+
+def _tent_abs_location(value, shapes, lsi, loc, attn, g):
+    """S of the location gradients from the dense tent form: level pixel n of
+    the sample enters with the derivative of its tent weight, so
+    S_x = W |A| sum_d |g_d| sum_n |d tent_n / dx| |v_n,d| (and the same in y
+    with H). Valid away from integer coordinates."""
+    B, Nv, M, D = value.shape
+    out = np.zeros(loc.shape)
+    for l in range(loc.shape[3]):
+        H, W = shapes[l]
+        yy, xx = np.meshgrid(np.arange(H), np.arange(W), indexing="ij")
+        xn, yn = xx.reshape(-1).astype(np.float64), yy.reshape(-1).astype(np.float64)
+        vl = np.abs(value[:, lsi[l]:lsi[l] + H * W])
+        x = coord32(loc[..., l, :, 0], W).astype(np.float64)[..., None]
+        y = coord32(loc[..., l, :, 1], H).astype(np.float64)[..., None]
+        tx = np.maximum(0.0, 1.0 - np.abs(x - xn))
+        ty = np.maximum(0.0, 1.0 - np.abs(y - yn))
+        near_x = (np.abs(x - xn) < 1.0).astype(np.float64)
+        near_y = (np.abs(y - yn) < 1.0).astype(np.float64)
+        gv = np.einsum("bqmd,bnmd->bqmn", np.abs(g), vl)[:, :, :, None, :]
+        a = np.abs(attn[..., l, :])
+        out[..., l, :, 0] = W * a * (near_x * ty * gv).sum(-1)
+        out[..., l, :, 1] = H * a * (tx * near_y * gv).sum(-1)
+    return out
+
+
+def pin_abs_sums_core(lib=None):
+    """Term sums of the core forward and backward: forward S = forward of
+    |value| with |A|; grad_value S = grad_value with |A| and |g|; weight
+    gradient S = weight gradient of |value| and |g|; location gradient S from
+    the tent form; |result| <= S."""
+    for seed in (24, 25):
+        rng = np.random.default_rng(seed)
+        value, shapes, lsi, loc, attn, g = random_case(rng, lo=-0.3, hi=1.3)
+        o, oa = oracle.forward(value, shapes, lsi, loc, attn, with_abs=True, lib=lib)
+        gv, gl, ga, gva, gla, gaa = oracle.backward(value, shapes, lsi, loc, attn, g,
+                                                    with_abs=True, lib=lib)
+        av, aa, ag = np.abs(value), np.abs(attn), np.abs(g)
+        _close(oa, fwd(lib, av, shapes, lsi, loc, aa), 1e-13, "forward S = forward(|value|, |A|)")
+        gv_pos, _, ga_pos = bwd(lib, av, shapes, lsi, loc, aa, ag)
+        gv_a, _, _ = bwd(lib, value, shapes, lsi, loc, aa, ag)
+        _close(gva, gv_a, 1e-13, "grad_value S = grad_value(|A|, |g|)")
+        _close(gaa, ga_pos, 1e-13, "weight-gradient S = weight gradient(|value|, |g|)")
+        _close(gla, _tent_abs_location(value, shapes, lsi, loc, attn, g), 1e-12,
+               "location-gradient S vs tent form")
+        for r, s, what in ((o, oa, "output"), (gv, gva, "grad_value"), (gl, gla, "grad_loc"),
+                           (ga, gaa, "grad_attn")):
+            _le_abs_sum(r, s, what)
+        # non-negative inputs: every term of the output is non-negative
+        _close(fwd(lib, av, shapes, lsi, loc, aa), oa, 1e-13, "S equals r for non-negative terms")
+
+
+def _fused_locations(shapes, ref, off):
+    """Single-precision locations of the fused front-end (quotient, then sum,
+    each rounded to float) and the matching (W, H) per level."""
+    L = ref.shape[2]
+    loc = np.empty(off.shape, np.float32)
+    for l in range(L):
+        H, W = shapes[l]
+        q = (off[:, :, :, l] / np.array([W, H], np.float32)).astype(np.float32)
+        loc[:, :, :, l] = (ref[:, :, None, l, None, :] + q).astype(np.float32)
+    return loc
+
+
+def pin_abs_sums_fused(lib=None):
+    """Term sums of the fused front-end, from the core's (pinned above): the
+    value-gradient S is the core's at the fused locations and softmax weights;
+    the offset S is the core location S over (W, H); the reference-point S is
+    its sum over heads and points; the logit S is A_j (S_gA_j + sum_i A_i
+    S_gA_i), the two terms of the softmax Jacobian; |result| <= S."""
+    rng = np.random.default_rng(35)
+    value, shapes, lsi, ref, off, logits, g = random_fused_case(rng)
+    B, Nq, M, L, K, _ = off.shape
+    o, oa = oracle.forward_fused(value, shapes, lsi, ref, off, logits, with_abs=True, lib=lib)
+    outs = oracle.backward_fused(value, shapes, lsi, ref, off, logits, g, with_abs=True, lib=lib)
+    gv, gr, go, gz, gva, gra, goa, gza = outs
+    z = logits.astype(np.float64)
+    e = np.exp(z - z.max(-1, keepdims=True))
+    A = (e / e.sum(-1, keepdims=True)).reshape(B, Nq, M, L, K)
+    loc = _fused_locations(shapes, ref, off)
+    _, coa = oracle.forward(value, shapes, lsi, loc, A, with_abs=True, lib=lib)
+    _, _, _, cgva, cgla, cgaa = oracle.backward(value, shapes, lsi, loc, A, g, with_abs=True,
+                                                lib=lib)
+    _close(oa, coa, 1e-12, "fused forward S")
+    _close(gva, cgva, 1e-12, "fused grad_value S")
+    wh = np.array([[shapes[l][1], shapes[l][0]] for l in range(L)], np.float64)
+    _close(goa, cgla / wh[None, None, None, :, None, :], 1e-12, "offset-gradient S")
+    _close(gra, cgla.sum(axis=(2, 4)), 1e-12, "reference-point-gradient S")
+    ga_s = cgaa.reshape(B, Nq, M, L * K)
+    a = A.reshape(B, Nq, M, L * K)
+    _close(gza, a * (ga_s + (a * ga_s).sum(-1, keepdims=True)), 1e-12, "logit-gradient S")
+    for r, s, what in ((o, oa, "fused output"), (gv, gva, "fused grad_value"),
+                       (gr, gra, "grad_ref"), (go, goa, "grad_off"), (gz, gza, "grad_logits")):
+        _le_abs_sum(r, s, what)
+
+
 # ----------------------------------------------------------------------------- fused front-end
 # Pinned conventions (cf-1.com section 3.2): location = reference point +
 # offset / (W_l, H_l) with offsets in level pixels and the normalizer stacked
@@ -607,7 +717,8 @@ def pin_fused_finite_differences(lib=None):
 ALL_PINS = [pin_golden_hand_worked, pin_pixel_centres, pin_constant_field, pin_bilinear_field,
             pin_out_of_bounds, pin_linearity, pin_grid_sample, pin_brute_force,
             pin_finite_differences, pin_single_scale_resampling, pin_scatter_conservation,
-            pin_permutation, pin_fused_torch, pin_fused_pixel_shift, pin_fused_finite_differences]
+            pin_permutation, pin_fused_torch, pin_fused_pixel_shift, pin_fused_finite_differences,
+            pin_abs_sums_core, pin_abs_sums_fused]
 
 
 # ----------------------------------------------------------------------------- DCNv3 aggregation
@@ -685,41 +796,76 @@ def pin_dcn_integer_shift(lib=None):
         _close(got[0][inside], want[0][inside], 1e-12, f"dcn integer shift ({dx}, {dy})")
 
 
-def pin_dcn_matches_core(lib=None):
-    """On power-of-two sizes with dyadic offsets the pixel point P maps to the
-    normalized location (P + 0.5) / (W, H) exactly, so the aggregation equals
-    the core on one level (heads = groups, weights = mask), and its gradients
-    equal the core's: grad_offset = grad_loc / (W, H), grad_mask = grad_attn."""
-    rng = np.random.default_rng(53)
+def _dcn_as_core(rng, B=2):
+    """A DCNv3 problem on a power-of-two input with dyadic offsets, and the same
+    problem as a core problem: the pixel point P maps to the normalized
+    location (P + 0.5) / (W, H) exactly (heads = groups, one level, weights =
+    mask)."""
     H, W, G, D = 8, 16, 2, 3
     kernel, stride, pad, dil = (3, 3), (1, 2), (1, 1), (2, 1)
     Ho, Wo = _dcn_out_size(H, W, kernel, stride, pad, dil)
     K = 9
-    x = rng.standard_normal((2, H, W, G, D))
-    off = (rng.integers(-48, 49, size=(2, Ho, Wo, G, K, 2)) / 16.0).astype(np.float32)
-    mask = rng.standard_normal((2, Ho, Wo, G, K))
-    g = rng.standard_normal((2, Ho, Wo, G, D))
+    x = rng.standard_normal((B, H, W, G, D))
+    off = (rng.integers(-48, 49, size=(B, Ho, Wo, G, K, 2)) / 16.0).astype(np.float32)
+    mask = rng.standard_normal((B, Ho, Wo, G, K))
+    g = rng.standard_normal((B, Ho, Wo, G, D))
     ky, kx = np.divmod(np.arange(K), kernel[1])
     ho = np.arange(Ho)[None, :, None, None, None]
     wo = np.arange(Wo)[None, None, :, None, None]
     kx, ky = kx[None, None, None, None, :], ky[None, None, None, None, :]
     Px = (wo * stride[1] - pad[1] + kx * dil[1]) + off[..., 0].astype(np.float64)
     Py = (ho * stride[0] - pad[0] + ky * dil[0]) + off[..., 1].astype(np.float64)
-    loc = np.stack([(Px + 0.5) / W, (Py + 0.5) / H], -1)                # [2,Ho,Wo,G,K,2]
-    loc = loc.reshape(2, Ho * Wo, G, 1, K, 2).astype(np.float32)
+    loc = np.stack([(Px + 0.5) / W, (Py + 0.5) / H], -1)                # [B,Ho,Wo,G,K,2]
+    loc = loc.reshape(B, Ho * Wo, G, 1, K, 2).astype(np.float32)
     shapes, lsi = level_tables([(H, W)])
-    value = x.reshape(2, H * W, G, D)
-    attn = mask.reshape(2, Ho * Wo, G, 1, K)
-    want = oracle.forward(value, shapes, lsi, loc, attn, lib=lib)
-    got = oracle.dcn_forward(x, off, mask, kernel, stride, pad, dil, lib=lib)
+    core = dict(value=x.reshape(B, H * W, G, D), shapes=shapes, lsi=lsi, loc=loc,
+                attn=mask.reshape(B, Ho * Wo, G, 1, K), g=g.reshape(B, Ho * Wo, G, D))
+    dcn = dict(x=x, off=off, mask=mask, g=g, kernel=kernel, stride=stride, pad=pad, dil=dil)
+    return dcn, core, (W, H)
+
+
+def pin_dcn_matches_core(lib=None):
+    """On power-of-two sizes with dyadic offsets the pixel point P maps to the
+    normalized location (P + 0.5) / (W, H) exactly, so the aggregation equals
+    the core on one level (heads = groups, weights = mask), and its gradients
+    equal the core's: grad_offset = grad_loc / (W, H), grad_mask = grad_attn."""
+    dc, c, (W, H) = _dcn_as_core(np.random.default_rng(53))
+    geo = (dc["kernel"], dc["stride"], dc["pad"], dc["dil"])
+    want = oracle.forward(c["value"], c["shapes"], c["lsi"], c["loc"], c["attn"], lib=lib)
+    got = oracle.dcn_forward(dc["x"], dc["off"], dc["mask"], *geo, lib=lib)
     _close(got.reshape(want.shape), want, 1e-12, "dcn forward vs core")
-    rgv, rgl, rga = oracle.backward(value, shapes, lsi, loc, attn, g.reshape(2, Ho * Wo, G, D),
-                                    lib=lib)
-    gi, go, gm = oracle.dcn_backward(x, off, mask, g, kernel, stride, pad, dil, lib=lib)
+    rgv, rgl, rga = oracle.backward(c["value"], c["shapes"], c["lsi"], c["loc"], c["attn"],
+                                    c["g"], lib=lib)
+    gi, go, gm = oracle.dcn_backward(dc["x"], dc["off"], dc["mask"], dc["g"], *geo, lib=lib)
     _close(gi.reshape(rgv.shape), rgv, 1e-12, "dcn grad_input vs core grad_value")
     _close(gm.reshape(rga.shape), rga, 1e-12, "dcn grad_mask vs core grad_attn")
     _close(go.reshape(rgl.shape), rgl / np.array([W, H], np.float64), 1e-12,
            "dcn grad_offset vs core grad_loc / (W, H)")
+
+
+def pin_abs_sums_dcn(lib=None):
+    """Term sums of the DCNv3 aggregation: forward S = aggregation of |input|
+    with |mask|; grad_input S = grad_input with |mask| and |g|; grad_mask S =
+    grad_mask of |input| and |g|; offset S = the core's location S (pinned by
+    the tent form) over (W, H) on the exact mapping above; |result| <= S."""
+    dc, c, (W, H) = _dcn_as_core(np.random.default_rng(55))
+    geo = (dc["kernel"], dc["stride"], dc["pad"], dc["dil"])
+    x, off, mask, g = dc["x"], dc["off"], dc["mask"], dc["g"]
+    o, oa = oracle.dcn_forward(x, off, mask, *geo, with_abs=True, lib=lib)
+    gi, go, gm, gia, goa, gma = oracle.dcn_backward(x, off, mask, g, *geo, with_abs=True, lib=lib)
+    _close(oa, oracle.dcn_forward(np.abs(x), off, np.abs(mask), *geo, lib=lib), 1e-13,
+           "dcn forward S = forward(|input|, |mask|)")
+    gi_a, _, _ = oracle.dcn_backward(x, off, np.abs(mask), np.abs(g), *geo, lib=lib)
+    _close(gia, gi_a, 1e-13, "dcn grad_input S = grad_input(|mask|, |g|)")
+    _, _, gm_a = oracle.dcn_backward(np.abs(x), off, mask, np.abs(g), *geo, lib=lib)
+    _close(gma, gm_a, 1e-13, "dcn grad_mask S = grad_mask(|input|, |g|)")
+    _, _, _, _, cgla, _ = oracle.backward(c["value"], c["shapes"], c["lsi"], c["loc"], c["attn"],
+                                          c["g"], with_abs=True, lib=lib)
+    _close(goa.reshape(cgla.shape), cgla / np.array([W, H], np.float64), 1e-12,
+           "dcn offset S = core location S / (W, H)")
+    for r, s, what in ((o, oa, "dcn output"), (gi, gia, "grad_input"), (go, goa, "grad_offset"),
+                       (gm, gma, "grad_mask")):
+        _le_abs_sum(r, s, what)
 
 
 def pin_dcn_finite_differences(lib=None):
@@ -762,4 +908,4 @@ def pin_dcn_finite_differences(lib=None):
 
 
 ALL_PINS += [pin_dcn_depthwise_conv, pin_dcn_integer_shift, pin_dcn_matches_core,
-             pin_dcn_finite_differences]
+             pin_dcn_finite_differences, pin_abs_sums_dcn]

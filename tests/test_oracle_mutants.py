@@ -60,6 +60,30 @@ MUTANTS = {
     "dcn_offset_grad_without_mask": ("grad_offset[2 * p] = m * gx;", "grad_offset[2 * p] = gx;"),
     "dcn_input_grad_wrong_group": ("const size_t base = (size_t)(((b * Nv + c[i].row) * G + g) * D);\n                            for (int64_t d = 0; d < D; ++d) {\n                                const double v = input[base + d];",
                                    "const size_t base = (size_t)(((b * Nv + c[i].row) * G + (G - 1 - g)) * D);\n                            for (int64_t d = 0; d < D; ++d) {\n                                const double v = input[base + d];"),
+    # term sums S (they scale every GPU parity tolerance)
+    "forward_abs_inflated": ("if (oa) oa[d] += fabs(t);", "if (oa) oa[d] += 1e6 * fabs(t);"),
+    "value_grad_abs_doubled": ("if (grad_value_abs) grad_value_abs[base + d] += fabs(t);",
+                               "if (grad_value_abs) grad_value_abs[base + d] += 2.0 * fabs(t);"),
+    "attn_grad_abs_drops_g": ("ga_abs += fabs(g[d]) * s_abs;", "ga_abs += s_abs;"),
+    "loc_grad_abs_drops_W": ("grad_loc_abs[2 * p] = fabs(a) * gx_abs * (double)W;",
+                             "grad_loc_abs[2 * p] = fabs(a) * gx_abs;"),
+    "loc_grad_abs_drops_A": ("grad_loc_abs[2 * p + 1] = fabs(a) * gy_abs * (double)H;",
+                             "grad_loc_abs[2 * p + 1] = gy_abs * (double)H;"),
+    "loc_grad_abs_signed_terms": ("dsx_abs += fabs(c[i].dw_dx * vd);", "dsx_abs += c[i].dw_dx * vd;"),
+    "fused_logit_abs_drops_a": ("if (grad_logits_abs) grad_logits_abs[p] = a * (ga_abs[p] + s_abs);",
+                                "if (grad_logits_abs) grad_logits_abs[p] = (ga_abs[p] + s_abs);"),
+    "fused_logit_abs_no_sum": ("if (grad_logits_abs) grad_logits_abs[p] = a * (ga_abs[p] + s_abs);",
+                               "if (grad_logits_abs) grad_logits_abs[p] = a * ga_abs[p];"),
+    "fused_offset_abs_times_W": ("grad_off_abs[2 * p] = gloc_abs[2 * p] / (double)W;",
+                                 "grad_off_abs[2 * p] = gloc_abs[2 * p] * (double)W;"),
+    "fused_ref_abs_one_head": ("grad_ref_abs[r] += gloc_abs[2 * p];",
+                               "grad_ref_abs[r] += m == 0 ? gloc_abs[2 * p] : 0.0;"),
+    "dcn_forward_abs_inflated": ("if (oa) oa[d] += fabs(term);", "if (oa) oa[d] += 1e6 * fabs(term);"),
+    "dcn_input_abs_doubled": ("if (grad_input_abs) grad_input_abs[base + d] += fabs(term);",
+                              "if (grad_input_abs) grad_input_abs[base + d] += 2.0 * fabs(term);"),
+    "dcn_mask_abs_drops_g": ("gm_abs += fabs(gr[d] * c[i].w * v);", "gm_abs += fabs(c[i].w * v);"),
+    "dcn_offset_abs_without_mask": ("grad_offset_abs[2 * p] = fabs(m) * gx_abs;",
+                                    "grad_offset_abs[2 * p] = gx_abs;"),
 }
 
 CHILD = r"""
