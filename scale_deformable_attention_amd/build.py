@@ -1,7 +1,10 @@
-"""Build the HIP library (gfx950) in-tree: scale_deformable_attention_amd/libmsda.so."""
+"""Build the HIP library (gfx950) in-tree: scale_deformable_attention_amd/libmsda.so.
+
+Each source is compiled to an object on its own (in parallel), then linked."""
 import os
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -13,8 +16,10 @@ ARCH = "gfx950"
 
 # -packed-fp32-ops off: hipcc would otherwise pair fp32 adds/muls/fmas into
 # packed instructions by itself.
-HIPCC_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+HIPCC_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
                "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# the host pass does not know the packed-fp32 feature and says so: harmless
+_NOISE = "is not a recognized feature for this target"
 
 
 def hipcc():
@@ -23,21 +28,45 @@ def hipcc():
     return path if os.path.exists(path) else "hipcc"
 
 
+def _messages(r):
+    return [l for l in (r.stdout + r.stderr).splitlines() if _NOISE not in l]
+
+
 def build(output=LIBRARY, extra_flags=(), verbose=False):
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, *SOURCES, "-o", output + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    # the host pass does not know the packed-fp32 feature and says so: harmless
-    noise = "is not a recognized feature for this target"
-    msgs = [l for l in (r.stdout + r.stderr).splitlines() if noise not in l]
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if verbose and msgs:
-        print("\n".join(msgs))
+    with tempfile.TemporaryDirectory(prefix="msda_build_") as tmp:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmp, os.path.basename(src) + ".o")
+            cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-c", src, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                          text=True))
+            objs.append(obj)
+        failed = []
+        for src, pr in zip(SOURCES, procs):
+            out, err = pr.communicate()
+            r = subprocess.CompletedProcess(pr.args, pr.returncode, out, err)
+            msgs = _messages(r)
+            if pr.returncode != 0:
+                failed.append(f"{os.path.basename(src)}:\n" + "\n".join(msgs))
+            elif verbose and msgs:
+                print("\n".join(msgs))
+        if failed:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
+        cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", output + ".tmp"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + "\n".join(_messages(r)))
     os.replace(output + ".tmp", output)
     return output
 
 
 if __name__ == "__main__":
-    build(extra_flags=sys.argv[1:], verbose=True)
+    args = sys.argv[1:]
+    out = LIBRARY
+    if len(args) >= 2 and args[0] == "--output":
+        out, args = args[1], args[2:]
+    build(output=out, extra_flags=args, verbose=True)
