@@ -39,9 +39,10 @@
  *
  * Ownership: every tensor pointer is a DEVICE pointer owned by the caller; a
  * pointer to a tensor with no elements may be NULL. Scratch memory, where a
- * call needs any, is a caller-provided workspace argument. The library
- * allocates nothing, keeps no pointer after a call returns, holds no state
- * and may be called from several host threads. All work is enqueued
+ * call needs any, is a caller-provided workspace argument (except for
+ * msda_backward_noalloc, whose scratch is a static device array of the
+ * library). The library allocates nothing, keeps no pointer after a call
+ * returns, holds no other state and may be called from several host threads. All work is enqueued
  * on `stream` (0 = the null stream) with no host synchronization; results are
  * ready when the stream reaches them. Outputs are overwritten, never
  * accumulated into.
@@ -67,7 +68,7 @@ extern "C" {
 #endif
 
 #define MSDA_VERSION_MAJOR 0
-#define MSDA_VERSION_MINOR 6
+#define MSDA_VERSION_MINOR 7
 #define MSDA_VERSION_PATCH 0
 
 /* Largest number of feature levels the kernels accept. */
@@ -83,7 +84,9 @@ typedef enum {
     MSDA_SUCCESS = 0,
     MSDA_ERROR_INVALID_VALUE = 1, /* NULL/unaligned pointer, negative or inconsistent size */
     MSDA_ERROR_NOT_SUPPORTED = 2, /* valid request outside what the kernels implement      */
-    MSDA_ERROR_LAUNCH = 3         /* the HIP runtime refused a launch                      */
+    MSDA_ERROR_LAUNCH = 3,        /* the HIP runtime refused a launch                      */
+    MSDA_ERROR_SCRATCH_TOO_SMALL = 4 /* msda_backward_noalloc: the problem needs more scratch
+                                        than its static array holds                         */
 } msda_status_t;
 
 /* Problem sizes. B, Nq and K may be 0 (empty work; outputs are still
@@ -154,6 +157,38 @@ msda_status_t msda_backward(const msda_dims_t *dims, msda_dtype_t value_dtype,
  * backward's size checks would. No HIP call. */
 msda_status_t msda_backward_workspace_size(const msda_dims_t *dims, msda_dtype_t value_dtype,
                                            size_t *bytes);
+
+/* Scratch bytes the allocation-free backward holds per GPU. */
+#define MSDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * msda_backward without the workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments (less the workspace),
+ * results and errors as msda_backward; the call allocates nothing.
+ *
+ * Its scratch (the value gradient's binning workspace) is a static device
+ * array of MSDA_NOALLOC_SCRATCH_BYTES bytes, of which each GPU the library runs on
+ * holds its own copy until the process ends.
+ *  - A problem whose msda_backward_workspace_size() exceeds
+ *    MSDA_NOALLOC_SCRATCH_BYTES (when grad_value is requested) returns
+ *    MSDA_ERROR_SCRATCH_TOO_SMALL and enqueues nothing: use msda_backward with a
+ *    workspace for it.
+ *  - The first call on a device looks that device's copy of the array up
+ *    (hipGetSymbolAddress; no allocation). The current device must be the one
+ *    `stream` belongs to.
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents (each call rewrites what it reads before reading it):
+ *    calls that overlap on one GPU, from other streams or host threads, race
+ *    and give wrong results. Order them on one stream or serialize them.
+ */
+msda_status_t msda_backward_noalloc(const msda_dims_t *dims, msda_dtype_t value_dtype,
+                                    const void *value, const int64_t *spatial_shapes,
+                                    const int64_t *level_start_index,
+                                    const float *sampling_locations,
+                                    const float *attention_weights, const float *grad_output,
+                                    float *grad_value, float *grad_sampling_locations,
+                                    float *grad_attention_weights, hipStream_t stream);
 
 /*
  * Reduced-precision storage (guide, section 4.1 and the CSDN explainer's

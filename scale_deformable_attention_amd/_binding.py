@@ -17,7 +17,9 @@ MSDA_DTYPE_F32 = 0
 MSDA_DTYPE_BF16 = 1
 MSDA_DTYPE_F16 = 2
 STATUS = {0: "MSDA_SUCCESS", 1: "MSDA_ERROR_INVALID_VALUE", 2: "MSDA_ERROR_NOT_SUPPORTED",
-          3: "MSDA_ERROR_LAUNCH"}
+          3: "MSDA_ERROR_LAUNCH", 4: "MSDA_ERROR_SCRATCH_TOO_SMALL"}
+# scratch the allocation-free backward holds per GPU (include/msda.h)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MsdaDims(ctypes.Structure):
@@ -71,6 +73,9 @@ def library():
         lib.msda_backward.restype = ctypes.c_int
         lib.msda_backward.argtypes = [ctypes.POINTER(MsdaDims), ctypes.c_int, vp, i64p, i64p, fp,
                                       fp, fp, fp, fp, fp, vp, ctypes.c_size_t, vp]
+        lib.msda_backward_noalloc.restype = ctypes.c_int
+        lib.msda_backward_noalloc.argtypes = [ctypes.POINTER(MsdaDims), ctypes.c_int, vp, i64p,
+                                              i64p, fp, fp, fp, fp, fp, fp, vp]
         lib.msda_backward_workspace_size.restype = ctypes.c_int
         lib.msda_backward_workspace_size.argtypes = [ctypes.POINTER(MsdaDims), ctypes.c_int,
                                                      ctypes.POINTER(ctypes.c_size_t)]
@@ -234,6 +239,50 @@ def msda_backward_workspace_size(value, sampling_locations, D=None):
     if st != 0:
         raise MsdaError(st, "msda_backward_workspace_size")
     return n.value
+
+
+def msda_backward_noalloc(value, spatial_shapes, level_start_index, sampling_locations,
+                          attention_weights, grad_output, grad_value=None,
+                          grad_sampling_locations=None, grad_attention_weights=None,
+                          needs=(True, True, True), stream=None):
+    """Core backward through msda_backward_noalloc (include/msda.h): no
+    workspace; the library's static per-GPU scratch serves instead. fp32
+    gradients, value fp32, bf16 or f16. Returns (grad_value,
+    grad_sampling_locations, grad_attention_weights) like msda_backward; the
+    gradients not given are allocated here (by torch), the call itself
+    allocates nothing. Raises MsdaError (MSDA_ERROR_SCRATCH_TOO_SMALL) for a
+    problem whose binning workspace exceeds the static scratch."""
+    dev, dims = _common(value, spatial_shapes, level_start_index, sampling_locations,
+                        attention_weights)
+    if sampling_locations.dtype != torch.float32 or attention_weights.dtype != torch.float32:
+        raise ValueError("msda_backward_noalloc takes fp32 locations and weights")
+    _check(grad_output, "grad_output", (torch.float32,), dev)
+    if grad_output.numel() != dims.B * dims.Nq * dims.M * dims.D:
+        raise ValueError("grad_output has the wrong number of elements")
+    outs = []
+    for need, given, shape, name in (
+            (needs[0], grad_value, (dims.B, dims.Nv, dims.M, dims.D), "grad_value"),
+            (needs[1], grad_sampling_locations, tuple(sampling_locations.shape),
+             "grad_sampling_locations"),
+            (needs[2], grad_attention_weights, tuple(attention_weights.shape),
+             "grad_attention_weights")):
+        if not need:
+            outs.append(None)
+        elif given is None:
+            outs.append(torch.empty(shape, dtype=torch.float32, device=dev))
+        else:
+            _check(given, name, (torch.float32,), dev)
+            if tuple(given.shape) != shape:
+                raise ValueError(f"{name} must have shape {shape}")
+            outs.append(given)
+    st = library().msda_backward_noalloc(ctypes.byref(dims), _value_dtype(value), _ptr(value),
+                                         _ptr(spatial_shapes), _ptr(level_start_index),
+                                         _ptr(sampling_locations), _ptr(attention_weights),
+                                         _ptr(grad_output), _ptr(outs[0]), _ptr(outs[1]),
+                                         _ptr(outs[2]), _stream(dev, stream))
+    if st != 0:
+        raise MsdaError(st, "msda_backward_noalloc")
+    return tuple(outs)
 
 
 def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, attention_weights,

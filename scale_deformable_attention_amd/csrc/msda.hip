@@ -1836,6 +1836,61 @@ msda_status_t msda_backward_ex(const msda_dims_t* dims, const msda_precision_t* 
                          workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+// ------------------------------------------------------------------ allocation-free backward
+// The scratch of msda_backward_noalloc: a static device array, one copy per GPU
+// (reserved when the code object is loaded on that GPU, held until the process
+// ends). In host code `scratch` names a host-side stand-in, not device memory:
+// kernels and copies get the device address looked up once per device below.
+static __device__ __align__(256) unsigned char scratch[MSDA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// This device's copy of `scratch`, looked up on the first call on the device
+// (with the device current); nullptr if the runtime cannot give it.
+void* noalloc_scratch(int dev) {
+    static std::atomic<void*> known[kMaxDevices];
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* ptr = known[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    known[dev].store(ptr, std::memory_order_release);
+    return ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+msda_status_t msda_backward_noalloc(const msda_dims_t* dims, msda_dtype_t value_dtype,
+                                    const void* value, const int64_t* spatial_shapes,
+                                    const int64_t* level_start_index,
+                                    const float* sampling_locations,
+                                    const float* attention_weights, const float* grad_output,
+                                    float* grad_value, float* grad_sampling_locations,
+                                    float* grad_attention_weights, hipStream_t stream) {
+    const msda_status_t st = check_dims(dims, value_dtype, true);
+    if (st != MSDA_SUCCESS) return st;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (grad_value && sizes_of(dims).value > 0) {
+        const size_t need = plan_backward(dims).bytes;
+        if (need > MSDA_NOALLOC_SCRATCH_BYTES) return MSDA_ERROR_SCRATCH_TOO_SMALL;
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return MSDA_ERROR_LAUNCH;
+        ws = noalloc_scratch(dev);
+        if (!ws) return MSDA_ERROR_LAUNCH;
+        ws_bytes = MSDA_NOALLOC_SCRATCH_BYTES;
+    }
+    const msda_precision_t pr = {value_dtype, MSDA_DTYPE_F32, MSDA_DTYPE_F32};
+    return backward_impl(dims, pr, value, spatial_shapes, level_start_index, sampling_locations,
+                         attention_weights, grad_output, grad_value, grad_sampling_locations,
+                         grad_attention_weights, ws, ws_bytes, stream);
+}
+
 msda_status_t msda_forward_fused(const msda_dims_t* dims, msda_dtype_t value_dtype,
                                  const void* value, const int64_t* spatial_shapes,
                                  const int64_t* level_start_index, const float* reference_points,
@@ -2085,6 +2140,9 @@ const char* msda_status_string(msda_status_t status) {
         case MSDA_ERROR_INVALID_VALUE: return "invalid value (pointer, alignment, size or workspace)";
         case MSDA_ERROR_NOT_SUPPORTED: return "not supported (D, level count or tensor size)";
         case MSDA_ERROR_LAUNCH: return "kernel launch failed";
+        case MSDA_ERROR_SCRATCH_TOO_SMALL:
+            return "the problem needs more scratch than the allocation-free backward holds "
+                   "(use msda_backward with a workspace)";
     }
     return "unknown status";
 }

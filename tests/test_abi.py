@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["msda_backward", "msda_backward_ex", "msda_backward_fused",
-                                    "msda_backward_fused_workspace_size",
+                                    "msda_backward_fused_workspace_size", "msda_backward_noalloc",
                                     "msda_backward_workspace_size", "msda_check_tables",
                                     "msda_dcn_backward", "msda_dcn_backward_workspace_size",
                                     "msda_dcn_forward", "msda_forward", "msda_forward_ex",
@@ -44,8 +44,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = msda.library()
-    assert lib.msda_version() == 600
-    for s in range(4):
+    assert lib.msda_version() == 700
+    for s in range(5):
         assert len(lib.msda_status_string(s)) > 0
     assert lib.msda_status_string(99) == b"unknown status"
 
@@ -311,3 +311,20 @@ def test_c_client_builds_and_reports_version():
     r = subprocess.run([binary], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stderr
     assert int(r.stdout.strip()) == msda.msda_version()
+
+
+def test_noalloc_backward_checks():
+    """The allocation-free backward checks its arguments like msda_backward and
+    refuses, before any HIP call, a problem whose binning workspace is larger
+    than its static scratch (unless grad_value is not requested)."""
+    lib = msda.library()
+
+    def call(d, grad_value=FAKE):
+        return lib.msda_backward_noalloc(None if d is None else ctypes.byref(d), 0, FAKE, FAKE,
+                                         FAKE, FAKE, FAKE, FAKE, grad_value, FAKE, FAKE, None)
+    assert call(None) == INVALID
+    assert call(dims(D=12)) == UNSUPPORTED
+    big = dims(B=4, M=8, D=32, L=4, K=4, Nq=22223, Nv=22223)
+    assert workspace_size(big)[1] > _binding.NOALLOC_SCRATCH_BYTES
+    assert call(big) == 4
+    assert b"allocation-free" in lib.msda_status_string(4)
