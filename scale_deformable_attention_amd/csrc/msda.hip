@@ -168,6 +168,7 @@ struct Params {
     // read from `off` and the modulation scalars from `attn`
     int out_W, kernel_w, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w;
     int lvl_H, lvl_W;         // the level table when shapes is null (one level)
+    int hp;                   // heads taken together in the work order (tuple_of)
 };
 
 // Where a kernel's sampling locations and weights come from.
@@ -358,23 +359,32 @@ __device__ inline uint32_t tuple_base_bytes(const Params& p, int t, int row_byte
 // ------------------------------------------------------------------ work order
 // Workgroups are handed to the 8 XCDs round-robin (block i runs on XCD i % 8)
 // and each XCD has its own L2. The tuple kernels therefore walk tuples in
-// (b, m, q) order and give each XCD one contiguous share of that order: an
-// XCD then works through one (b, m) value plane at a time (2.8 MB at the
-// 800x1333 pyramid, D = 32 fp32), which its 4 MB L2 holds, and consecutive
-// queries of one head sample neighbouring rows.
+// (b, m, q) order (heads sharing cache lines together, see tuple_of) and give
+// each XCD one contiguous share of that order: an XCD then works through one
+// (b, m) value plane at a time (2.8 MB at the 800x1333 pyramid, D = 32 fp32),
+// which its 4 MB L2 holds, and consecutive queries of one head sample
+// neighbouring rows.
 __device__ inline int xcd_block() {
     const int blk = blockIdx.x, nblk = gridDim.x;
     const int x = blk % 8, i = blk / 8, per = nblk / 8, rem = nblk % 8;
     return x * per + (x < rem ? x : rem) + i;
 }
 
-// Position in the (b, m, q) work order -> index of the tuple in memory order
-// ((b * Nq + q) * M + m).
+// Position in the work order -> index of the tuple in memory order
+// ((b * Nq + q) * M + m). The work order is (b, m, q), except that heads whose
+// rows share a 128-byte cache line (p.hp > 1 of them: rows narrower than a
+// line, e.g. 64-byte bf16 rows at D = 32) are taken together, q by q:
+// (b, m / hp, q, m % hp). The plane of one head alone then touches every line
+// of its head group, and visiting the hp planes one after another would bring
+// each line in hp times.
 __device__ inline int tuple_of(const Params& p, int logical) {
-    const int bm = logical / p.Nq;
-    const int q = logical - bm * p.Nq;
-    const int b = bm / p.M;
-    const int m = bm - b * p.M;
+    const int mi = logical % p.hp;
+    const int rest = logical / p.hp;
+    const int bmg = rest / p.Nq;
+    const int q = rest - bmg * p.Nq;
+    const int groups = p.M / p.hp;
+    const int b = bmg / groups;
+    const int m = (bmg - b * groups) * p.hp + mi;
     return (b * p.Nq + q) * p.M + m;
 }
 
@@ -1537,7 +1547,11 @@ Params make_params(const msda_dims_t* d, msda_dtype_t dt, const void* value, con
     p.LK = (int)(d->L * d->K);
     p.T = (int)(d->B * d->Nq * d->M);
     const int64_t elems = d->B * d->Nv * d->M * d->D;
-    p.value_bytes = (uint32_t)(elems * (dt == MSDA_DTYPE_F32 ? 4 : 2));
+    const int64_t elem = dt == MSDA_DTYPE_F32 ? 4 : 2;
+    p.value_bytes = (uint32_t)(elems * elem);
+    // heads whose value rows share a 128-byte line, taken together
+    const int64_t per_line = 128 / (d->D * elem);
+    p.hp = (per_line > 1 && d->M % per_line == 0) ? (int)per_line : 1;
     return p;
 }
 
