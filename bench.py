@@ -478,6 +478,9 @@ def main():
                     help="skip the one-call-at-a-time warm/cold timing (profiler runs)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--workspace-mib", type=float, default=0.0,
+                    help="backward workspace in MiB (0: msda_backward_workspace_size, the "
+                         "one-pass size; less runs the value gradient in passes)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -528,8 +531,10 @@ def main():
     gv = torch.empty(w.B, w.Nv, w.M, w.D, dtype=gdt, device=dev)
     gl = torch.empty(loc.shape, dtype=torch.float32, device=dev)
     ga = torch.empty(attn.shape, dtype=torch.float32, device=dev)
-    ws = torch.empty(max(msda.msda_backward_workspace_size(value, loc), 1), dtype=torch.uint8,
-                     device=dev)
+    ws_bytes = msda.msda_backward_workspace_size(value, loc)
+    if args.workspace_mib > 0:
+        ws_bytes = int(args.workspace_mib * (1 << 20))
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     backward = w.backward
     fused = args.frontend == "fused"
     if fused:
@@ -540,8 +545,10 @@ def main():
         gref = torch.empty_like(ref)
         goff = torch.empty_like(off)
         glog = torch.empty_like(logits)
-        ws = torch.empty(max(msda.msda_backward_fused_workspace_size(value, off), 1),
-                         dtype=torch.uint8, device=dev)
+        ws_bytes = msda.msda_backward_fused_workspace_size(value, off)
+        if args.workspace_mib > 0:
+            ws_bytes = int(args.workspace_mib * (1 << 20))
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
         def fwd():
             msda.msda_forward_fused(value, shapes, lsi, ref, off, logits, output=out)

@@ -154,9 +154,22 @@ msda_status_t msda_backward(const msda_dims_t *dims, msda_dtype_t value_dtype,
 
 /* Bytes of workspace msda_backward needs for these sizes (a function of the
  * sizes alone, not of the level shapes or data). Returns the same status the
- * backward's size checks would. No HIP call. */
+ * backward's size checks would. No HIP call.
+ *
+ * This is the workspace of the fastest plan, which bins the points of all
+ * B*M (batch, head) planes at once. A smaller workspace is accepted down to
+ * msda_backward_workspace_min_size(): the value gradient then runs in passes
+ * over groups of planes that share it (the results are the same, the call is
+ * slower: each pass ends on its densest tiles). The fused and DCNv3 backward
+ * calls follow the same rule (their workspace holds a fixed part, given by
+ * their own size function minus the core's, before the planes' bins). */
 msda_status_t msda_backward_workspace_size(const msda_dims_t *dims, msda_dtype_t value_dtype,
                                            size_t *bytes);
+
+/* The smallest workspace msda_backward accepts for these sizes: the bins of
+ * one (batch, head) plane per pass. No HIP call. */
+msda_status_t msda_backward_workspace_min_size(const msda_dims_t *dims,
+                                               msda_dtype_t value_dtype, size_t *bytes);
 
 /* Scratch bytes the allocation-free backward holds per GPU. */
 #define MSDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)

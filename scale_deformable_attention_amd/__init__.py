@@ -9,12 +9,13 @@ from ._binding import (MSDA_DTYPE_BF16, MSDA_DTYPE_F16, MSDA_DTYPE_F32, MsdaErro
                        ms_deform_attn_fused, msda_dcn_backward, msda_dcn_backward_workspace_size,
                        msda_dcn_forward,
                        msda_backward, msda_backward_fused, msda_backward_noalloc, msda_backward_fused_workspace_size,
-                       msda_backward_workspace_size, msda_check_tables, msda_forward,
+                       msda_backward_workspace_size, msda_backward_workspace_min_size,
+                       msda_check_tables, msda_forward,
                        msda_forward_fused, msda_layer_backward, msda_layer_forward,
                        msda_layer_sizes, msda_linear_backward,
                        msda_linear_backward_workspace_size, msda_linear_forward, msda_version)
 
-__all__ = ["msda_forward", "msda_backward", "msda_backward_workspace_size", "msda_backward_noalloc",
+__all__ = ["msda_forward", "msda_backward", "msda_backward_workspace_size", "msda_backward_noalloc", "msda_backward_workspace_min_size",
            "msda_forward_fused", "msda_backward_fused", "msda_backward_fused_workspace_size",
            "msda_linear_forward", "msda_linear_backward", "msda_linear_backward_workspace_size",
            "msda_layer_forward", "msda_layer_backward", "msda_layer_sizes",

@@ -76,6 +76,9 @@ def library():
         lib.msda_backward_noalloc.restype = ctypes.c_int
         lib.msda_backward_noalloc.argtypes = [ctypes.POINTER(MsdaDims), ctypes.c_int, vp, i64p,
                                               i64p, fp, fp, fp, fp, fp, fp, vp]
+        lib.msda_backward_workspace_min_size.restype = ctypes.c_int
+        lib.msda_backward_workspace_min_size.argtypes = [ctypes.POINTER(MsdaDims), ctypes.c_int,
+                                                         ctypes.POINTER(ctypes.c_size_t)]
         lib.msda_backward_workspace_size.restype = ctypes.c_int
         lib.msda_backward_workspace_size.argtypes = [ctypes.POINTER(MsdaDims), ctypes.c_int,
                                                      ctypes.POINTER(ctypes.c_size_t)]
@@ -228,6 +231,20 @@ def msda_forward(value, spatial_shapes, level_start_index, sampling_locations, a
     return output
 
 
+def msda_backward_workspace_min_size(value, sampling_locations):
+    """Smallest workspace msda_backward accepts for these tensors' sizes (the
+    value gradient then runs one (b, m) plane per pass)."""
+    B, Nv, M, Dv = value.shape
+    _, Nq, _, L, K, _ = sampling_locations.shape
+    dims = MsdaDims(B, Nv, M, Dv, L, Nq, K)
+    n = ctypes.c_size_t(0)
+    st = library().msda_backward_workspace_min_size(ctypes.byref(dims), _value_dtype(value),
+                                                    ctypes.byref(n))
+    if st != 0:
+        raise MsdaError(st, "msda_backward_workspace_min_size")
+    return n.value
+
+
 def msda_backward_workspace_size(value, sampling_locations, D=None):
     """Workspace bytes msda_backward needs for these tensors' sizes."""
     B, Nv, M, Dv = value.shape
@@ -294,8 +311,9 @@ def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, 
     the location and weight gradients are fp32, grad_value is fp32 or, with
     ``grad_value_dtype=torch.bfloat16``, bf16. An entry of ``needs`` set to
     False skips (and returns None for) that gradient. ``workspace`` (a uint8
-    GPU tensor of at least msda_backward_workspace_size bytes) is allocated
-    here when not given and grad_value is needed."""
+    GPU tensor; msda_backward_workspace_size bytes run the value gradient in
+    one pass, fewer -- down to one (b, m) plane's bins -- in several) is
+    allocated here when not given and grad_value is needed."""
     dev, dims = _common(value, spatial_shapes, level_start_index, sampling_locations,
                         attention_weights)
     _check(grad_output, "grad_output", (torch.float32,), dev)
@@ -329,8 +347,11 @@ def msda_backward(value, spatial_shapes, level_start_index, sampling_locations, 
             raise MsdaError(st, "msda_backward_workspace_size")
         if workspace is None:
             workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
-        elif workspace.device != dev or workspace.numel() * workspace.element_size() < n.value:
-            raise ValueError(f"workspace must be a {n.value}-byte tensor on {dev}")
+        elif workspace.device != dev or workspace.dtype != torch.uint8:
+            # a smaller workspace than msda_backward_workspace_size is used in
+            # several passes over the (b, m) planes; the library refuses one
+            # that does not hold a single plane's bins
+            raise ValueError(f"workspace must be a uint8 tensor on {dev}")
         ws_bytes = workspace.numel() * workspace.element_size()
     else:
         workspace = None
@@ -493,8 +514,8 @@ def msda_backward_fused(value, spatial_shapes, level_start_index, reference_poin
     n = msda_backward_fused_workspace_size(value, sampling_offsets)
     if workspace is None:
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
-    elif workspace.device != dev or workspace.numel() * workspace.element_size() < n:
-        raise ValueError(f"workspace must be a {n}-byte tensor on {dev}")
+    elif workspace.device != dev or workspace.dtype != torch.uint8:
+        raise ValueError(f"workspace must be a uint8 tensor on {dev}")
     st = library().msda_backward_fused(
         ctypes.byref(dims), _value_dtype(value), _ptr(value), _ptr(spatial_shapes),
         _ptr(level_start_index), _ptr(reference_points), _ptr(sampling_offsets),

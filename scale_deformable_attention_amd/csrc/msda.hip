@@ -149,10 +149,12 @@ struct Params {
     // grad_value binning (backward only)
     int nW;                   // bin blocks per (b, m)
     int Qc;                   // queries per bin block
-    int t_stride;             // row stride of the per-block tile table
+    int t_stride;             // rows of the tile table per (b, m): tiles + 1
+    int bm0, bm_count;        // the (b, m) planes of this pass: [bm0, bm0 + bm_count)
     uint32_t slab_per_block;  // point-index capacity of one bin block's slab
-    uint2* table;             // [B*M][t_stride][nW] (count, offset)
-    float4* slab;             // [B*M*nW][slab_per_block] (tuple bits, x, y, A) entries
+    uint32_t* table;          // [bm_count][t_stride][nW] slab offset of each tile's entries
+                              // (tile t's count = row t+1 - row t)
+    float4* slab;             // [bm_count*nW][slab_per_block] (tuple bits, x, y, A) entries
     uint32_t* counters;       // tile work counters, one per XCD group, kCounterStride apart
     // fused front-end: locations and weights formed from the model's raw
     // outputs inside the kernels
@@ -924,14 +926,15 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
     setup_tiles<TS::TW, TH>(p, lt, &s_tiles);
     // tables inconsistent with Nv could exceed the row: drop those tiles
     // rather than write past the workspace
-    const int T = block_uniform(min(s_tiles, p.t_stride));
+    const int T = block_uniform(min(s_tiles, p.t_stride - 1));
     const int tid = threadIdx.x;
-    const int bm = blockIdx.x / p.nW, w = blockIdx.x - bm * p.nW;
+    const int bml = blockIdx.x / p.nW, w = blockIdx.x - bml * p.nW;   // plane of the pass
+    const int bm = p.bm0 + bml;
     const int b = bm / p.M, m = bm - b * p.M;
     const int q_begin = min(w * p.Qc, p.Nq), q_end = min(q_begin + p.Qc, p.Nq);
     const int npts = (q_end - q_begin) * p.LK;
     // this block's column of the (tile, bin block) table of its (b, m)
-    uint2* row = p.table + (size_t)bm * p.t_stride * p.nW + w;
+    uint32_t* row = p.table + (size_t)bml * p.t_stride * p.nW + w;
     float4* slab = p.slab + (size_t)blockIdx.x * p.slab_per_block;
     if (blockIdx.x == 0 && tid < 8) p.counters[tid * kCounterStride] = 0;   // for the tile kernel that follows
     // location (and weight) of the walk's current point, or of its first point
@@ -995,7 +998,7 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
             }
             __syncthreads();
             const uint32_t total = block_exclusive_scan(cnt, off, rn, scratch);
-            for (int i = tid; i < rn; i += kBlock) row[(size_t)(r0 + i) * p.nW] = make_uint2(cnt[i], base + off[i]);
+            for (int i = tid; i < rn; i += kBlock) row[(size_t)(r0 + i) * p.nW] = base + off[i];
             __syncthreads();
             for (int i = tid; i < rn; i += kBlock) cnt[i] = 0;
             __syncthreads();
@@ -1016,6 +1019,7 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
             base += total;
             __syncthreads();
         }
+        if (tid == 0) row[(size_t)T * p.nW] = base;   // end of the last tile's entries
         return;
     }
     // a point index that is always valid (npts > 0 whenever a loop body runs)
@@ -1050,7 +1054,7 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
         }
         __syncthreads();
         const uint32_t total = block_exclusive_scan(cnt, off, rn, scratch);
-        for (int i = tid; i < rn; i += kBlock) row[(size_t)(r0 + i) * p.nW] = make_uint2(cnt[i], base + off[i]);
+        for (int i = tid; i < rn; i += kBlock) row[(size_t)(r0 + i) * p.nW] = base + off[i];
         __syncthreads();
         for (int i = tid; i < rn; i += kBlock) cnt[i] = 0;
         __syncthreads();
@@ -1092,6 +1096,7 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
         base += total;
         __syncthreads();
     }
+    if (tid == 0) row[(size_t)T * p.nW] = base;   // end of the last tile's entries
 }
 
 // One work item = one tile of one (b, m). Work items are fetched dynamically
@@ -1138,9 +1143,9 @@ void msda_tile_kernel(Params p) {
         grec[kZero] = kOutside;   // out of the buffer's range: loads zeros
     }
     setup_tiles<TW, TH>(p, lt, &s_tiles);
-    const int T = block_uniform(min(s_tiles, p.t_stride));
+    const int T = block_uniform(min(s_tiles, p.t_stride - 1));
     const int tid = threadIdx.x;
-    const int BM = p.B * p.M;
+    const int BM = p.bm_count;   // the planes of this pass
     const int col = tid / G, r = tid % G;
     // upstream-gradient rows through a buffer descriptor: 32-bit offsets
     const __amdgpu_buffer_rsrc_t grsrc =
@@ -1169,13 +1174,15 @@ void msda_tile_kernel(Params p) {
         const LevelTiles L_ = lt[l];
         const int ty = (tl - L_.tile_base) / L_.ntx, tx = (tl - L_.tile_base) - ty * L_.ntx;
         const int y_base = ty * TH, x_base = tx * TW;
-        const int b = bm / p.M, m = bm - b * p.M;
+        const int b = (p.bm0 + bm) / p.M, m = (p.bm0 + bm) - b * p.M;
 
-        // this tile's entries in every slab of (b, m)
+        // this tile's entries in every slab of (b, m): rows tl and tl + 1 of
+        // the table hold where they start and end
+        const uint32_t* trow = p.table + ((size_t)bm * p.t_stride + tl) * p.nW;
         for (int w = tid; w < p.nW; w += kBlock) {
-            const uint2 e = p.table[((size_t)bm * p.t_stride + tl) * p.nW + w];
-            wcnt[w] = e.x;
-            woff[w] = e.y;
+            const uint32_t lo = trow[w];
+            wcnt[w] = trow[p.nW + w] - lo;
+            woff[w] = lo;
         }
         __syncthreads();
         const uint32_t E = (uint32_t)block_uniform((int)block_exclusive_scan(wcnt, wstart, p.nW, scratch));
@@ -1474,23 +1481,36 @@ msda_status_t check_dims(const msda_dims_t* d, msda_dtype_t dt, bool backward) {
 }
 
 // Workspace of the grad_value path (bin + tile kernels): 8 work counters of
-// the tile kernel (kCounterStride words apart), then per (b, m), nW bin blocks each own Qc queries, a row of
-// (count, offset) per tile and a slab of 16-byte entries (at most 4 per point:
-// one per corner tile). The
-// tile count of one (b, m) is bounded from Nv and L alone: a level of H x W
-// pixels has ceil(H/4) ceil(W/TW) tiles (TW >= 15), which is at most
-// H/4 + 3/4 when W <= TW and below (H+3) W / (2 TW) <= 2 H W / 15 otherwise,
-// so sum_l <= Nv/4 + L.
+// the tile kernel (kCounterStride words apart), then, for each (b, m) plane of
+// a pass, nW bin blocks each owning Qc queries, a table of nW slab offsets per
+// tile boundary and a slab of 16-byte entries per bin block (at most 4 per
+// point: one per tile its inside corners fall in). The tile count of one
+// (b, m) is bounded from Nv and L alone: a level of H x W pixels has
+// ceil(H/4) ceil(W/TW) tiles (TW >= 15), which is at most H/4 + 3/4 when
+// W <= TW and below (H+3) W / (2 TW) <= 2 H W / 15 otherwise, so
+// sum_l <= Nv/4 + L, and the table has Nv/4 + L + 1 rows per (b, m).
+//
+// The planes are binned and swept in passes of bm_per_pass planes that share
+// the workspace: the bytes per plane are fixed by the sizes, so a workspace
+// of any size from one plane's up to all planes' (one pass, the fastest) is
+// used in as few passes as it allows. Passes of a multiple of 8 planes keep
+// the tile kernel's 8 XCD groups busy alike.
 struct BwdPlan {
     int64_t nW = 0, Qc = 0, t_stride = 0, slab_per_block = 0;
+    int64_t bm_per_pass = 0, passes = 0;
     int tall = 0;   // tiles of kTileHTall rows (1) or kTileH rows (0)
     int cached = 0; // bin blocks of at most kBinUnroll points per thread (1)
     size_t counters_off = 0, table_off = 0, slab_off = 0, bytes = 0;
+    size_t min_bytes = 0;   // the workspace of one plane per pass
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-BwdPlan plan_backward(const msda_dims_t* d) {
+constexpr size_t kCountersBytes = 8 * kCounterStride * sizeof(uint32_t);
+
+// The plan for a workspace of at most `budget` bytes (the fewest passes that
+// fit; bytes = 0 when not even one plane fits).
+BwdPlan plan_backward(const msda_dims_t* d, size_t budget = SIZE_MAX) {
     BwdPlan pl;
     const int64_t BM = d->B * d->M;
     if (BM == 0) return pl;
@@ -1516,17 +1536,36 @@ BwdPlan plan_backward(const msda_dims_t* d) {
     const int64_t Qc = d->Nq > 0 ? (d->Nq + nW - 1) / nW : 0;
     pl.nW = Qc > 0 ? (d->Nq + Qc - 1) / Qc : 1;
     pl.Qc = Qc;
-    pl.t_stride = (d->Nv + 3) / 4 + d->L;
+    pl.t_stride = (d->Nv + 3) / 4 + d->L + 1;
     static_assert(kTileH >= 4 && kTileHTall >= 4, "the tile-count bound above assumes tiles of 4 rows or more");
     // tall tiles where a (b, m) has fewer points than pixels
     pl.tall = d->Nq * d->L * d->K < d->Nv ? 1 : 0;
     pl.slab_per_block = round_up((size_t)(4 * Qc * d->L * d->K), 64);
-    const size_t table_bytes = (size_t)(BM * pl.nW * pl.t_stride) * sizeof(uint2);
-    const size_t slab_bytes = (size_t)(BM * pl.nW * pl.slab_per_block) * sizeof(float4);
+    const size_t table_plane = (size_t)(pl.nW * pl.t_stride) * sizeof(uint32_t);
+    const size_t slab_plane = (size_t)(pl.nW * pl.slab_per_block) * sizeof(float4);
+    auto bytes_for = [&](int64_t planes) {
+        return round_up(kCountersBytes, kWorkspaceAlign) +
+               round_up(table_plane * planes, kWorkspaceAlign) +
+               round_up(slab_plane * planes, kWorkspaceAlign);
+    };
+    pl.min_bytes = bytes_for(1);
+    int64_t per = BM;
+    if (bytes_for(per) > budget) {
+        if (pl.min_bytes > budget) return pl;   // bytes = 0: does not fit
+        // the most planes that fit, rounded down to a multiple of 8 when >= 8
+        int64_t lo = 1, hi = BM;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) / 2;
+            if (bytes_for(mid) <= budget) lo = mid; else hi = mid - 1;
+        }
+        per = lo >= 8 ? lo - lo % 8 : lo;
+    }
+    pl.bm_per_pass = per;
+    pl.passes = (BM + per - 1) / per;
     pl.counters_off = 0;
-    pl.table_off = round_up(8 * kCounterStride * sizeof(uint32_t), kWorkspaceAlign);   // after the 8 work counters
-    pl.slab_off = pl.table_off + round_up(table_bytes, kWorkspaceAlign);
-    pl.bytes = pl.slab_off + round_up(slab_bytes, kWorkspaceAlign);
+    pl.table_off = round_up(kCountersBytes, kWorkspaceAlign);   // after the 8 work counters
+    pl.slab_off = pl.table_off + round_up(table_plane * per, kWorkspaceAlign);
+    pl.bytes = bytes_for(per);
     return pl;
 }
 
@@ -1657,56 +1696,66 @@ Kernels pick(msda_dtype_t dt, int64_t D) {
     return Kernels();
 }
 
-// grad_value: the bin kernel, then the tile kernel, on the workspace of `pl`
-// (bins and tiles hold the variants indexed as in Kernels; the plan picks).
+// grad_value: the bin kernel, then the tile kernel, pass after pass, on the
+// workspace of `pl` (bins and tiles hold the variants indexed as in Kernels;
+// the plan picks).
 msda_status_t launch_grad_value(Params& p, const BwdPlan& pl, const msda_dims_t* dims,
                                 const void* const* bins, const void* const* tiles,
                                 void* workspace, hipStream_t stream, bool bf16_out = false) {
     // the register-cached bin kernel holds kBinUnroll points per thread
     if (pl.cached && pl.Qc * dims->L * dims->K > (int64_t)kBinUnroll * kBlock)
         return MSDA_ERROR_LAUNCH;
+    if (pl.bytes == 0 || pl.bm_per_pass < 1) return MSDA_ERROR_INVALID_VALUE;
     const void* bin = bins[pl.tall + 2 * pl.cached];
     const void* tile = tiles[pl.tall];
     p.nW = (int)pl.nW;
     p.Qc = (int)pl.Qc;
     p.t_stride = (int)pl.t_stride;
     p.slab_per_block = (uint32_t)pl.slab_per_block;
-    p.table = reinterpret_cast<uint2*>(static_cast<char*>(workspace) + pl.table_off);
+    p.table = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + pl.table_off);
     p.slab = reinterpret_cast<float4*>(static_cast<char*>(workspace) + pl.slab_off);
     p.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + pl.counters_off);
-    const int64_t BM = dims->B * dims->M;
-    msda_status_t s = launch(bin, BM * pl.nW, p, stream);
-    if (s != MSDA_SUCCESS) return s;
-    // persistent: blocks fetch (b, m, tile) work items, as many blocks as fit
-    // on the GPU at once; the grid is a multiple of 8 for the XCD-affine
-    // schedule
+    // persistent tile kernel: blocks fetch (b, m, tile) work items, as many
+    // blocks as fit on the GPU at once; the grid is a multiple of 8 for the
+    // XCD-affine schedule
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return MSDA_ERROR_LAUNCH;
     const int per_cu = tile_blocks_per_cu(dims->D, tile, bf16_out, pl.tall);
-    const int64_t items = BM * pl.t_stride;
     const int64_t resident = ((int64_t)per_cu * (cus > 0 ? cus : 1) + 7) / 8 * 8;
-    const int64_t grid = items < resident ? ((items + 7) / 8) * 8 : resident;
-    return launch(tile, grid, p, stream);
+    const int64_t BM = dims->B * dims->M;
+    for (int64_t bm0 = 0; bm0 < BM; bm0 += pl.bm_per_pass) {
+        p.bm0 = (int)bm0;
+        p.bm_count = (int)std::min<int64_t>(pl.bm_per_pass, BM - bm0);
+        msda_status_t s = launch(bin, p.bm_count * pl.nW, p, stream);
+        if (s != MSDA_SUCCESS) return s;
+        const int64_t items = p.bm_count * (pl.t_stride - 1);
+        const int64_t grid = items < resident ? ((items + 7) / 8) * 8 : resident;
+        s = launch(tile, grid, p, stream);
+        if (s != MSDA_SUCCESS) return s;
+    }
+    return MSDA_SUCCESS;
 }
 
-// Workspace of the fused backward: the core's (grad_value path), then the
-// tuples' softmax statistics, then room for the offsets' gradient when the
-// caller asks for the reference points' gradient only.
+// Workspace of the fused backward: the tuples' softmax statistics, room for
+// the offsets' gradient when the caller asks for the reference points'
+// gradient only, then the core's grad_value workspace (planned for what is
+// left of `budget`).
 struct FusedPlan {
     BwdPlan core;
-    size_t smax_off = 0, goff_off = 0, bytes = 0;
+    size_t smax_off = 0, goff_off = 0, core_off = 0, bytes = 0;
 };
 
-FusedPlan plan_backward_fused(const msda_dims_t* d) {
+FusedPlan plan_backward_fused(const msda_dims_t* d, size_t budget = SIZE_MAX) {
     FusedPlan f;
-    f.core = plan_backward(d);
     const Sizes n = sizes_of(d);
     const int64_t T = d->B * d->Nq * d->M;
-    f.smax_off = round_up(f.core.bytes, kWorkspaceAlign);
-    f.goff_off = f.smax_off + round_up((size_t)T * sizeof(float2), kWorkspaceAlign);
-    f.bytes = f.goff_off + round_up((size_t)n.points * 2 * sizeof(float), kWorkspaceAlign);
+    f.smax_off = 0;
+    f.goff_off = round_up((size_t)T * sizeof(float2), kWorkspaceAlign);
+    f.core_off = f.goff_off + round_up((size_t)n.points * 2 * sizeof(float), kWorkspaceAlign);
+    f.core = plan_backward(d, budget > f.core_off ? budget - f.core_off : 0);
+    f.bytes = f.core_off + f.core.bytes;
     return f;
 }
 
@@ -1768,9 +1817,8 @@ msda_status_t backward_impl(const msda_dims_t* dims, const msda_precision_t& pr,
         !aligned(spatial_shapes, 8) || !aligned(level_start_index, 8) ||
         !aligned(workspace, kWorkspaceAlign))
         return MSDA_ERROR_INVALID_VALUE;
-    const BwdPlan pl = plan_backward(dims);
-    if (grad_value && n.value && (!workspace || workspace_bytes < pl.bytes))
-        return MSDA_ERROR_INVALID_VALUE;
+    const BwdPlan pl = plan_backward(dims, workspace ? workspace_bytes : 0);
+    if (grad_value && n.value && (!workspace || pl.bytes == 0)) return MSDA_ERROR_INVALID_VALUE;
     Params p = make_params(dims, pr.value, value, spatial_shapes, level_start_index,
                            static_cast<const float*>(sampling_locations),
                            static_cast<const float*>(attention_weights));
@@ -1820,6 +1868,15 @@ msda_status_t msda_backward_workspace_size(const msda_dims_t* dims, msda_dtype_t
     const msda_status_t st = check_dims(dims, value_dtype, true);
     if (st != MSDA_SUCCESS) return st;
     *bytes = plan_backward(dims).bytes;
+    return MSDA_SUCCESS;
+}
+
+msda_status_t msda_backward_workspace_min_size(const msda_dims_t* dims, msda_dtype_t value_dtype,
+                                               size_t* bytes) {
+    if (!bytes) return MSDA_ERROR_INVALID_VALUE;
+    const msda_status_t st = check_dims(dims, value_dtype, true);
+    if (st != MSDA_SUCCESS) return st;
+    *bytes = plan_backward(dims).min_bytes;
     return MSDA_SUCCESS;
 }
 
@@ -1891,8 +1948,9 @@ msda_status_t msda_backward_noalloc(const msda_dims_t* dims, msda_dtype_t value_
     void* ws = nullptr;
     size_t ws_bytes = 0;
     if (grad_value && sizes_of(dims).value > 0) {
-        const size_t need = plan_backward(dims).bytes;
-        if (need > MSDA_NOALLOC_SCRATCH_BYTES) return MSDA_ERROR_SCRATCH_TOO_SMALL;
+        // as many (b, m) planes per pass as the scratch holds
+        if (plan_backward(dims, MSDA_NOALLOC_SCRATCH_BYTES).bytes == 0)
+            return MSDA_ERROR_SCRATCH_TOO_SMALL;
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return MSDA_ERROR_LAUNCH;
         ws = noalloc_scratch(dev);
@@ -1973,8 +2031,9 @@ msda_status_t msda_backward_fused(const msda_dims_t* dims, msda_dtype_t value_dt
     const bool want_point =
         p.T > 0 && (grad_reference_points || grad_sampling_offsets || grad_attention_logits);
     if (!want_value && !want_point) return MSDA_SUCCESS;
-    const FusedPlan pl = plan_backward_fused(dims);
-    if (!workspace || workspace_bytes < pl.bytes) return MSDA_ERROR_INVALID_VALUE;
+    const FusedPlan pl = plan_backward_fused(dims, workspace ? workspace_bytes : 0);
+    if (!workspace || workspace_bytes < pl.core_off || (want_value && pl.core.bytes == 0))
+        return MSDA_ERROR_INVALID_VALUE;
     p.ref = reference_points;
     p.off = sampling_offsets;
     p.logits = attention_logits;
@@ -1989,7 +2048,8 @@ msda_status_t msda_backward_fused(const msda_dims_t* dims, msda_dtype_t value_dt
                              p, stream);
     if (s != MSDA_SUCCESS) return s;
     if (want_value) {
-        s = launch_grad_value(p, pl.core, dims, k.bin_fused, k.tile, workspace, stream);
+        s = launch_grad_value(p, pl.core, dims, k.bin_fused, k.tile,
+                              static_cast<char*>(workspace) + pl.core_off, stream);
         if (s != MSDA_SUCCESS) return s;
     }
     if (!want_point) return MSDA_SUCCESS;
@@ -2112,9 +2172,8 @@ msda_status_t msda_dcn_backward(const msda_dcn_dims_t* dcn, msda_dtype_t input_d
         !aligned(offset, 8) || !aligned(grad_offset, 8) || !aligned(mask, 4) ||
         !aligned(grad_mask, 4) || !aligned(workspace, kWorkspaceAlign))
         return MSDA_ERROR_INVALID_VALUE;
-    const BwdPlan pl = plan_backward(&dims);
-    if (grad_input && n.value && (!workspace || workspace_bytes < pl.bytes))
-        return MSDA_ERROR_INVALID_VALUE;
+    const BwdPlan pl = plan_backward(&dims, workspace ? workspace_bytes : 0);
+    if (grad_input && n.value && (!workspace || pl.bytes == 0)) return MSDA_ERROR_INVALID_VALUE;
     Params p = make_params(&dims, input_dtype, input, nullptr, nullptr, nullptr, mask);
     dcn_params(p, dcn);
     p.off = offset;

@@ -43,13 +43,15 @@ def plan(B, M, Nq, L, K, Nv):
     return nW, Qc, cached, tall
 
 
-def workspace_bytes(B, M, Nq, L, K, Nv):
+def workspace_bytes(B, M, Nq, L, K, Nv, planes=None):
+    """Workspace of `planes` (b, m) planes per pass (all of them: one pass)."""
     BM = B * M
     if BM == 0:
         return 0
+    planes = BM if planes is None else planes
     nW, Qc, _, _ = plan(B, M, Nq, L, K, Nv)
-    t_stride = (Nv + 3) // 4 + L
+    t_stride = (Nv + 3) // 4 + L + 1          # tile boundaries per (b, m)
     slab_per_block = _up(4 * Qc * L * K, 64)
-    table = BM * nW * t_stride * 8
-    slab = BM * nW * slab_per_block * 16
+    table = planes * nW * t_stride * 4        # one slab offset per boundary and bin block
+    slab = planes * nW * slab_per_block * 16
     return _up(COUNTERS, ALIGN) + _up(table, ALIGN) + _up(slab, ALIGN)

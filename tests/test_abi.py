@@ -24,6 +24,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["msda_backward", "msda_backward_ex", "msda_backward_fused",
                                     "msda_backward_fused_workspace_size", "msda_backward_noalloc",
+                                    "msda_backward_workspace_min_size",
                                     "msda_backward_workspace_size", "msda_check_tables",
                                     "msda_dcn_backward", "msda_dcn_backward_workspace_size",
                                     "msda_dcn_forward", "msda_forward", "msda_forward_ex",
@@ -162,8 +163,16 @@ def test_workspace_size_and_checks():
     assert st2 == 0 and n2 > n
     assert workspace_size(dims(D=12))[0] == UNSUPPORTED
     assert msda.library().msda_backward_workspace_size(ctypes.byref(dims()), 0, None) == INVALID
-    # too small, missing or misaligned workspace is rejected before any launch
-    assert bwd_status(dims(), ws_bytes=n - 1) == INVALID
+    # a workspace smaller than one (b, m) plane's bins, missing or misaligned
+    # is rejected before any launch (between one plane's and n bytes the value
+    # gradient runs in several passes)
+    import bin_plan
+    one_plane = bin_plan.workspace_bytes(1, 2, 16, 2, 2, 80, planes=1)
+    m = ctypes.c_size_t(0)
+    assert msda.library().msda_backward_workspace_min_size(ctypes.byref(dims()), 0,
+                                                           ctypes.byref(m)) == 0
+    assert m.value == one_plane < n
+    assert bwd_status(dims(), ws_bytes=one_plane - 1) == INVALID
     assert bwd_status(dims(), ws=None) == INVALID
     assert bwd_status(dims(), ws=ctypes.c_void_p(0x10010)) == INVALID
     # no grad_value: no workspace needed (the call then launches, so only the
@@ -182,7 +191,11 @@ def test_fused_workspace_size_and_checks():
                                                   ctypes.byref(n)) == UNSUPPORTED
     assert lib.msda_backward_fused_workspace_size(ctypes.byref(dims()), 0, None) == INVALID
     lib.msda_backward_fused_workspace_size(ctypes.byref(dims()), 0, ctypes.byref(n))
-    assert fused_bwd_status(dims(), ws_bytes=n.value - 1) == INVALID
+    # fixed part (softmax statistics, offset-gradient room) + one plane's bins
+    import bin_plan
+    fixed = n.value - core
+    one_plane = fixed + bin_plan.workspace_bytes(1, 2, 16, 2, 2, 80, planes=1)
+    assert fused_bwd_status(dims(), ws_bytes=one_plane - 1) == INVALID
     assert fused_bwd_status(dims(), ws=None) == INVALID
     assert fused_bwd_status(dims(), ws=ctypes.c_void_p(0x10010)) == INVALID
 
@@ -280,7 +293,10 @@ def test_dcn_argument_checks():
         ctypes.byref(dcn_dims()), 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, ws,
         ctypes.c_size_t(nbytes), None)
     assert bwd(None, 0) == INVALID
-    assert bwd(FAKE, n.value - 1) == INVALID
+    import bin_plan   # the grouped problem as a core one: 2 planes of 42 pixels, 9 points
+    one_plane = bin_plan.workspace_bytes(1, 2, 42, 1, 9, 42, planes=1)
+    assert one_plane < n.value
+    assert bwd(FAKE, one_plane - 1) == INVALID
 
 
 def test_precision_checks():
@@ -315,8 +331,8 @@ def test_c_client_builds_and_reports_version():
 
 def test_noalloc_backward_checks():
     """The allocation-free backward checks its arguments like msda_backward and
-    refuses, before any HIP call, a problem whose binning workspace is larger
-    than its static scratch (unless grad_value is not requested)."""
+    refuses, before any HIP call, a problem one of whose (b, m) planes needs
+    more binning workspace than its static scratch holds."""
     lib = msda.library()
 
     def call(d, grad_value=FAKE):
@@ -324,7 +340,11 @@ def test_noalloc_backward_checks():
                                          FAKE, FAKE, FAKE, FAKE, grad_value, FAKE, FAKE, None)
     assert call(None) == INVALID
     assert call(dims(D=12)) == UNSUPPORTED
-    big = dims(B=4, M=8, D=32, L=4, K=4, Nq=22223, Nv=22223)
-    assert workspace_size(big)[1] > _binding.NOALLOC_SCRATCH_BYTES
+    # one (b, m) plane's bins beyond the scratch: refused (larger problems whose
+    # planes fit run in passes)
+    big = dims(B=1, M=1, D=32, L=4, K=4, Nq=100000, Nv=22223)
+    import bin_plan
+    assert bin_plan.workspace_bytes(1, 1, 100000, 4, 4, 22223, planes=1) > \
+        _binding.NOALLOC_SCRATCH_BYTES
     assert call(big) == 4
     assert b"allocation-free" in lib.msda_status_string(4)

@@ -87,6 +87,30 @@ def parity(w, x=None, backward=True):
     return x, t
 
 
+def test_backward_in_passes():
+    """A workspace holding one (b, group) plane's bins: the input gradient runs
+    in passes over the planes and matches the oracle."""
+    import bin_plan
+    import scale_deformable_attention_amd as msda
+    w = wl.DcnWorkload("dcn_passes", B=2, H=12, W=14, G=4, D=16, sigma_px=1.5, seed=450)
+    x = wl.generate_dcn(w)
+    t = to_gpu(x, w)
+    geo = geometry(w)
+    Ho, Wo = w.out_size
+    K = w.kernel[0] * w.kernel[1]
+    nbytes = bin_plan.workspace_bytes(w.B, w.G, Ho * Wo, 1, K, w.H * w.W, planes=1)
+    print(f"[dcn parity] {w.name}: {nbytes} B of workspace, one plane per pass", flush=True)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=t["input"].device)
+    gi, go, gm = msda.msda_dcn_backward(t["input"], t["offset"], t["mask"], t["grad_output"],
+                                        workspace=ws, **geo)
+    torch.cuda.synchronize()
+    rgi, rgo, rgm, agi, ago, agm = oracle.dcn_backward(
+        x["input"], x["offset"], x["mask"], x["grad_output"], with_abs=True, **geo)
+    check("grad_input", gi.cpu().numpy(), rgi, agi, RTOL["f32"])
+    check("grad_offset", go.cpu().numpy(), rgo, ago, RTOL["f32"])
+    check("grad_mask", gm.cpu().numpy(), rgm, agm, RTOL["f32"])
+
+
 def test_tiny():
     parity(wl.DCN_WORKLOADS["dcn_tiny"])
 

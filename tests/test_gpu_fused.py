@@ -113,6 +113,28 @@ def parity(w, x=None, backward=True):
     return x, t
 
 
+def test_backward_in_passes():
+    """A workspace holding the fixed part and the bins of 3 of the 16 (b, m)
+    planes: the value gradient runs in passes; all four gradients match."""
+    import bin_plan
+    import scale_deformable_attention_amd as msda
+    w = wl.Workload("fused_passes", B=2, M=8, D=32, K=4, shapes=SMALL_PYRAMID, ref="grid",
+                    sigma_px=3.0, seed=190)
+    x = perturb_levels(wl.generate(w), 191)
+    t = to_gpu(x, "f32")
+    full = msda.msda_backward_fused_workspace_size(t["value"], t["sampling_offsets"])
+    core = bin_plan.workspace_bytes(w.B, w.M, w.num_queries, w.L, w.K, w.Nv)
+    nbytes = full - core + bin_plan.workspace_bytes(w.B, w.M, w.num_queries, w.L, w.K, w.Nv,
+                                                    planes=3)
+    print(f"[fused parity] {w.name}: {nbytes} of {full} B of workspace", flush=True)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=t["value"].device)
+    got = msda.msda_backward_fused(*args(t), t["grad_output"], workspace=ws)
+    torch.cuda.synchronize()
+    res = oracle.backward_fused(*oracle_args(x), x["grad_output"], with_abs=True)
+    for name, g, r, a in zip(GRADS, [g.cpu().numpy() for g in got], res[:4], res[4:]):
+        check(name, g, r, a, RTOL["f32"])
+
+
 def perturb_levels(x, seed, scale=0.02):
     """Give every level its own reference point (a small shift per level)."""
     rng = np.random.default_rng(seed)

@@ -78,10 +78,36 @@ def test_noalloc_matches_backward_on_two_calls():
     _compare(small, xs, got_s, ref_s)
 
 
-def test_noalloc_refuses_a_problem_beyond_its_scratch():
+def test_noalloc_runs_a_large_problem_in_passes():
+    """A problem whose bins exceed the static scratch but whose single (b, m)
+    planes fit runs in several passes over the planes."""
+    import bin_plan
     import scale_deformable_attention_amd as msda
     dev = _dev()
-    B, Nv, M, D, L, K, Nq = 4, 22223, 8, 32, 4, 4, 22223
+    w = wl.Workload("noalloc_passes", B=2, M=8, D=32, K=4,
+                    shapes=((50, 84), (25, 42), (13, 21), (7, 11)), ref="uniform",
+                    sigma_px=3.0, Nq=5000, seed=951)
+    full = bin_plan.workspace_bytes(w.B, w.M, w.num_queries, w.L, w.K, w.Nv)
+    assert full > msda._binding.NOALLOC_SCRATCH_BYTES
+    assert bin_plan.workspace_bytes(w.B, w.M, w.num_queries, w.L, w.K, w.Nv, planes=1) < \
+        msda._binding.NOALLOC_SCRATCH_BYTES
+    x, t = _inputs(w, dev)
+    print(f"[noalloc] {w.name}: {full / 2**20:.0f} MiB of bins in passes", flush=True)
+    got = msda.msda_backward_noalloc(*_args(t))
+    torch.cuda.synchronize()
+    ref = msda.msda_backward(*_args(t))
+    torch.cuda.synchronize()
+    _compare(w, x, got, ref)
+
+
+def test_noalloc_refuses_a_problem_beyond_its_scratch():
+    """One (b, m) plane's bins larger than the scratch: refused, nothing written."""
+    import bin_plan
+    import scale_deformable_attention_amd as msda
+    dev = _dev()
+    B, Nv, M, D, L, K, Nq = 1, 22223, 1, 32, 4, 4, 100000
+    assert bin_plan.workspace_bytes(B, M, Nq, L, K, Nv, planes=1) > \
+        msda._binding.NOALLOC_SCRATCH_BYTES
     value = torch.zeros(B, Nv, M, D, device=dev)
     shapes = torch.tensor([[100, 167], [50, 84], [25, 42], [13, 21]], dtype=torch.int64,
                           device=dev)
@@ -89,7 +115,6 @@ def test_noalloc_refuses_a_problem_beyond_its_scratch():
     loc = torch.full((B, Nq, M, L, K, 2), 0.5, device=dev)
     attn = torch.full((B, Nq, M, L, K), 0.25, device=dev)
     g = torch.ones(B, Nq, M * D, device=dev)
-    assert msda.msda_backward_workspace_size(value, loc) > msda._binding.NOALLOC_SCRATCH_BYTES
     gv = torch.full((B, Nv, M, D), 7.0, device=dev)
     with pytest.raises(msda.MsdaError) as e:
         msda.msda_backward_noalloc(value, shapes, lsi, loc, attn, g, grad_value=gv)
