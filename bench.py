@@ -59,27 +59,69 @@ SPLIT_PRODUCTS = 6
 METRIC = "sampled points/sec (B·Nq·M·L·K) fwd+bwd; achieved HBM GB/s vs peak"
 
 
-def algorithmic_bytes(w, value_bytes_per_elem=4, fused=False, point_bytes=12, grad_value_bytes=4):
+def fused_locations(x):
+    """The fused front-end's single-precision locations: reference point plus
+    offset over the level's (W, H), the quotient and the sum each rounded."""
+    ref, off = x["reference_points_levels"], x["sampling_offsets"]
+    wh = np.array([[s_[1], s_[0]] for s_ in x["spatial_shapes"]], np.float32)   # [L, 2] (W, H)
+    q = (off / wh[None, None, None, :, None, :]).astype(np.float32)
+    return (ref[:, :, None, :, None, :] + q).astype(np.float32)
+
+
+def touched_value_rows(w, x, loc=None):
+    """(b, pixel, head) value rows that some sample's inside-the-level corner
+    reads, counted from the inputs: the rows a gather must bring in at least
+    once (all of them on the encoder workloads; about a third on the decoder,
+    whose 300 queries sample a small part of the pyramid). The pixel
+    coordinates are formed as the kernels form them (single-precision
+    u * W - 0.5)."""
+    loc = x["sampling_locations"] if loc is None else loc
+    B, Nq, M, L, K, _ = loc.shape
+    shapes, lsi = x["spatial_shapes"], x["level_start_index"]
+    seen = np.zeros((B, w.Nv, M), bool)
+    bi = np.arange(B)[:, None, None, None]
+    mi = np.arange(M)[None, None, :, None]
+    for l in range(L):
+        H, W = int(shapes[l][0]), int(shapes[l][1])
+        px = (loc[:, :, :, l, :, 0].astype(np.float32) * np.float32(W) - np.float32(0.5))
+        py = (loc[:, :, :, l, :, 1].astype(np.float32) * np.float32(H) - np.float32(0.5))
+        x0 = np.floor(px).astype(np.int64)
+        y0 = np.floor(py).astype(np.int64)
+        for dy in (0, 1):
+            for dx in (0, 1):
+                xc, yc = x0 + dx, y0 + dy
+                ok = (xc >= 0) & (xc < W) & (yc >= 0) & (yc < H)
+                row = int(lsi[l]) + np.where(ok, yc * W + xc, 0)
+                bb, mm, rr = np.broadcast_arrays(bi, mi, row)
+                seen[bb[ok], rr[ok], mm[ok]] = True
+    return int(seen.sum())
+
+
+def algorithmic_bytes(w, value_bytes_per_elem=4, fused=False, point_bytes=12, grad_value_bytes=4,
+                      touched_rows=None):
     """Compulsory bytes of each launch (each input read once, each output
     written once). Per sampled point: location 8 B + weight 4 B (+ their
     gradients 8 B + 4 B in the backward); fused: offset 8 B + logit 4 B (+
     their gradients), the same count. Per (b,q,m): D*4 B of output (or
-    upstream gradient). Per value element: read once (+ grad_value written
-    once in the backward). Fused also reads a reference point of 8 B per
-    (b,q,l) (and writes its gradient in the backward)."""
+    upstream gradient). Per value row touched by some sample: D elements read
+    once (touched_rows; every row if not given); per value element: grad_value
+    written once in the backward (all of it: untouched rows are written as
+    zeros). Fused also reads a reference point of 8 B per (b,q,l) (and writes
+    its gradient in the backward)."""
     P = w.points
     T = w.B * w.num_queries * w.M
     V = w.B * w.Nv * w.M * w.D
+    Vr = V if touched_rows is None else touched_rows * w.D
     R = w.B * w.num_queries * w.L * 8 if fused else 0
     pb, gb = point_bytes, grad_value_bytes
-    fwd = V * value_bytes_per_elem + P * pb + T * w.D * 4 + R
+    fwd = Vr * value_bytes_per_elem + P * pb + T * w.D * 4 + R
     # location/weight gradients: value, locations, weights, upstream gradient
     # in; their gradients (12 B per point) out
-    bwd_point = V * value_bytes_per_elem + P * pb + T * w.D * 4 + P * 12 + 2 * R
+    bwd_point = Vr * value_bytes_per_elem + P * pb + T * w.D * 4 + P * 12 + 2 * R
     # grad_value: locations, weights, upstream gradient in; grad_value out
     bwd_value = P * pb + T * w.D * 4 + V * gb + R
     # the whole backward reads each input once and writes each gradient once
-    bwd = V * value_bytes_per_elem + P * pb + T * w.D * 4 + V * gb + P * 12 + 2 * R
+    bwd = Vr * value_bytes_per_elem + P * pb + T * w.D * 4 + V * gb + P * 12 + 2 * R
     return {"forward": fwd, "bwd_point": bwd_point, "bwd_value": bwd_value, "backward": bwd,
             "step": fwd + bwd}
 
@@ -148,32 +190,81 @@ def calibrate_copy(mib):
                       "launches": 5}), flush=True)
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, x, budget_s, fused=False):
-    """The oracle as it stands (single thread) on a bounded sample: whole batch
-    entries of the workload, forward + backward, until the budget is used."""
+    """The oracle as it stands (plain C, one thread per call, double
+    accumulation) timed on a bounded sample of the same workload: whole batch
+    entries, forward + backward, first on one thread, then on every host
+    thread. For the second leg a batch entry's queries are split into one
+    slice per thread, each thread runs the oracle's forward and backward on
+    its slice (ctypes releases the interpreter lock during each call) and the
+    slices' partial grad_value sums are added afterwards (inside the timing).
+    Each leg runs batch entries until it has used half the budget."""
+    import threading
     import oracle
-    done_points, t_total, batches = 0, 0.0, 0
-    per_batch = w.points // w.B
     fwd, bwd = (oracle.forward_fused, oracle.backward_fused) if fused else \
         (oracle.forward, oracle.backward)
     keys = ("reference_points_levels", "sampling_offsets", "attention_logits") if fused else \
         ("sampling_locations", "attention_weights")
-    for b in range(w.B):
-        sl = slice(b, b + 1)
-        args = (x["value"][sl], x["spatial_shapes"], x["level_start_index"]) + \
-            tuple(x[k][sl] for k in keys)
-        t0 = time.perf_counter()
-        fwd(*args)
-        bwd(*args, x["grad_output"][sl])
-        t_total += time.perf_counter() - t0
-        done_points += per_batch
-        batches += 1
-        if t_total >= budget_s:
-            break
-    return {"value": done_points / t_total, "unit": "points/s", "cores": 1, "kind": "oracle",
-            "sample": f"{batches} of {w.B} batch entries of the same workload, forward + "
-                      f"backward, {done_points} points in {t_total:.1f} s, single thread, "
-                      f"double accumulation"}
+    per_batch = w.points // w.B
+    Nq = w.num_queries
+
+    def run_entry(b, nthreads):
+        bounds = np.linspace(0, Nq, nthreads + 1).astype(int)
+        parts = [None] * nthreads
+
+        def work(i):
+            qs = slice(bounds[i], bounds[i + 1])
+            args = (x["value"][b:b + 1], x["spatial_shapes"], x["level_start_index"]) + \
+                tuple(x[k][b:b + 1, qs] for k in keys)
+            fwd(*args)
+            parts[i] = bwd(*args, x["grad_output"][b:b + 1, qs])[0]
+        if nthreads == 1:
+            work(0)
+        else:
+            ts = [threading.Thread(target=work, args=(i,)) for i in range(nthreads)]
+            for t in ts:
+                t.start()
+            for t in ts:
+                t.join()
+        gv = parts[0]
+        for p_ in parts[1:]:
+            gv = gv + p_
+        return gv
+
+    def leg(nthreads):
+        done, t_total, entries = 0, 0.0, 0
+        while t_total < budget_s / 2:
+            b = entries % w.B
+            t0 = time.perf_counter()
+            run_entry(b, nthreads)
+            t_total += time.perf_counter() - t0
+            done += per_batch
+            entries += 1
+        return done / t_total, entries, done, t_total
+
+    threads = os.cpu_count() or 1
+    v1, e1, d1, t1 = leg(1)
+    vn, en, dn, tn = leg(threads)
+    model = cpu_model()
+    return {"value": vn, "unit": "points/s", "cores": threads, "kind": "oracle",
+            "sample": f"{en} batch entries of the same workload (each {per_batch} points, "
+                      f"forward + backward) on {threads} threads, query slices per thread, "
+                      f"{dn} points in {tn:.1f} s; double accumulation",
+            "cpu_model": model,
+            "single_thread": {"value": v1, "unit": "points/s", "cores": 1,
+                              "sample": f"{e1} batch entries, {d1} points in {t1:.1f} s"}}
 
 
 def layer_flops(w):
@@ -647,9 +738,11 @@ def main():
 
     ms_per_step = total_ms / args.steps
     pts_per_s = w.points / (ms_per_step * 1e-3)
+    touched = touched_value_rows(w, x, fused_locations(x) if fused else
+                                 (loc_np.astype(np.float32) if args.loc_dtype == "f16" else None))
     ab = algorithmic_bytes(w, 4 if w.value_dtype == "f32" else 2, fused,
                            6 if args.loc_dtype == "f16" else 12,
-                           2 if args.grad_dtype == "bf16" else 4)
+                           2 if args.grad_dtype == "bf16" else 4, touched)
     kernel_bytes = dict(zip(names, (ab["forward"], ab["bwd_point"], ab["bwd_value"])))
     dom_name = max(kernels, key=kernels.get)
     dom_ms, dom_bytes = kernels[dom_name], kernel_bytes[dom_name]
