@@ -156,6 +156,7 @@ struct Params {
                               // (tile t's count = row t+1 - row t)
     float4* slab;             // [bm_count*nW][slab_per_block] (tuple bits, x, y, A) entries
     uint32_t* counters;       // tile work counters, one per XCD group, kCounterStride apart
+    uint32_t grad_value_bytes;  // record count of the grad_value buffer (its stores are range-checked)
     // fused front-end: locations and weights formed from the model's raw
     // outputs inside the kernels
     const float* ref;         // [B, Nq, L, 2] reference points (x, y), normalized
@@ -1150,6 +1151,7 @@ void msda_tile_kernel(Params p) {
     // upstream-gradient rows through a buffer descriptor: 32-bit offsets
     const __amdgpu_buffer_rsrc_t grsrc =
         make_rsrc(p.grad_out, (uint32_t)((size_t)p.T * D * sizeof(float)));
+    const __amdgpu_buffer_rsrc_t gvrsrc = make_rsrc(p.grad_value, p.grad_value_bytes);
 
     const int xcd = blockIdx.x % 8;
     const int nbm_x = BM >= 8 ? (BM - xcd + 7) / 8 : 0;
@@ -1359,22 +1361,30 @@ void msda_tile_kernel(Params p) {
                 }
             }
         }
-        // every pixel of the tile that is inside the level, written once
+        // every pixel of the tile that is inside the level, written once,
+        // through a buffer descriptor: level tables inconsistent with Nv (the
+        // caller's contract, not checked on the device) cannot write past
+        // grad_value -- such a store lands beyond the record count and is
+        // dropped
         const int x = x_base + col;
         if (col < TW && x < L_.W) {
 #pragma unroll
             for (int yy = 0; yy < TH; ++yy) {
                 const int y = y_base + yy;
                 if (y < L_.H) {
-                    const size_t rowi = (size_t)b * p.Nv + L_.start + (size_t)y * L_.W + x;
-                    const size_t e = (rowi * p.M + m) * D + r * 4;
+                    const uint64_t rowi = (uint64_t)b * p.Nv + L_.start + (uint64_t)y * L_.W + x;
+                    const uint64_t byte = ((rowi * p.M + m) * D + r * 4) * (kBf16Out ? 2 : 4);
+                    const uint32_t voff = byte < p.grad_value_bytes ? (uint32_t)byte : kOutside;
                     if constexpr (kBf16Out) {
                         // rounded once, from the fp32 sum
-                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.grad_value) + e) =
-                            make_uint2(float_to_bf16_bits(own[yy].x) | (float_to_bf16_bits(own[yy].y) << 16),
-                                       float_to_bf16_bits(own[yy].z) | (float_to_bf16_bits(own[yy].w) << 16));
+                        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                        const u32x2 v = {float_to_bf16_bits(own[yy].x) | (float_to_bf16_bits(own[yy].y) << 16),
+                                         float_to_bf16_bits(own[yy].z) | (float_to_bf16_bits(own[yy].w) << 16)};
+                        __builtin_amdgcn_raw_buffer_store_b64(v, gvrsrc, voff, 0, 0);
                     } else {
-                        *reinterpret_cast<float4*>(p.grad_value + e) = own[yy];
+                        const u32x4 v = {as_uint(own[yy].x), as_uint(own[yy].y), as_uint(own[yy].z),
+                                         as_uint(own[yy].w)};
+                        __builtin_amdgcn_raw_buffer_store_b128(v, gvrsrc, voff, 0, 0);
                     }
                 }
             }
@@ -1715,6 +1725,8 @@ msda_status_t launch_grad_value(Params& p, const BwdPlan& pl, const msda_dims_t*
     p.table = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + pl.table_off);
     p.slab = reinterpret_cast<float4*>(static_cast<char*>(workspace) + pl.slab_off);
     p.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + pl.counters_off);
+    p.grad_value_bytes =
+        (uint32_t)(dims->B * dims->Nv * dims->M * dims->D * (bf16_out ? 2 : 4));   // < 2 GiB
     // persistent tile kernel: blocks fetch (b, m, tile) work items, as many
     // blocks as fit on the GPU at once; the grid is a multiple of 8 for the
     // XCD-affine schedule
