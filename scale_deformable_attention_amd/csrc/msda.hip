@@ -32,6 +32,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <cmath>
 
 #include "msda.h"
 
@@ -397,34 +398,106 @@ struct alignas(16) FwdRecord {
     float w[4];   // A * bilinear weight, 0 for corners outside
 };
 
-template <typename T, int D, int FE>
-__global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
+// A wave's LDS in the forward: the records of a chunk, or (fused front-end,
+// before a round's first chunk) the partial softmax statistics.
+union FwdWaveLds {
+    FwdRecord records[kWave];
+    float stat[kWave];
+};
+
+// ---- coarse levels in LDS
+// The tuple kernels are bound by the texture path (its address and
+// data-return units ~90% busy on the 800x1333 training batch), whose cost
+// follows the corner gathers issued through it, by the cache lines they
+// touch. Corners read from LDS do not use it. The staged forward runs a block
+// over kStagedQueries queries of one (b, m) plane: the block first copies the
+// rows of the plane's coarsest levels that fit in kStageBytes into LDS (at
+// D = 32 fp32 on the 800x1333 pyramid: the 13 x 21 level, 35 KB), then reads
+// those levels' corners there and the other levels' through buffer loads.
+// The stage is kept small so that three blocks (24 waves) share a CU: stages
+// of two levels and more, at one or two blocks per CU, lost more to latency
+// than the texture path gained, and staging half rows (two blocks per tuple,
+// one per channel half) doubled the lines each gather touches. The point
+// kernel keeps the plain work order: at 16 waves per CU (its registers) the
+// same staging made it slower.
+constexpr int kStagedWaves = 8;
+constexpr int kStagedBlock = kWave * kStagedWaves;
+constexpr int kStageBytes = 36 * 1024;     // staged rows, after one zero row at offset 0
+constexpr int kStagedQueries = 128;        // queries of one plane per block
+constexpr int kStagedMinQueries = 2048;    // planes with fewer queries take the plain kernels
+
+// Row widths (one head, bytes) with staged kernels.
+constexpr bool staged_row(int row_bytes) { return row_bytes == 64 || row_bytes == 128; }
+
+// Picks the coarsest levels whose rows (kRowBytes each: one head of the
+// plane) fit in the stage after a zero row, and copies them from the value
+// tensor (head_base: byte offset of the plane's row 0; row_stride: bytes from
+// one row of the tensor to the next). stage_base[l] = byte offset of level l's
+// first row in the stage, or -1. Ends with a block barrier.
+template <int kRowBytes>
+__device__ inline void stage_levels(const Params& p, const int4* levels, int* stage_base,
+                                    unsigned char* stage, __amdgpu_buffer_rsrc_t vrsrc,
+                                    uint32_t head_base, uint32_t row_stride) {
+    constexpr int kPieces = kRowBytes / 16;
+    static_assert(kRowBytes % 16 == 0 && kPieces <= kStagedBlock, "rows of 16-byte pieces");
+    if (threadIdx.x == 0) {
+        uint32_t used = kRowBytes;
+        for (int l = p.L - 1; l >= 0; --l) {
+            const uint64_t bytes = (uint64_t)levels[l].x * (uint64_t)levels[l].y * kRowBytes;
+            if (used + bytes <= (uint64_t)kStageBytes) {
+                stage_base[l] = (int)used;
+                used += (uint32_t)bytes;
+            } else {
+                stage_base[l] = -1;
+            }
+        }
+    }
+    if (threadIdx.x < (unsigned)kPieces)
+        *reinterpret_cast<u32x4*>(stage + threadIdx.x * 16u) = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    for (int l = 0; l < p.L; ++l) {
+        const int sb = block_uniform(stage_base[l]);
+        if (sb < 0) continue;
+        // a staged level holds at most kStageBytes / kRowBytes pixels
+        const int pieces = levels[l].x * levels[l].y * kPieces;
+        const uint32_t src0 = head_base + (uint32_t)levels[l].z * row_stride;
+        for (int i = threadIdx.x; i < pieces; i += kStagedBlock) {
+            const int pix = i / kPieces, c = i - pix * kPieces;
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+                vrsrc, src0 + (uint32_t)pix * row_stride + (uint32_t)c * 16u, 0, 0);
+            *reinterpret_cast<u32x4*>(stage + sb + i * 16) = v;
+        }
+    }
+    __syncthreads();
+}
+
+// Whether a staged level holds point j's corners (j below LK; read from LDS,
+// the same for every lane that asks about the same point).
+__device__ inline bool point_staged(const Params& p, const int* stage_base, int j) {
+    return stage_base[(unsigned)j / (unsigned)p.K] >= 0;
+}
+
+// One round of a forward kernel: a wave computes TPW tuples.
+//  phase 1: lane (jrow, i) builds the records of points jrow, jrow + G, ... of
+//           tuple t1 (one point per chunk of G), in LDS;
+//  phase 2: lane group g gathers the chunk's points of tuple t2 and
+//           accumulates channels [r*PL, r*PL + PL) (r: lane within the group).
+// base1: byte offset of tuple t1's row 0 in the value tensor. kStaged: the
+// corners of staged levels (stage_base as stage_levels left it) come from the
+// stage, their outside corners from its zero row.
+template <typename T, int D, int FE, bool kStaged>
+__device__ __forceinline__ void fwd_round(const Params& p, const int4* levels, FwdWaveLds& wl,
+                                          __amdgpu_buffer_rsrc_t vrsrc,
+                                          const unsigned char* stage, const int* stage_base,
+                                          int t1, bool t1_ok, uint32_t base1, int t2, bool t2_ok) {
     constexpr bool kFused = FE == kFeFused;
     using S = Shape<T, D>;
     constexpr int G = S::G, TPW = S::TPW, PL = S::kPerLane;
-    constexpr int kRowBytesPerHead = D * Elem<T>::kBytes;
-    __shared__ int4 levels[MSDA_MAX_LEVELS];
-    __shared__ FwdRecord records[kWavesPerBlock][kWave];
-    __shared__ float stat[kFused ? kWavesPerBlock : 1][kWave];
-    load_levels(p, levels);
-
+    constexpr uint32_t kHeadBytes = D * Elem<T>::kBytes;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int tuple0 = (xcd_block() * kWavesPerBlock + wave) * TPW;   // work-order position
-    if (tuple0 >= p.T) return;  // wave-uniform; no block barrier follows
-    const uint32_t row_bytes = (uint32_t)p.M * kRowBytesPerHead;
-    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(p.value, p.value_bytes);
-
-    // phase-1 role: this lane builds records of tuple t1 = tuple0 + lane % TPW
-    const int t1w = tuple0 + lane % TPW;
-    const int t1 = t1w < p.T ? tuple_of(p, t1w) : 0;
     const int jrow = lane / TPW;
-    const bool t1_ok = t1w < p.T;
-    const uint32_t base1 = t1_ok ? tuple_base_bytes(p, t1, row_bytes, kRowBytesPerHead) : 0;
-    // phase-2 role: this lane accumulates channels [r*PL, r*PL+PL) of tuple t2
     const int g = lane / G, r = lane % G;
-    const int t2w = tuple0 + g;
-    const int t2 = t2w < p.T ? tuple_of(p, t2w) : p.T;
+    const uint32_t row_bytes = (uint32_t)p.M * kHeadBytes;
 
     float acc[PL];
 #pragma unroll
@@ -457,10 +530,10 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
         }
         if (t1_ok)
             for (int j = jrow + kZ * G; j < p.LK; j += G) mx = fmaxf(mx, z[j]);
-        stat[wave][lane] = mx;
+        wl.stat[lane] = mx;
         wave_sync();
         mx = -INFINITY;
-        for (int i = 0; i < G; ++i) mx = fmaxf(mx, stat[wave][i * TPW + lane % TPW]);
+        for (int i = 0; i < G; ++i) mx = fmaxf(mx, wl.stat[i * TPW + lane % TPW]);
         wave_sync();
         float se = 0.0f;
 #pragma unroll
@@ -468,11 +541,11 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
             if (t1_ok && jrow + i * G < p.LK) se += expf(zr[i] - mx);
         if (t1_ok)
             for (int j = jrow + kZ * G; j < p.LK; j += G) se += expf(z[j] - mx);
-        stat[wave][lane] = se;
+        wl.stat[lane] = se;
         wave_sync();
         se = 0.0f;
-        for (int i = 0; i < G; ++i) se += stat[wave][i * TPW + lane % TPW];
-        wave_sync();
+        for (int i = 0; i < G; ++i) se += wl.stat[i * TPW + lane % TPW];
+        wave_sync();   // the records below reuse the statistics' LDS
         zmax = mx;
         inv_sum = 1.0f / se;
     }
@@ -483,50 +556,135 @@ __global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
         // phase 1: one point per lane -> record in LDS
         FwdRecord rec;
         const int j = jc + jrow;
+        bool st = false;
+        if constexpr (kStaged) st = j < p.LK && point_staged(p, stage_base, j);
         if (t1_ok && j < p.LK) {
             const int l = (unsigned)j / (unsigned)p.K;
             const int4 lv = levels[l];
             float2 uv;
             float a;
             finish_point<FE>(in, lv, zmax, inv_sum, uv, a);
-            const Geometry geo = geometry_of<FE>(uv, lv, base1, row_bytes);
+            const Geometry geo =
+                st ? geometry_of<FE>(uv, lv, (uint32_t)stage_base[l] - (uint32_t)lv.z * kHeadBytes,
+                                     kHeadBytes)
+                   : geometry_of<FE>(uv, lv, base1, row_bytes);
             const float ay0 = a * (1.0f - geo.fy), ay1 = a * geo.fy;
             const float w[4] = {ay0 * (1.0f - geo.fx), ay0 * geo.fx, ay1 * (1.0f - geo.fx),
                                 ay1 * geo.fx};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                rec.off[c] = geo.off[c];
+                rec.off[c] = (st && !geo.valid[c]) ? 0u : geo.off[c];
                 rec.w[c] = geo.valid[c] ? w[c] : 0.0f;
             }
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                rec.off[c] = kOutside;
+                rec.off[c] = st ? 0u : kOutside;
                 rec.w[c] = 0.0f;
             }
         }
-        records[wave][lane] = rec;
+        wl.records[lane] = rec;
         wave_sync();
-        // phase 2: the group gathers its G points of this chunk
+        // phase 2: the group gathers its G points of this chunk; point jc + i
+        // lies on one level for every group, so the choice of source is
+        // wave-uniform
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            const FwdRecord q = records[wave][i * TPW + g];
+            const FwdRecord q = wl.records[i * TPW + g];
+            bool lds = false;
+            if constexpr (kStaged)
+                lds = block_uniform((jc + i < p.LK && point_staged(p, stage_base, jc + i)) ? 1 : 0);
+            if (lds) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(
-                    vrsrc, q.off[c] + (uint32_t)r * 16u, 0, 0);
-                float v[PL];
-                Elem<T>::widen(raw, v);
+                for (int c = 0; c < 4; ++c) {
+                    const u32x4 raw =
+                        *reinterpret_cast<const u32x4*>(stage + q.off[c] + (uint32_t)r * 16u);
+                    float v[PL];
+                    Elem<T>::widen(raw, v);
 #pragma unroll
-                for (int e = 0; e < PL; ++e) acc[e] = fmaf(q.w[c], v[e], acc[e]);
+                    for (int e = 0; e < PL; ++e) acc[e] = fmaf(q.w[c], v[e], acc[e]);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(
+                        vrsrc, q.off[c] + (uint32_t)r * 16u, 0, 0);
+                    float v[PL];
+                    Elem<T>::widen(raw, v);
+#pragma unroll
+                    for (int e = 0; e < PL; ++e) acc[e] = fmaf(q.w[c], v[e], acc[e]);
+                }
             }
         }
-        wave_sync();
+        wave_sync();   // the next chunk (or round) rewrites this LDS
     }
-    if (t2 < p.T) {
+    if (t2_ok) {
         float4* dst = reinterpret_cast<float4*>(p.out + (size_t)t2 * D + r * PL);
 #pragma unroll
         for (int e = 0; e < PL; e += 4) dst[e / 4] = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+    }
+}
+
+// The forward over the work order: a wave takes TPW consecutive tuples.
+template <typename T, int D, int FE>
+__global__ __launch_bounds__(kBlock) void msda_fwd_kernel(Params p) {
+    using S = Shape<T, D>;
+    constexpr int G = S::G, TPW = S::TPW;
+    constexpr int kHeadBytes = D * Elem<T>::kBytes;
+    __shared__ int4 levels[MSDA_MAX_LEVELS];
+    __shared__ FwdWaveLds wave_lds[kWavesPerBlock];
+    load_levels(p, levels);
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int tuple0 = (xcd_block() * kWavesPerBlock + wave) * TPW;   // work-order position
+    if (tuple0 >= p.T) return;  // wave-uniform; no block barrier follows
+    const uint32_t row_bytes = (uint32_t)p.M * kHeadBytes;
+    const int t1w = tuple0 + lane % TPW;
+    const bool t1_ok = t1w < p.T;
+    const int t1 = t1_ok ? tuple_of(p, t1w) : 0;
+    const uint32_t base1 = t1_ok ? tuple_base_bytes(p, t1, row_bytes, kHeadBytes) : 0;
+    const int t2w = tuple0 + lane / G;
+    const bool t2_ok = t2w < p.T;
+    const int t2 = t2_ok ? tuple_of(p, t2w) : 0;
+    fwd_round<T, D, FE, false>(p, levels, wave_lds[wave], make_rsrc(p.value, p.value_bytes),
+                               nullptr, nullptr, t1, t1_ok, base1, t2, t2_ok);
+}
+
+// The forward with the coarse levels in LDS: a block takes kStagedQueries
+// queries of one (b, m) plane (XCD-contiguous, so that an XCD works through
+// a plane at a time); its waves take rounds of TPW queries.
+template <typename T, int D, int FE>
+__global__ __launch_bounds__(kStagedBlock) void msda_fwd_staged_kernel(Params p) {
+    using S = Shape<T, D>;
+    constexpr int G = S::G, TPW = S::TPW;
+    constexpr int kHeadBytes = D * Elem<T>::kBytes;
+    __shared__ int4 levels[MSDA_MAX_LEVELS];
+    __shared__ int stage_base[MSDA_MAX_LEVELS];
+    __shared__ FwdWaveLds wave_lds[kStagedWaves];
+    __shared__ __align__(16) unsigned char stage[kStageBytes];
+    load_levels(p, levels);
+
+    const int nqc = (p.Nq + kStagedQueries - 1) / kStagedQueries;
+    const int item = xcd_block();
+    const int qc = item % nqc, bm = item / nqc;
+    const int b = bm / p.M, m = bm - b * p.M;
+    const int q_begin = qc * kStagedQueries, q_end = min(q_begin + kStagedQueries, p.Nq);
+    const uint32_t row_bytes = (uint32_t)p.M * kHeadBytes;
+    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(p.value, p.value_bytes);
+    const uint32_t head_base = (uint32_t)b * (uint32_t)p.Nv * row_bytes + (uint32_t)m * kHeadBytes;
+    stage_levels<kHeadBytes>(p, levels, stage_base, stage, vrsrc, head_base, row_bytes);
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    // every bound of this loop is wave-uniform and no block barrier follows
+    for (int q0 = q_begin + wave * TPW; q0 < q_end; q0 += kStagedWaves * TPW) {
+        const int q1 = q0 + lane % TPW, q2 = q0 + lane / G;
+        const bool t1_ok = q1 < q_end, t2_ok = q2 < q_end;
+        const int t1 = t1_ok ? (b * p.Nq + q1) * p.M + m : 0;
+        const int t2 = t2_ok ? (b * p.Nq + q2) * p.M + m : 0;
+        fwd_round<T, D, FE, true>(p, levels, wave_lds[wave], vrsrc, stage, stage_base, t1, t1_ok,
+                                  head_base, t2, t2_ok);
     }
 }
 
@@ -1654,6 +1812,12 @@ struct Kernels {
     const void* point_half = nullptr;
     const void* bin_half[4] = {};
     const void* tile_bf16[2] = {};      // grad_value stored as bf16
+    // forward with the coarse levels in LDS, per front-end (null where
+    // staged_row() rules the head's row width out)
+    const void* fwd_staged = nullptr;
+    const void* fwd_fused_staged = nullptr;
+    const void* fwd_half_staged = nullptr;
+    int head_bytes = 0;   // D * element size
     int tuples_per_block = 0;
 };
 
@@ -1689,7 +1853,44 @@ Kernels kernels_for() {
     k.tile_bf16[0] = reinterpret_cast<const void*>(&msda_tile_kernel<D, true, kTileH>);
     k.tile_bf16[1] = reinterpret_cast<const void*>(&msda_tile_kernel<D, true, kTileHTall>);
     k.tuples_per_block = Shape<T, D>::TPW * kWavesPerBlock;
+    k.head_bytes = D * Elem<T>::kBytes;
+    if constexpr (staged_row(D * Elem<T>::kBytes)) {
+        k.fwd_staged = reinterpret_cast<const void*>(&msda_fwd_staged_kernel<T, D, kFeCore>);
+        k.fwd_fused_staged = reinterpret_cast<const void*>(&msda_fwd_staged_kernel<T, D, kFeFused>);
+        k.fwd_half_staged =
+            reinterpret_cast<const void*>(&msda_fwd_staged_kernel<T, D, kFeCoreHalf>);
+    }
     return k;
+}
+
+// Whether the staged forward pays: planes of enough
+// queries, and a coarsest level that fits in the stage. The level table is in
+// device memory, so the host estimates the coarsest level's size from Nv and
+// L as that of a pyramid that halves both sides from level to level
+// (Nv = c (4^L - 1) / 3 for c pixels at the coarsest level). A wrong guess
+// costs time, not correctness: the staged kernel stages what fits (possibly
+// nothing) and reads every other level through buffer loads.
+bool use_staged(const Params& p, int head_bytes) {
+    if (!staged_row(head_bytes) || p.Nq < kStagedMinQueries || p.LK <= 0) return false;
+    const double coarsest = 3.0 * (double)p.Nv / (std::ldexp(1.0, 2 * p.L) - 1.0);
+    return (coarsest + 1.0) * head_bytes <= (double)kStageBytes;
+}
+
+// The forward of one front-end: the staged kernel where use_staged() says
+// so, else the plain one.
+msda_status_t launch_forward(const void* plain, const void* staged, const Kernels& k, Params& p,
+                             hipStream_t stream) {
+    if (staged && use_staged(p, k.head_bytes)) {
+        const int64_t nqc = (p.Nq + kStagedQueries - 1) / kStagedQueries;
+        const int64_t blocks = (int64_t)p.B * p.M * nqc;
+        if (blocks <= 0) return MSDA_SUCCESS;
+        void* args[] = {&p};
+        const hipError_t e = hipLaunchKernel(staged, dim3((unsigned)blocks), dim3(kStagedBlock),
+                                             args, 0, stream);
+        return e == hipSuccess ? MSDA_SUCCESS : MSDA_ERROR_LAUNCH;
+    }
+    if (!plain) return MSDA_ERROR_NOT_SUPPORTED;
+    return launch(plain, ((int64_t)p.T + k.tuples_per_block - 1) / k.tuples_per_block, p, stream);
 }
 
 Kernels pick(msda_dtype_t dt, int64_t D) {
@@ -1804,9 +2005,8 @@ msda_status_t forward_impl(const msda_dims_t* dims, const msda_precision_t& pr, 
     p.out = output;
     if (p.T == 0) return MSDA_SUCCESS;
     const Kernels k = pick(pr.value, dims->D);
-    const void* kern = half ? k.fwd_half : k.fwd;
-    if (!kern) return MSDA_ERROR_NOT_SUPPORTED;
-    return launch(kern, ((int64_t)p.T + k.tuples_per_block - 1) / k.tuples_per_block, p, stream);
+    return launch_forward(half ? k.fwd_half : k.fwd, half ? k.fwd_half_staged : k.fwd_staged, k, p,
+                          stream);
 }
 
 msda_status_t backward_impl(const msda_dims_t* dims, const msda_precision_t& pr, const void* value,
@@ -2000,9 +2200,7 @@ msda_status_t msda_forward_fused(const msda_dims_t* dims, msda_dtype_t value_dty
     p.out = output;
     if (p.T == 0) return MSDA_SUCCESS;
     const Kernels k = pick(value_dtype, dims->D);
-    if (!k.fwd_fused) return MSDA_ERROR_NOT_SUPPORTED;
-    return launch(k.fwd_fused, ((int64_t)p.T + k.tuples_per_block - 1) / k.tuples_per_block, p,
-                  stream);
+    return launch_forward(k.fwd_fused, k.fwd_fused_staged, k, p, stream);
 }
 
 msda_status_t msda_backward_fused_workspace_size(const msda_dims_t* dims,

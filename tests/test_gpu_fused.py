@@ -113,6 +113,15 @@ def parity(w, x=None, backward=True):
     return x, t
 
 
+def test_staged_levels():
+    """A plane of 2500 queries: the forward and point kernels with the coarse
+    levels in LDS."""
+    w = wl.Workload("fused_staged", B=1, M=2, D=32, K=4,
+                    shapes=((64, 96), (32, 48), (16, 24), (8, 12)), ref="uniform",
+                    sigma_px=3.0, Nq=2500, seed=192)
+    parity(w, x=perturb_levels(wl.generate(w), 193))
+
+
 def test_backward_in_passes():
     """A workspace holding the fixed part and the bins of 3 of the 16 (b, m)
     planes: the value gradient runs in passes; all four gradients match."""

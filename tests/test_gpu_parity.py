@@ -100,6 +100,48 @@ def parity(w, backward=True, batch_slice=None, x=None):
     return x, t
 
 
+# ---------------------------------------------------------------- coarse levels in LDS
+# Planes of at least 2048 queries take the forward and point kernels that copy
+# the coarsest levels' rows (one head) into LDS first. On this pyramid the
+# 8 x 12 level fits the stage at 128-byte rows (D = 32 fp32, D = 64 bf16), the
+# two coarsest at 64-byte rows (D = 16 fp32, D = 32 bf16); D = 64 fp32 rows
+# take the plain kernels.
+STAGED_PYRAMID = ((64, 96), (32, 48), (16, 24), (8, 12))
+
+
+@pytest.mark.parametrize("value_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [16, 32, 64])
+def test_staged_levels(D, value_dtype):
+    w = wl.Workload(f"staged_D{D}_{value_dtype}", B=1, M=2, D=D, K=4, shapes=STAGED_PYRAMID,
+                    ref="uniform", sigma_px=3.0, Nq=2500, value_dtype=value_dtype, seed=960 + D)
+    parity(w)
+
+
+def test_staged_levels_ragged():
+    # 3 points per level, a query count that leaves the last block one query,
+    # odd heads, offsets reaching outside every level
+    w = wl.Workload("staged_ragged", B=2, M=3, D=32, K=3, shapes=STAGED_PYRAMID[1:],
+                    ref="uniform", sigma_px=9.0, Nq=2049, seed=967)
+    parity(w)
+
+
+def test_staged_levels_out_of_order():
+    # the coarsest level listed first: it is the one staged, the others not
+    w = wl.Workload("staged_order", B=1, M=2, D=32, K=2,
+                    shapes=(STAGED_PYRAMID[3], STAGED_PYRAMID[0], STAGED_PYRAMID[2],
+                            STAGED_PYRAMID[1]),
+                    ref="uniform", sigma_px=3.0, Nq=2100, seed=968)
+    parity(w)
+
+
+def test_staged_kernels_with_no_level_staged():
+    # four 20 x 20 levels: a halving pyramid of the same size would have a
+    # coarsest level that fits, so the staged kernels run, but no level fits
+    w = wl.Workload("staged_none", B=1, M=2, D=32, K=2, shapes=((20, 20),) * 4, ref="uniform",
+                    sigma_px=2.0, Nq=2100, seed=969)
+    parity(w)
+
+
 # ---------------------------------------------------------------- workspace
 @pytest.mark.parametrize("planes", [1, 3, 8])
 def test_backward_in_passes(planes):

@@ -105,6 +105,13 @@ def test_half_locations_and_weights(D):
     core_case(w, half_locations=True, value_dtype="f32", grad_bf16=False)
 
 
+def test_half_locations_with_staged_levels():
+    w = wl.Workload("hloc_staged", B=1, M=2, D=32, K=4,
+                    shapes=((64, 96), (32, 48), (16, 24), (8, 12)), ref="uniform",
+                    sigma_px=3.0, Nq=2500, seed=530)
+    core_case(w, half_locations=True, value_dtype="f32", grad_bf16=False)
+
+
 @pytest.mark.parametrize("D", [8, 16, 32, 64])
 def test_bf16_grad_value(D):
     w = wl.Workload(f"bf16out_D{D}", B=2, M=4, D=D, K=3, shapes=SMALL_PYRAMID[:3],
