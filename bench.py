@@ -137,6 +137,22 @@ KERNEL_NAMES = {
 
 KERNEL_SOURCE = os.path.join(ROOT, "scale_deformable_attention_amd", "csrc", "msda.hip")
 
+# The library's choice of forward kernel for the core and fused front-ends: the
+# variant that reads the coarsest levels from LDS (msda_fwd_staged_kernel) for
+# planes of at least 2048 queries and head rows of 64 or 128 bytes, when the
+# coarsest level of a pyramid with Nv pixels over L levels, each halving both
+# sides, 3 Nv / (4^L - 1) pixels, fits with one more row in 36 KB.
+STAGE_BYTES, STAGED_MIN_QUERIES = 36 * 1024, 2048
+
+
+def forward_kernel(w, value_bytes_per_elem, fused=False):
+    head = w.D * value_bytes_per_elem
+    coarsest = 3.0 * w.Nv / (4.0 ** w.L - 1.0)
+    staged = (head in (64, 128) and w.num_queries >= STAGED_MIN_QUERIES and w.L * w.K > 0
+              and (coarsest + 1.0) * head <= STAGE_BYTES)
+    name = "msda_fwd_staged_kernel" if staged else "msda_fwd_kernel"
+    return name + ("<fused>" if fused else "")
+
 
 def source_digest():
     with open(KERNEL_SOURCE, "rb") as f:
@@ -700,6 +716,7 @@ def main():
     # (fused: the backward's softmax-statistics kernel runs in both halves, the
     # reference-point reduction after the point kernel)
     names = KERNEL_NAMES["fused" if fused else "core"]
+    names = (forward_kernel(w, 4 if w.value_dtype == "f32" else 2, fused),) + names[1:]
     kernels = {names[0]: timed(fwd, args.steps)}
     if backward:
         kernels[names[1]] = timed(lambda: bwd((False, True, True)), args.steps)

@@ -665,10 +665,15 @@ __global__ __launch_bounds__(kStagedBlock) void msda_fwd_staged_kernel(Params p)
     __shared__ __align__(16) unsigned char stage[kStageBytes];
     load_levels(p, levels);
 
+    // work item (b, m / hp, query range, m % hp): the blocks of heads whose
+    // rows share cache lines (see tuple_of) take the same query range one
+    // after another, on one XCD, while those lines are in its L2
     const int nqc = (p.Nq + kStagedQueries - 1) / kStagedQueries;
     const int item = xcd_block();
-    const int qc = item % nqc, bm = item / nqc;
-    const int b = bm / p.M, m = bm - b * p.M;
+    const int mi = item % p.hp, rest = item / p.hp;
+    const int qc = rest % nqc, bmg = rest / nqc;
+    const int groups = p.M / p.hp;
+    const int b = bmg / groups, m = (bmg - b * groups) * p.hp + mi;
     const int q_begin = qc * kStagedQueries, q_end = min(q_begin + kStagedQueries, p.Nq);
     const uint32_t row_bytes = (uint32_t)p.M * kHeadBytes;
     const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(p.value, p.value_bytes);
