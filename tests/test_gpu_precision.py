@@ -112,6 +112,15 @@ def test_half_locations_with_staged_levels():
     core_case(w, half_locations=True, value_dtype="f32", grad_bf16=False)
 
 
+@pytest.mark.parametrize("D", [32, 64])
+def test_f16_values_with_staged_levels(D):
+    # 64- and 128-byte binary16 rows: the forward stages the coarse levels
+    w = wl.Workload(f"f16_staged_D{D}", B=1, M=4, D=D, K=4,
+                    shapes=((64, 96), (32, 48), (16, 24), (8, 12)), ref="uniform",
+                    sigma_px=3.0, Nq=2300, value_dtype="f16", seed=531 + D)
+    core_case(w, half_locations=False, value_dtype="f16", grad_bf16=False)
+
+
 @pytest.mark.parametrize("D", [8, 16, 32, 64])
 def test_bf16_grad_value(D):
     w = wl.Workload(f"bf16out_D{D}", B=2, M=4, D=D, K=3, shapes=SMALL_PYRAMID[:3],
