@@ -781,6 +781,37 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
     }
     float s_ag = 0.0f;   // fused: this lane's part of sum_j A_j gA_j over the tuple
 
+    // The gradients of this lane's points are held in registers and stored
+    // kHold chunks at a time (all at the end of the tuple for up to kHold
+    // chunks): on this GPU loads and stores share one outstanding-operation
+    // counter that drains in order, so a store issued between two chunks
+    // makes every later wait for gathered rows also wait for the store's
+    // acknowledgement. Slot h holds the point of chunk (first held chunk) + h:
+    // xy goes to the location (or offset) gradient, s to the weight (or
+    // logit, or mask) gradient. (Two slots where a lane group is 8 lanes or
+    // more: four cost the fused front-end a wave per SIMD.)
+    constexpr int kHold = G >= 8 ? 2 : 4;
+    float2 held_xy[kHold];
+    float held_s[kHold];
+#pragma unroll
+    for (int h = 0; h < kHold; ++h) {
+        held_xy[h] = make_float2(0.0f, 0.0f);
+        held_s[h] = 0.0f;
+    }
+    auto store_held = [&](int jc0, int chunks) {
+        float* xy_out = kFused || FE == kFeDcn ? p.grad_off : p.grad_loc;
+        float* s_out = kFused ? p.grad_logits : p.grad_attn;
+#pragma unroll
+        for (int h = 0; h < kHold; ++h) {
+            const int j = jc0 + h * G + r;
+            if (h < chunks && t_ok && j < p.LK) {
+                const size_t pt = (size_t)t * p.LK + j;
+                if (xy_out) *reinterpret_cast<float2*>(xy_out + 2 * pt) = held_xy[h];
+                if (s_out) s_out[pt] = held_s[h];
+            }
+        }
+    };
+
     // this lane's point of the next chunk is loaded one chunk ahead, while
     // the current chunk's rows are gathered
     auto fetch = [&](int jc) {
@@ -795,14 +826,12 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
         // phase 1: this lane's point -> corner offsets in LDS; keep the rest
         const int j = jc + r;
         const bool mine = t_ok && j < p.LK;
-        size_t pt = 0;
         float Hf = 0.0f, Wf = 0.0f;
         float a = 0.0f;
         Geometry geo;
         if (mine) {
             const int l = (unsigned)j / (unsigned)p.K;
             const int4 lv = levels[l];
-            pt = (size_t)t * p.LK + j;
             Hf = (float)lv.x;
             Wf = (float)lv.y;
             float2 uv;
@@ -860,26 +889,25 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
                     gy = fmaf(dwdy[c], mine_dot[c], gy);
                 }
             }
-            if constexpr (kFused) {
-                // offsets: d loc / d off = 1 / (W, H) cancels the pixel scale;
-                // the logits' gradient is finished below, once the tuple's
-                // sum is known (gA parked in the output meanwhile)
-                if (p.grad_off)
-                    *reinterpret_cast<float2*>(p.grad_off + 2 * pt) = make_float2(a * gx, a * gy);
-                if (p.grad_logits) p.grad_logits[pt] = ga;
-                s_ag = fmaf(a, ga, s_ag);
-            } else if constexpr (FE == kFeDcn) {
-                // pixel offsets: d(x, y) / d offset = 1; the modulation
-                // scalar's gradient is the plain weight gradient
-                if (p.grad_off)
-                    *reinterpret_cast<float2*>(p.grad_off + 2 * pt) = make_float2(a * gx, a * gy);
-                if (p.grad_attn) p.grad_attn[pt] = ga;
-            } else {
-                if (p.grad_attn) p.grad_attn[pt] = ga;
-                if (p.grad_loc)
-                    *reinterpret_cast<float2*>(p.grad_loc + 2 * pt) = make_float2(a * Wf * gx, a * Hf * gy);
+            // fused: offsets, d loc / d off = 1 / (W, H) cancels the pixel
+            // scale; the logits' gradient is finished below, once the tuple's
+            // sum is known (gA parked in the output meanwhile). DCNv3: pixel
+            // offsets, d(x, y) / d offset = 1, and the modulation scalar's
+            // gradient is the plain weight gradient.
+            const float2 xy = kFused || FE == kFeDcn ? make_float2(a * gx, a * gy)
+                                                     : make_float2(a * Wf * gx, a * Hf * gy);
+            const int slot = (jc / G) % kHold;
+#pragma unroll
+            for (int h = 0; h < kHold; ++h) {
+                held_xy[h] = slot == h ? xy : held_xy[h];
+                held_s[h] = slot == h ? ga : held_s[h];
             }
+            if constexpr (kFused) s_ag = fmaf(a, ga, s_ag);
         }
+        // wave-uniform: every kHold-th chunk, and the last
+        const int chunk = jc / G;
+        if (chunk % kHold == kHold - 1 || jc + G >= p.LK)
+            store_held(jc - (chunk % kHold) * G, chunk % kHold + 1);
     }
     if constexpr (kFused) {
         // softmax Jacobian: dL/dz_j = A_j (gA_j - sum_i A_i gA_i)
