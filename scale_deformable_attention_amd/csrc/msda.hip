@@ -1107,14 +1107,29 @@ struct PointWalk {
 
 // kCached: the block has at most kBinUnroll points per thread, loaded once and
 // kept in registers for both passes (otherwise each pass loads them).
+// Core front-ends: the entries bound for the first kBinStage slots of the
+// block's slab (of the current tile range) are written to LDS first and
+// copied out in order, whole lines at a time; scattered 16-byte stores to the
+// slab touch one cache line per lane. Sized so that the LDS still holds as
+// many blocks per CU as the registers allow (4 cached, 5 not). (The fused and
+// DCNv3 front-ends measured slower with it.)
+template <int FE, bool kCached>
+constexpr int bin_stage() {
+    return FE == kFeCore || FE == kFeCoreHalf ? (kCached ? 2000 : 1488) : 0;
+}
+
 template <int D, int FE, int TH, bool kCached>
-__global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
+__global__ __launch_bounds__(kBlock)
+__attribute__((amdgpu_waves_per_eu(kCached && bin_stage<FE, kCached>() > 0 ? 4 : 1)))
+void msda_bin_kernel(Params p) {
     using TS = TileShape<D, TH>;
+    constexpr int kStage = bin_stage<FE, kCached>();
     __shared__ LevelTiles lt[MSDA_MAX_LEVELS];
     __shared__ int s_tiles;
     __shared__ uint32_t cnt[kBinRange];
     __shared__ uint32_t off[kBinRange];
     __shared__ uint32_t scratch[kWavesPerBlock];
+    __shared__ float4 staged[kStage > 0 ? kStage : 1];
     setup_tiles<TS::TW, TH>(p, lt, &s_tiles);
     // tables inconsistent with Nv could exceed the row: drop those tiles
     // rather than write past the workspace
@@ -1203,10 +1218,18 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     if (ok[u] && emit[c] && tile[c] >= r0 && tile[c] < r0 + rn) {
-                        const uint32_t slot = atomicAdd(&cnt[tile[c] - r0], 1u);
-                        slab[base + off[tile[c] - r0] + slot] = rec;
+                        const uint32_t pos = off[tile[c] - r0] + atomicAdd(&cnt[tile[c] - r0], 1u);
+                        if (pos < (uint32_t)kStage)
+                            staged[pos] = rec;
+                        else
+                            slab[base + pos] = rec;
                     }
                 }
+            }
+            if constexpr (kStage > 0) {
+                __syncthreads();
+                for (uint32_t i = tid; i < min(total, (uint32_t)kStage); i += kBlock)
+                    slab[base + i] = staged[i];
             }
             base += total;
             __syncthreads();
@@ -1279,11 +1302,19 @@ __global__ __launch_bounds__(kBlock) void msda_bin_kernel(Params p) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     if (ok[u] && emit[c] && tile[c] >= r0 && tile[c] < r0 + rn) {
-                        const uint32_t slot = atomicAdd(&cnt[tile[c] - r0], 1u);
-                        slab[base + off[tile[c] - r0] + slot] = rec;
+                        const uint32_t pos = off[tile[c] - r0] + atomicAdd(&cnt[tile[c] - r0], 1u);
+                        if (pos < (uint32_t)kStage)
+                            staged[pos] = rec;
+                        else
+                            slab[base + pos] = rec;
                     }
                 }
             }
+        }
+        if constexpr (kStage > 0) {
+            __syncthreads();
+            for (uint32_t i = tid; i < min(total, (uint32_t)kStage); i += kBlock)
+                slab[base + i] = staged[i];
         }
         base += total;
         __syncthreads();

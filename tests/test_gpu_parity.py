@@ -134,6 +134,21 @@ def test_staged_levels_out_of_order():
     parity(w)
 
 
+def test_staged_levels_sixteen_levels():
+    # sixteen small levels: the stage takes as many of the coarsest as fit
+    shapes = tuple((2 + (i % 5), 3 + (i * 7) % 9) for i in range(16))
+    w = wl.Workload("staged_sixteen", B=1, M=2, D=32, K=1, shapes=shapes, ref="uniform",
+                    sigma_px=1.5, Nq=2048, seed=970)
+    parity(w)
+
+
+def test_staged_levels_unpaired_heads():
+    # 64-byte bf16 rows with an odd head count: no head pairing
+    w = wl.Workload("staged_unpaired", B=1, M=3, D=32, K=2, shapes=STAGED_PYRAMID,
+                    ref="uniform", sigma_px=3.0, Nq=2100, value_dtype="bf16", seed=971)
+    parity(w)
+
+
 def test_staged_kernels_with_no_level_staged():
     # four 20 x 20 levels: a halving pyramid of the same size would have a
     # coarsest level that fits, so the staged kernels run, but no level fits
