@@ -871,6 +871,12 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
                 dot[c] = group_sum<G>(dot[c]);
                 mine_dot[c] = r == i ? dot[c] : mine_dot[c];
             }
+            // four-lane groups (bf16 at D = 32, fp32 at D = 16): the second half of
+            // the chunk's points is scheduled after the first (DCNv3 117 -> 98 us,
+            // bf16 values 229 -> 217 us; at eight-lane groups the same split
+            // left the core unchanged and slowed the fused front-end)
+            if constexpr (G == 4 && !kFused)
+                if (i == G / 2 - 1) __builtin_amdgcn_sched_barrier(0);
         }
         wave_sync();   // the next chunk rewrites offs
         // phase 3: this lane turns the dot products into the weight and
