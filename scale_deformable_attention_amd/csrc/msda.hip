@@ -86,6 +86,16 @@ __device__ inline float4 load_streaming(const float4* p) {
     return make_float4(v.x, v.y, v.z, v.w);
 }
 
+// A 16-byte store marked non-temporal: data written once and not read again
+// by this kernel (the bin kernel's slab entries, read by the tile kernel that
+// follows), so that it does not displace the lines the kernel reuses.
+__device__ inline void store_streaming(float4* p, float4 v) {
+    __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
+}
+
+// Cache-policy operand of the raw buffer intrinsics: non-temporal.
+constexpr int kBufferNonTemporal = 2;
+
 template <typename T>
 struct Elem;
 template <>
@@ -158,6 +168,7 @@ struct Params {
     float4* slab;             // [bm_count*nW][slab_per_block] (tuple bits, x, y, A) entries
     uint32_t* counters;       // tile work counters, one per XCD group, kCounterStride apart
     uint32_t grad_value_bytes;  // record count of the grad_value buffer (its stores are range-checked)
+    int slab_streaming;       // the pass's entries exceed the L2s: write them non-temporal
     // fused front-end: locations and weights formed from the model's raw
     // outputs inside the kernels
     const float* ref;         // [B, Nq, L, 2] reference points (x, y), normalized
@@ -1234,8 +1245,12 @@ void msda_bin_kernel(Params p) {
             }
             if constexpr (kStage > 0) {
                 __syncthreads();
-                for (uint32_t i = tid; i < min(total, (uint32_t)kStage); i += kBlock)
-                    slab[base + i] = staged[i];
+                for (uint32_t i = tid; i < min(total, (uint32_t)kStage); i += kBlock) {
+                    if (p.slab_streaming)
+                        store_streaming(slab + base + i, staged[i]);
+                    else
+                        slab[base + i] = staged[i];
+                }
             }
             base += total;
             __syncthreads();
@@ -1319,8 +1334,12 @@ void msda_bin_kernel(Params p) {
         }
         if constexpr (kStage > 0) {
             __syncthreads();
-            for (uint32_t i = tid; i < min(total, (uint32_t)kStage); i += kBlock)
-                slab[base + i] = staged[i];
+            for (uint32_t i = tid; i < min(total, (uint32_t)kStage); i += kBlock) {
+                if (p.slab_streaming)
+                    store_streaming(slab + base + i, staged[i]);
+                else
+                    slab[base + i] = staged[i];
+            }
         }
         base += total;
         __syncthreads();
@@ -1593,7 +1612,8 @@ void msda_tile_kernel(Params p) {
         // through a buffer descriptor: level tables inconsistent with Nv (the
         // caller's contract, not checked on the device) cannot write past
         // grad_value -- such a store lands beyond the record count and is
-        // dropped
+        // dropped. Non-temporal: no later tile reads it, and the L2 is
+        // better spent on the upstream-gradient rows the tiles share.
         const int x = x_base + col;
         if (col < TW && x < L_.W) {
 #pragma unroll
@@ -1608,11 +1628,11 @@ void msda_tile_kernel(Params p) {
                         typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
                         const u32x2 v = {float_to_bf16_bits(own[yy].x) | (float_to_bf16_bits(own[yy].y) << 16),
                                          float_to_bf16_bits(own[yy].z) | (float_to_bf16_bits(own[yy].w) << 16)};
-                        __builtin_amdgcn_raw_buffer_store_b64(v, gvrsrc, voff, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b64(v, gvrsrc, voff, 0, kBufferNonTemporal);
                     } else {
                         const u32x4 v = {as_uint(own[yy].x), as_uint(own[yy].y), as_uint(own[yy].z),
                                          as_uint(own[yy].w)};
-                        __builtin_amdgcn_raw_buffer_store_b128(v, gvrsrc, voff, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(v, gvrsrc, voff, 0, kBufferNonTemporal);
                     }
                 }
             }
@@ -2011,6 +2031,12 @@ msda_status_t launch_grad_value(Params& p, const BwdPlan& pl, const msda_dims_t*
     for (int64_t bm0 = 0; bm0 < BM; bm0 += pl.bm_per_pass) {
         p.bm0 = (int)bm0;
         p.bm_count = (int)std::min<int64_t>(pl.bm_per_pass, BM - bm0);
+        // a pass whose entries (about one 16-byte entry per point) outgrow
+        // the eight 4 MB L2s writes them non-temporal (encoder_train: 182 MB,
+        // grad_value stage 284 -> 266 us); a small one keeps them in the L2
+        // for the tile kernel (the 300-query decoder: 4.9 MB, 3 us faster)
+        p.slab_streaming =
+            (int64_t)p.bm_count * dims->Nq * dims->L * dims->K * 16 > ((int64_t)32 << 20);
         msda_status_t s = launch(bin, p.bm_count * pl.nW, p, stream);
         if (s != MSDA_SUCCESS) return s;
         const int64_t items = p.bm_count * (pl.t_stride - 1);
