@@ -774,7 +774,10 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
         const float4* src = reinterpret_cast<const float4*>(p.grad_out + (size_t)t * D + r * PL);
 #pragma unroll
         for (int e = 0; e < PL; e += 4) {
-            const float4 v4 = src[e / 4];
+            // read once: non-temporal where a group is eight lanes or more
+            // (fp32 at D = 32: point kernel 282 -> 255 us; four-lane groups
+            // measured slower)
+            const float4 v4 = G >= 8 ? load_streaming(src + e / 4) : src[e / 4];
             go[e] = v4.x;
             go[e + 1] = v4.y;
             go[e + 2] = v4.z;
