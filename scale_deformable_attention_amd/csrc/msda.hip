@@ -811,11 +811,17 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
     constexpr int kHold = G >= 8 ? 2 : 4;
     float2 held_xy[kHold];
     float held_s[kHold];
+    float held_a[kFused ? kHold : 1];   // fused: the held points' weights A
 #pragma unroll
     for (int h = 0; h < kHold; ++h) {
         held_xy[h] = make_float2(0.0f, 0.0f);
         held_s[h] = 0.0f;
+        if constexpr (kFused) held_a[h] = 0.0f;
     }
+    // fused, every point of the tuple held until its end: the logits'
+    // gradient is finished in registers after the last chunk instead of
+    // parking gA in the output and reading it back
+    const bool fused_in_registers = kFused && p.LK <= kHold * G;
     auto store_held = [&](int jc0, int chunks) {
         float* xy_out = kFused || FE == kFeDcn ? p.grad_off : p.grad_loc;
         float* s_out = kFused ? p.grad_logits : p.grad_attn;
@@ -938,18 +944,29 @@ __global__ __launch_bounds__(kBlock) void msda_bwd_point_kernel(Params p) {
             for (int h = 0; h < kHold; ++h) {
                 held_xy[h] = slot == h ? xy : held_xy[h];
                 held_s[h] = slot == h ? ga : held_s[h];
+                if constexpr (kFused) held_a[h] = slot == h ? a : held_a[h];
             }
             if constexpr (kFused) s_ag = fmaf(a, ga, s_ag);
         }
         // wave-uniform: every kHold-th chunk, and the last
         const int chunk = jc / G;
-        if (chunk % kHold == kHold - 1 || jc + G >= p.LK)
+        if (!fused_in_registers && (chunk % kHold == kHold - 1 || jc + G >= p.LK))
             store_held(jc - (chunk % kHold) * G, chunk % kHold + 1);
     }
     if constexpr (kFused) {
         // softmax Jacobian: dL/dz_j = A_j (gA_j - sum_i A_i gA_i)
         const float s_all = group_sum<G>(s_ag);
-        if (p.grad_logits && t_ok) {
+        if (fused_in_registers) {
+#pragma unroll
+            for (int h = 0; h < kHold; ++h) {
+                const int j = h * G + r;
+                if (t_ok && j < p.LK) {
+                    const size_t pt = (size_t)t * p.LK + j;
+                    if (p.grad_off) *reinterpret_cast<float2*>(p.grad_off + 2 * pt) = held_xy[h];
+                    if (p.grad_logits) p.grad_logits[pt] = held_a[h] * (held_s[h] - s_all);
+                }
+            }
+        } else if (p.grad_logits && t_ok) {
             for (int j = r; j < p.LK; j += G) {
                 const size_t pt = (size_t)t * p.LK + j;
                 const float a = expf(p.logits[pt] - zmax) * inv_sum;
