@@ -1161,15 +1161,15 @@ struct PointWalk {
 
 // kCached: the block has at most kBinUnroll points per thread, loaded once and
 // kept in registers for both passes (otherwise each pass loads them).
-// Core and fused front-ends: the entries bound for the first kBinStage slots
-// of the block's slab (of the current tile range) are written to LDS first
-// and copied out in order, whole lines at a time; scattered 16-byte stores to
-// the slab touch one cache line per lane. Sized so that the LDS still holds
-// as many blocks per CU as the registers allow (4 cached, 5 not). (The DCNv3
-// and binary16-location front-ends measured slower with it.)
+// All but the DCNv3 front-end: the entries bound for the first kBinStage
+// slots of the block's slab (of the current tile range) are written to LDS
+// first and copied out in order, whole lines at a time; scattered 16-byte
+// stores to the slab touch one cache line per lane. Sized so that the LDS
+// still holds as many blocks per CU as the registers allow (4 cached, 5 not).
+// (DCNv3 measured slower with it: 141 -> 155 us for its grad_input stage.)
 template <int FE, bool kCached>
 constexpr int bin_stage() {
-    return FE == kFeCore || FE == kFeFused ? (kCached ? 2000 : 1488) : 0;
+    return FE != kFeDcn ? (kCached ? 2000 : 1488) : 0;
 }
 
 template <int D, int FE, int TH, bool kCached>
